@@ -1,0 +1,463 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Every function of oracle/orc.c is checked here against something other than
+its own formula: closed forms, invariants, exact integer cases, special cases
+that reduce to a library routine, and values printed on the pages.  A
+plausible mistake (dropped term, wrong sign or index, transposed operand,
+wrong scale, wrong pairing) fails at least one of these.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+R = np.random.default_rng(1234)
+
+
+def bf(x):
+    return oracle.bf16_round(np.asarray(x, np.float32))
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage emulation
+# ---------------------------------------------------------------------------
+
+def test_bf16_round_ties_and_specials():
+    one_ulp = 2.0 ** -7          # bf16 spacing in [1, 2)
+    cases = {
+        1.0: 1.0,
+        1.0 + one_ulp / 2: 1.0,                     # tie -> even (1.0)
+        1.0 + 3 * one_ulp / 2: 1.0 + 2 * one_ulp,    # tie -> even (upper)
+        1.0 + one_ulp / 2 + 2 ** -20: 1.0 + one_ulp,  # above the tie -> up
+        -(1.0 + one_ulp / 2): -1.0,
+        float(np.finfo(np.float32).max): np.inf,     # rounds past the largest bf16
+        0.0: 0.0,
+    }
+    for x, want in cases.items():
+        assert bf(np.float32(x))[()] == np.float32(want), x
+    assert np.isnan(bf(np.float32(np.nan)))
+    assert bf(np.float32(np.inf)) == np.inf
+    # representable values are fixed points
+    v = (R.integers(-2 ** 15, 2 ** 15, 1000) << 16).astype(np.uint32).view(np.float32)
+    v = v[np.isfinite(v)]
+    assert np.array_equal(bf(v), v)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_constant_vector_closed_form():
+    H, eps = 256, 1e-5
+    g = R.uniform(0.5, 1.5, H).astype(np.float32)
+    for c in (0.5, -2.0, 3e-3, 10.0):
+        x = np.full((1, H), c, np.float32)
+        out = oracle.rmsnorm(x, g, eps)
+        want = g * (c / np.sqrt(c * c + eps))
+        np.testing.assert_allclose(out[0], want, rtol=1e-6)
+
+
+def test_rmsnorm_residual_closed_form_and_h():
+    H, eps = 128, 1e-5
+    g = R.uniform(0.5, 1.5, H).astype(np.float32)
+    x = np.full((2, H), 1.25, np.float32)
+    r = np.full((2, H), -3.5, np.float32)
+    out, h = oracle.rmsnorm(x, g, eps, resid=r)
+    assert np.all(h == np.float32(-2.25))
+    np.testing.assert_allclose(out, np.broadcast_to(g * (-2.25 / np.sqrt(2.25 ** 2 + eps)), (2, H)),
+                               rtol=1e-6)
+    # r = -x gives h = 0 and a zero output
+    out0, h0 = oracle.rmsnorm(x, g, eps, resid=-x)
+    assert np.all(h0 == 0) and np.all(out0 == 0)
+
+
+def test_rmsnorm_invariants():
+    T, H = 5, 384
+    x = R.standard_normal((T, H)).astype(np.float32)
+    ones = np.ones(H, np.float32)
+    # eps = 0: scale invariance, and unit mean square
+    a = oracle.rmsnorm(x, ones, 0.0)
+    b = oracle.rmsnorm(x * 7.0, ones, 0.0)
+    np.testing.assert_allclose(a, b, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose((a.astype(np.float64) ** 2).mean(1), 1.0, rtol=1e-6)
+    # eps > 0: mean(out^2) = ms / (ms + eps)
+    eps = 0.3
+    c = oracle.rmsnorm(x, ones, eps)
+    ms = (x.astype(np.float64) ** 2).mean(1)
+    np.testing.assert_allclose((c.astype(np.float64) ** 2).mean(1), ms / (ms + eps), rtol=1e-5)
+    # gamma multiplies elementwise
+    g = R.uniform(0.5, 1.5, H).astype(np.float32)
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, eps), c * g, rtol=1e-6)
+
+
+def test_rmsnorm_bf16_mode_is_rounded_exact():
+    x = R.standard_normal((3, 256)).astype(np.float32)
+    g = R.uniform(0.5, 1.5, 256).astype(np.float32)
+    e = oracle.rmsnorm(x, g, 1e-5, mode=oracle.EXACT)
+    b = oracle.rmsnorm(x, g, 1e-5, mode=oracle.BF16)
+    assert np.array_equal(b, bf(e))
+
+
+# ---------------------------------------------------------------------------
+# projections
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(7, 13, 40), (33, 64, 24), (1, 5, 3)])
+def test_linear_exact_on_small_integers(M, N, K):
+    x = R.integers(-3, 4, (M, K))
+    w = R.integers(-3, 4, (N, K))
+    y = oracle.linear(x.astype(np.float32), w.astype(np.float32))
+    assert np.array_equal(y, (x @ w.T).astype(np.float32))   # integer matmul, library routine
+
+
+def test_linear_one_hot_selects_rows():
+    x = R.standard_normal((4, 9)).astype(np.float32)
+    w = np.zeros((3, 9), np.float32)
+    w[0, 2] = w[1, 7] = w[2, 0] = 1.0
+    y = oracle.linear(x, w)
+    assert np.array_equal(y, x[:, [2, 7, 0]])
+
+
+def test_linear_fp64_accumulation():
+    # 1 + 1e-8 * n: fp32 accumulation would lose the small terms entirely
+    K = 4096
+    x = np.full((1, K), 1e-8, np.float32)
+    x[0, 0] = 1.0
+    w = np.ones((1, K), np.float32)
+    y = oracle.linear(x, w)
+    assert y[0, 0] == np.float32(1.0 + (K - 1) * np.float64(np.float32(1e-8)))
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def test_rope_position_zero_is_identity():
+    u = R.standard_normal((3, 2, 64)).astype(np.float32)
+    assert np.array_equal(oracle.rope(u, np.zeros(3, np.int32), 1e4), u)
+
+
+def test_rope_golden_rotation_points():
+    gold = json.load(open(os.path.join(GOLD, "rope_points.json")))
+    cs = {1: (gold["cos1"], gold["sin1"]), 2: (gold["cos2"], gold["sin2"])}
+    for pt in gold["points"]:
+        D, i = pt["D"], pt["i"]
+        c, s = cs[pt["angle"]]
+        e = np.zeros((1, 1, D), np.float32)
+        e[0, 0, i] = 1.0
+        r = oracle.rope(e, np.array([pt["pos"]], np.int32), pt["theta"])[0, 0]
+        want = np.zeros(D)
+        want[i], want[i + D // 2] = c, s            # rotate-half partner slot
+        np.testing.assert_allclose(r, want, atol=2e-7)
+        f = np.zeros((1, 1, D), np.float32)
+        f[0, 0, i + D // 2] = 1.0
+        r2 = oracle.rope(f, np.array([pt["pos"]], np.int32), pt["theta"])[0, 0]
+        want2 = np.zeros(D)
+        want2[i], want2[i + D // 2] = -s, c
+        np.testing.assert_allclose(r2, want2, atol=2e-7)
+
+
+def test_rope_preserves_pair_norms_and_relative_position():
+    D = 128
+    q = R.standard_normal((1, 1, D)).astype(np.float32)
+    k = R.standard_normal((1, 1, D)).astype(np.float32)
+    pos = np.array([37], np.int32)
+    rq = oracle.rope(q, pos, 1e4)[0, 0].astype(np.float64)
+    q0 = q[0, 0].astype(np.float64)
+    h = D // 2
+    np.testing.assert_allclose(rq[:h] ** 2 + rq[h:] ** 2, q0[:h] ** 2 + q0[h:] ** 2, rtol=1e-5)
+
+    def score(p, r):
+        a = oracle.rope(q, np.array([p], np.int32), 1e4)[0, 0].astype(np.float64)
+        b = oracle.rope(k, np.array([r], np.int32), 1e4)[0, 0].astype(np.float64)
+        return a @ b
+
+    base = score(50, 20)
+    for shift in (1, 9, 333):
+        np.testing.assert_allclose(score(50 + shift, 20 + shift), base, rtol=1e-4, atol=1e-4)
+
+
+def test_qkv_rope_composition():
+    T, H, Hq, Hkv, D = 6, 64, 4, 2, 64
+    x = R.standard_normal((T, H)).astype(np.float32)
+    wq = R.standard_normal((Hq * D, H)).astype(np.float32)
+    wk = R.standard_normal((Hkv * D, H)).astype(np.float32)
+    wv = R.standard_normal((Hkv * D, H)).astype(np.float32)
+    pos = np.arange(T, dtype=np.int32) + 3
+    q, k, v = oracle.qkv_rope(x, wq, wk, wv, pos, 1e4, Hq, Hkv, D)
+    assert np.array_equal(v.reshape(T, -1), oracle.linear(x, wv))     # v is not rotated
+    qq = oracle.rope(oracle.linear(x, wq).reshape(T, Hq, D), pos, 1e4)
+    assert np.array_equal(q, qq)
+    kk = oracle.rope(oracle.linear(x, wk).reshape(T, Hkv, D), pos, 1e4)
+    assert np.array_equal(k, kk)
+
+
+# ---------------------------------------------------------------------------
+# reshape_and_cache
+# ---------------------------------------------------------------------------
+
+def test_reshape_and_cache_inverse_map_and_sentinels():
+    T, Hkv, D, BS = 37, 2, 64, 16
+    lens = [20, 17]
+    seq = np.repeat([0, 1], lens).astype(np.int32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    k = R.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = R.standard_normal((T, Hkv, D)).astype(np.float32)
+    nb = 7
+    bt = np.array([[5, 2], [0, 6]], np.int32)
+    kc = np.full((nb, Hkv, BS, D), np.nan, np.float32)
+    vc = np.full((nb, Hkv, BS, D), np.nan, np.float32)
+    oracle.reshape_and_cache(k, v, seq, pos, bt, kc, vc)
+    written = np.zeros((nb, BS), bool)
+    for t in range(T):
+        blk, slot = bt[seq[t], pos[t] // BS], pos[t] % BS
+        assert np.array_equal(kc[blk, :, slot], k[t]) and np.array_equal(vc[blk, :, slot], v[t])
+        written[blk, slot] = True
+    free = ~written
+    assert np.isnan(kc.transpose(0, 2, 1, 3)[free]).all()
+    assert np.isnan(vc.transpose(0, 2, 1, 3)[free]).all()
+    assert written.sum() == T
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def test_attention_identical_keys_give_mean_of_v():
+    S, Hq, Hkv, D = 9, 2, 1, 64
+    q = R.standard_normal((S, Hq, D)).astype(np.float32)
+    k = np.broadcast_to(R.standard_normal(D).astype(np.float32), (S, Hkv, D)).copy()
+    v = R.standard_normal((S, Hkv, D)).astype(np.float32)
+    out = oracle.attn_prefill(q, k, v, [0, S])
+    for i in range(S):
+        want = v[: i + 1, 0].astype(np.float64).mean(0)
+        for h in range(Hq):
+            np.testing.assert_allclose(out[i, h], want, rtol=1e-5, atol=1e-6)
+    assert np.array_equal(out[0, 0], v[0, 0])          # first causal row sees only v0
+
+
+def test_attention_softmax_rows_sum_to_one_and_scale():
+    S, D = 12, 64
+    q = R.standard_normal((S, 1, D)).astype(np.float32) * 2
+    k = R.standard_normal((S, 1, D)).astype(np.float32) * 2
+    v = np.zeros((S, 1, D), np.float32)
+    v[np.arange(S), 0, np.arange(S)] = 1.0             # one-hot values expose P itself
+    P = oracle.attn_prefill(q, k, v, [0, S])[:, 0, :S].astype(np.float64)
+    np.testing.assert_allclose(P.sum(1), 1.0, rtol=1e-6)
+    assert np.all(np.triu(P, 1) == 0)                   # causal: no weight on later keys
+    # two keys: P = logistic(scale * (s1 - s2)) with scale 1/sqrt(D)
+    a = 3.0
+    q2 = np.zeros((2, 1, D), np.float32)
+    q2[1, 0, 0] = a
+    k2 = np.zeros((2, 1, D), np.float32)
+    k2[0, 0, 0] = 1.0
+    v2 = np.zeros((2, 1, D), np.float32)
+    v2[0, 0, 0] = 1.0
+    p = oracle.attn_prefill(q2, k2, v2, [0, 2])[1, 0, 0]
+    np.testing.assert_allclose(p, 1.0 / (1.0 + np.exp(-a / np.sqrt(D))), rtol=1e-6)
+
+
+def test_attention_dominant_score_and_shift_invariance():
+    S, D = 5, 64
+    q = np.zeros((S, 1, D), np.float32)
+    q[:, 0, 0] = 60.0
+    k = np.zeros((S, 1, D), np.float32)
+    k[2, 0, 0] = 30.0                                   # key 2 dominates for rows >= 2
+    v = R.standard_normal((S, 1, D)).astype(np.float32)
+    out = oracle.attn_prefill(q, k, v, [0, S])
+    np.testing.assert_allclose(out[4, 0], v[2, 0], rtol=1e-5, atol=1e-5)
+    # adding the same vector to every key along a direction orthogonal to q
+    qo = R.standard_normal((S, 1, D)).astype(np.float32)
+    qo[:, 0, 1] = 0
+    ko = R.standard_normal((S, 1, D)).astype(np.float32)
+    shifted = ko.copy()
+    shifted[:, 0, 1] += 5.0
+    np.testing.assert_allclose(oracle.attn_prefill(qo, ko, v, [0, S]),
+                               oracle.attn_prefill(qo, shifted, v, [0, S]), rtol=1e-6, atol=1e-6)
+
+
+def test_attention_gqa_equals_repeated_mha_and_varlen_separates():
+    lens = [7, 4, 9]
+    T, Hq, Hkv, D = sum(lens), 4, 2, 64
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = R.standard_normal((T, Hq, D)).astype(np.float32)
+    k = R.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = R.standard_normal((T, Hkv, D)).astype(np.float32)
+    g = oracle.attn_prefill(q, k, v, cu)
+    m = oracle.attn_prefill(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), cu)
+    assert np.array_equal(g, m)
+    for b in range(3):
+        s, e = cu[b], cu[b + 1]
+        alone = oracle.attn_prefill(q[s:e], k[s:e], v[s:e], [0, e - s])
+        assert np.array_equal(g[s:e], alone)
+    # causality: changing later tokens of a sequence leaves earlier rows alone
+    k2 = k.copy()
+    k2[10:] += 1.0
+    g2 = oracle.attn_prefill(q, k2, v, cu)
+    assert np.array_equal(g2[:10], g[:10])
+
+
+def test_paged_decode_equals_contiguous_under_permutation():
+    B, Hq, Hkv, D, BS = 3, 4, 2, 64, 16
+    ctx = np.array([5, 33, 48], np.int32)
+    S = 48
+    kcont = R.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    vcont = R.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    q = R.standard_normal((B, Hq, D)).astype(np.float32)
+    nblk = (ctx + BS - 1) // BS
+    pool = int(nblk.sum()) + 4
+    perm = np.random.default_rng(7).permutation(pool)
+    bt = np.full((B, 3), -1, np.int32)
+    kc = np.full((pool, Hkv, BS, D), np.nan, np.float32)
+    vc = np.full((pool, Hkv, BS, D), np.nan, np.float32)
+    j = 0
+    for b in range(B):
+        for lb in range(nblk[b]):
+            p = perm[j]
+            j += 1
+            bt[b, lb] = p
+            n = min(BS, ctx[b] - lb * BS)
+            kc[p, :, :n] = kcont[b, :, lb * BS: lb * BS + n]
+            vc[p, :, :n] = vcont[b, :, lb * BS: lb * BS + n]
+    paged = oracle.attn_decode_paged(q, kc, vc, bt, ctx)
+    cont = oracle.attn_decode_contig(q, kcont, vcont, ctx)
+    assert np.array_equal(paged, cont)
+    # and the contiguous decode equals the last row of a prefill over the same keys
+    for b in range(B):
+        n = ctx[b]
+        qq = np.zeros((n, Hq, D), np.float32)
+        qq[-1] = q[b]
+        pre = oracle.attn_prefill(qq, kcont[b, :, :n].transpose(1, 0, 2),
+                                  vcont[b, :, :n].transpose(1, 0, 2), [0, n])
+        np.testing.assert_allclose(pre[-1], cont[b], rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU feed-forward
+# ---------------------------------------------------------------------------
+
+def test_swiglu_special_values():
+    H, I = 16, 32
+    x = np.zeros((1, H), np.float32)
+    x[0, 0] = 1.0
+    wg = np.zeros((I, H), np.float32)
+    wu = np.zeros((I, H), np.float32)
+    wg[:, 0] = np.linspace(-40, 40, I)
+    wu[:, 0] = 1.0
+    a = oracle.swiglu(x, wg, wu)[0].astype(np.float64)
+    z = wg[:, 0].astype(np.float64)
+    assert a[np.argmin(np.abs(z))] == pytest.approx(0.0, abs=2.0)   # near the origin
+    np.testing.assert_allclose(a[z > 30], z[z > 30], rtol=1e-9)      # silu(z) -> z
+    assert np.all(np.abs(a[z < -30]) < 1e-10)                         # silu(z) -> 0
+    # silu(0) = 0, silu(1) = 1 / (1 + e^-1)
+    wg2 = np.zeros((2, H), np.float32)
+    wg2[1, 0] = 1.0
+    wu2 = np.ones((2, H), np.float32)
+    a2 = oracle.swiglu(x, wg2, wu2)[0]
+    assert a2[0] == 0.0
+    assert a2[1] == pytest.approx(0.7310585786300049, rel=1e-7)
+    # up = 0 gives 0 whatever the gate
+    assert np.all(oracle.swiglu(x, wg, np.zeros_like(wu)) == 0)
+
+
+def test_ffn_composition_and_residual():
+    M, H, I = 3, 32, 48
+    x = R.standard_normal((M, H)).astype(np.float32)
+    wg, wu = (R.standard_normal((I, H)).astype(np.float32) for _ in range(2))
+    wd = R.standard_normal((H, I)).astype(np.float32)
+    r = R.standard_normal((M, H)).astype(np.float32)
+    a = oracle.swiglu(x, wg, wu)
+    y = oracle.ffn(x, wg, wu, wd, r)
+    assert np.array_equal(y, (oracle.linear(a, wd) + r).astype(np.float32))
+    assert np.array_equal(oracle.ffn(x, wg, wu, np.zeros_like(wd), r), r)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+def _tiny(gamma="uniform"):
+    from transformer_decoder_layer_residual_amd import inputs as gen
+    cfg = gen.CONFIGS[1]
+    return cfg, gen, gen.weights(cfg, gamma=gamma)
+
+
+def test_layer_identity_when_output_projections_vanish():
+    cfg, gen, w = _tiny()
+    w = dict(w, wo=np.zeros_like(w["wo"]), wd=np.zeros_like(w["wd"]))
+    pb = gen.packed([11, 5])
+    x = gen.hidden(cfg, pb.T)
+    y, h = oracle.layer_prefill(cfg.dims(), w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens)
+    assert np.array_equal(y, x) and np.array_equal(h, x)
+    w2 = dict(_tiny()[2], ln2=np.zeros(cfg.hidden, np.float32))
+    y2, h2 = oracle.layer_prefill(cfg.dims(), w2, x, pb.positions, pb.seq_of_token, pb.cu_seqlens)
+    assert np.array_equal(y2, h2)
+
+
+@pytest.mark.parametrize("mode", [oracle.EXACT, oracle.BF16, oracle.BF16_UNFUSED])
+def test_layer_prefill_equals_its_steps(mode):
+    cfg, gen, w = _tiny()
+    d = cfg.dims()
+    pb = gen.packed([13, 6])
+    x = gen.hidden(cfg, pb.T)
+    bt = gen.block_table(cfg, pb.lens)
+    kc = np.full((bt.num_blocks, 4, 16, 64), np.nan, np.float32)
+    vc = kc.copy()
+    y, h = oracle.layer_prefill(d, w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens, kc, vc,
+                                bt.table, mode=mode)
+    n1 = oracle.rmsnorm(x, w["ln1"], d["rms_eps"], mode=mode)
+    q, k, v = oracle.qkv_rope(n1, w["wq"], w["wk"], w["wv"], pb.positions, d["rope_theta"], 4, 4,
+                              64, mode=mode)
+    at = oracle.attn_prefill(q, k, v, pb.cu_seqlens, mode=mode).reshape(pb.T, -1)
+    o = oracle.linear(at, w["wo"], round_bf16=mode != oracle.EXACT)
+    n2, hh = oracle.rmsnorm(o, w["ln2"], d["rms_eps"], resid=x, mode=mode)
+    yy = oracle.ffn(n2, w["wg"], w["wu"], w["wd"], hh, mode=mode)
+    assert np.array_equal(h, hh) and np.array_equal(y, yy)
+    kc2 = np.full_like(kc, np.nan)
+    vc2 = np.full_like(vc, np.nan)
+    oracle.reshape_and_cache(k, v, pb.seq_of_token, pb.positions, bt.table, kc2, vc2)
+    assert np.array_equal(kc, kc2, equal_nan=True) and np.array_equal(vc, vc2, equal_nan=True)
+
+
+def test_decode_after_prefill_equals_prefill_row():
+    cfg, gen, w = _tiny()
+    d = cfg.dims()
+    n = 21
+    x = gen.hidden(cfg, n + 1)
+    bt = gen.block_table(cfg, [n + 1])
+    kc = np.full((bt.num_blocks, 4, 16, 64), np.nan, np.float32)
+    vc = kc.copy()
+    pb = gen.packed([n])
+    oracle.layer_prefill(d, w, x[:n], pb.positions, pb.seq_of_token, pb.cu_seqlens, kc, vc,
+                         bt.table)
+    yd, _ = oracle.layer_decode(d, w, x[n:], np.array([n + 1], np.int32), kc, vc, bt.table)
+    full = gen.packed([n + 1])
+    yp, _ = oracle.layer_prefill(d, w, x, full.positions, full.seq_of_token, full.cu_seqlens)
+    np.testing.assert_allclose(yd[0], yp[n], rtol=1e-6, atol=1e-6)
+
+
+def test_layer_bf16_modes_close_to_exact():
+    cfg, gen, w = _tiny()
+    w = {k: bf(v) for k, v in w.items()}
+    pb = gen.packed([24])
+    x = bf(gen.hidden(cfg, pb.T))
+    ye, _ = oracle.layer_prefill(cfg.dims(), w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens)
+    yb, _ = oracle.layer_prefill(cfg.dims(), w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens,
+                                 mode=oracle.BF16)
+    rel = np.linalg.norm(yb - ye) / np.linalg.norm(ye)
+    assert 0 < rel < 1e-2
+
+
+# ---------------------------------------------------------------------------
+# the pages' own numbers
+# ---------------------------------------------------------------------------
+
+def test_kv_cache_size_formula_matches_page_values():
+    gold = json.load(open(os.path.join(GOLD, "kv_cache_sizes.json")))
+    for c in gold["cases"]:
+        got = oracle.kv_cache_bytes(c["layers"], c["seq"], c["batch"], c["d"], c["elem_bytes"])
+        assert round(got / 1e9, 1) == pytest.approx(c["gb"], abs=0.11)
