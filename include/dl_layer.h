@@ -1,0 +1,266 @@
+/*
+ * dl_layer.h -- C ABI of the MI355X (gfx950) fused Llama-style decoder layer.
+ *
+ * The layer is the pre-norm chain named on the ops-transformer Llama2-7B page
+ * (seekfood.cn), paragraph "single-layer operator call chain":
+ *
+ *   x -> RMSNorm -> Q/K/V linear -> rotary embedding -> self-attention (GQA)
+ *     -> output linear -> residual add -> RMSNorm -> gate/up linear -> SiLU
+ *     -> down linear -> residual add
+ *
+ * with prefill and decode taking different attention kernels (same page,
+ * paragraph "KV cache and operators") and decode reading K/V from a paged
+ * cache addressed through block_table and context lengths (ATB KV-cache page,
+ * hwcomputing.csdn.net, section "KV cache memory bottleneck").
+ *
+ * Conventions (every entry point):
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned.  The library never allocates device memory:
+ *     scratch space is a caller-provided workspace whose minimum size comes
+ *     from the matching *_workspace_size query (the Setup/Execute split of the
+ *     ATB operation API, without hidden state).
+ *   - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
+ *     work on it and return; nothing synchronises.
+ *   - Weights are [out_features][in_features]; a projection is y = x W^T.
+ *   - dtype DL_BF16: weights, gammas, normalised activations, q/k/v, the KV
+ *     cache, attention output and FFN intermediate are bf16 (round to nearest
+ *     even), every product accumulates in fp32, and the residual stream
+ *     (hidden_in, h, hidden_out) is fp32.  DL_F32: everything is fp32.
+ *   - KV cache: separate K and V tensors, each [num_blocks][Hkv][BS][D] in the
+ *     layer dtype.  Position p of sequence s lives in physical block
+ *     block_table[s][p / BS] at slot p % BS.  block_table is
+ *     [B][max_blocks_per_seq] int32; unused entries may hold any value.
+ *   - Return value: DL_OK, or an error code, in which case NOTHING was
+ *     enqueued; dl_last_error() then describes the failure (thread-local).
+ *     DL_ERR_HIP reports a failed launch.
+ *   - Device-side preconditions (not checked, never fault): block_table
+ *     entries that are used lie in [0, num_blocks); 0 <= positions <
+ *     max_blocks_per_seq * BS; 1 <= context_lens[b] <= max_context_len.  An
+ *     out-of-range table entry makes the cache write drop the token and the
+ *     attention read block 0 instead (wrong numbers, no memory fault).
+ *   - Supported shapes: head_dim D in {64, 128}; Hq % Hkv == 0 with
+ *     Hq / Hkv in {1, 2, 4, 8}; BS in {16, 32, 64, 128}; hidden H a multiple
+ *     of 32 and <= 8192; intermediate I a multiple of 16; reduction sizes a
+ *     multiple of 8.  Anything else returns DL_ERR_UNSUPPORTED.
+ */
+#ifndef DL_LAYER_H
+#define DL_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DL_OK = 0,
+  DL_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent dims */
+  DL_ERR_UNSUPPORTED = 2,  /* shape outside the supported set (see above) */
+  DL_ERR_ALIGNMENT = 3,    /* a tensor pointer is not 16-byte aligned */
+  DL_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required */
+  DL_ERR_HIP = 5           /* the HIP runtime reported an error */
+} dl_status;
+
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+
+/* DL_FUSED: the fused kernels.  DL_UNFUSED: the kernel-per-op chain (separate
+ * q/k/v GEMMs, RoPE pass, score matrix in fp32, softmax, PV, separate gate and
+ * up GEMMs, SiLU and multiply passes, residual adds as their own kernels), the
+ * "step by step" execution mode of the ascend-transformer-boost page (section
+ * "fusion granularity boundaries"), kept as the HBM-bytes baseline. */
+typedef enum { DL_FUSED = 0, DL_UNFUSED = 1 } dl_mode;
+
+typedef struct {
+  int32_t hidden;        /* H */
+  int32_t n_q_heads;     /* Hq */
+  int32_t n_kv_heads;    /* Hkv */
+  int32_t head_dim;      /* D */
+  int32_t intermediate;  /* I */
+  int32_t block_size;    /* BS, KV-cache block size in tokens */
+  float rms_eps;
+  dl_dtype dtype;
+} dl_layer_dims;
+
+/* ln1/ln2 gammas [H]; w_q [Hq*D][H]; w_k, w_v [Hkv*D][H]; w_o [H][Hq*D];
+ * w_gate, w_up [I][H]; w_down [H][I] (the separate FFN weight shapes of the
+ * ascend-transformer-boost page, section "fusion operator matrix"). */
+typedef struct {
+  const void *ln1_gamma, *w_q, *w_k, *w_v, *w_o, *ln2_gamma, *w_gate, *w_up, *w_down;
+} dl_layer_weights;
+
+typedef struct {
+  void* k_cache;       /* [num_blocks][Hkv][BS][D] */
+  void* v_cache;       /* [num_blocks][Hkv][BS][D] */
+  int32_t num_blocks;
+} dl_kv_cache;
+
+/* Human-readable name of a status code (static string). */
+const char* dl_status_string(dl_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* dl_last_error(void);
+/* ABI version of this header (incremented on incompatible change). */
+int32_t dl_abi_version(void);
+
+/*
+ * RoPE table: cos_sin[p][i][0..1] = cos, sin of p * theta^(-2i/D) for
+ * p < max_pos, i < D/2, with the angle computed in fp64 and rounded to fp32.
+ * The pages name the rotary embedding on the QKV output without a formula;
+ * this is the rotate-half (i, i + D/2) pairing of Llama.
+ * cos_sin: device, max_pos * D floats.
+ */
+dl_status dl_rope_table_fill(float* cos_sin, int32_t max_pos, int32_t head_dim, double theta,
+                             void* stream);
+
+/*
+ * RMSNorm, optionally fused with the residual add (ascend-transformer-boost
+ * page, "fusion operator matrix": norm fused with the residual add; RMSNorm in
+ * the Llama chain of the ops-transformer page).
+ *   residual_in == NULL: out = gamma * x / sqrt(mean(x^2) + eps)
+ *   otherwise:           h = x + residual_in (fp32), written to residual_out
+ *                        (may alias residual_in), out = RMSNorm(h)
+ * x [T][H] of x_dtype; residual_in/out [T][H] fp32; gamma [H] and out [T][H]
+ * of out_dtype.  T may be 0.
+ */
+dl_status dl_rmsnorm_residual(const void* x, dl_dtype x_dtype, const float* residual_in,
+                              float* residual_out, const void* gamma, void* out, int32_t T,
+                              int32_t H, float eps, dl_dtype out_dtype, void* stream);
+
+/*
+ * Merged QKV projection with the rotary embedding as its epilogue
+ * (ops-transformer page, "single-layer operator call chain": MergedMatMul of
+ * the three linears sharing x, RoPE applied on the QKV output on chip).
+ *   [q | k | v] = x [Wq; Wk; Wv]^T, then q and k of every head rotated at the
+ *   token's position with cos_sin (from dl_rope_table_fill).
+ * x [T][H]; w_q [Hq*D][H]; w_k, w_v [Hkv*D][H]; positions [T] int32 in
+ * [0, max_pos); q [T][Hq][D]; k, v [T][Hkv][D].  All of dtype dt.
+ */
+size_t dl_qkv_rope_workspace_size(int32_t T, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                                  dl_dtype dt);
+dl_status dl_qkv_rope(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                      const int32_t* positions, const float* cos_sin, int32_t max_pos, void* q,
+                      void* k, void* v, int32_t T, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                      dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Reshape-and-cache (ATB KV-cache page, "KV cache memory bottleneck":
+ * ReshapeAndCache writes step K/V into the paged blocks through block_table).
+ * Token t of sequence seq_of_token[t] at position positions[t] is copied to
+ * block block_table[seq][pos / BS], slot pos % BS, of both caches.  A bit
+ * copy.  k, v [T][Hkv][D]; seq_of_token [T] int32, or NULL meaning
+ * seq_of_token[t] = t (one token per sequence, the decode case).
+ */
+dl_status dl_reshape_and_cache(const void* k, const void* v, const int32_t* seq_of_token,
+                               const int32_t* positions, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const dl_kv_cache* cache, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t BS, dl_dtype dt, void* stream);
+
+/*
+ * Prefill attention: causal, variable-length, grouped-query flash attention
+ * (ATB fusion-strategy page, "Attention fusion"; ops-transformer page, "KV
+ * cache and operators": prefill sends the full sequence through
+ * FlashAttention).  Packed sequences: sequence b owns rows
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens [B+1] int32, device, with
+ * cu_seqlens[B] == T and every length <= max_seqlen).  Row i of a sequence
+ * attends to rows 0..i of the same sequence; kv head = h / (Hq/Hkv).
+ * q, out [T][Hq][D]; k, v [T][Hkv][D].  scale is normally 1/sqrt(D).
+ */
+dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t max_seqlen,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, void* out, dl_dtype dt,
+                          void* stream);
+
+/*
+ * Paged decode attention (ops-transformer page, "KV cache and operators":
+ * Q [1, heads, 1, dim] against cached K/V with a decode-specialised kernel;
+ * ATB KV-cache page: PagedAttention over block_table and contextLens).
+ * Sequence b attends over cached positions 0 .. context_lens[b]-1 (the new
+ * token must already be in the cache).  q, out [B][Hq][D].  The result does
+ * not depend on which physical blocks hold the data.
+ */
+size_t dl_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int32_t max_context_len, int32_t BS);
+dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, float scale,
+                               void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Plain projection out = x W^T (the attention output linear of the chain,
+ * exported for step-by-step use).  x [M][K], w [N][K], out [M][N], dtype dt.
+ */
+size_t dl_linear_workspace_size(int32_t M, int32_t N, int32_t K, dl_dtype dt);
+dl_status dl_linear(const void* x, const void* w, void* out, int32_t M, int32_t N, int32_t K,
+                    dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * SwiGLU feed-forward with the residual add fused into the down projection
+ * (ops-transformer page: MergedMatMul(GateUp), SiLU, gate x up, down linear;
+ * ATB fusion-strategy page, "MLP fusion": residual fused into the last dense).
+ *   a   = silu(x Wg^T) * (x Wu^T)          (stage 1, a kept in the workspace)
+ *   out = residual + a Wd^T                 (stage 2; residual may be NULL)
+ * x [T][H] dtype dt; w_gate, w_up [I][H]; w_down [H][I]; residual, out [T][H]
+ * fp32 (out may alias residual).
+ */
+size_t dl_ffn_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt);
+dl_status dl_ffn_swiglu(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                        const float* residual, float* out, int32_t T, int32_t H, int32_t I,
+                        dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage 1 alone: a [T][I] (dtype dt) = silu(x Wg^T) * (x Wu^T). */
+size_t dl_gate_up_silu_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt);
+dl_status dl_gate_up_silu(const void* x, const void* w_gate, const void* w_up, void* a, int32_t T,
+                          int32_t H, int32_t I, dl_dtype dt, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Stage 2 alone: out [T][H] fp32 = residual + a Wd^T (residual may be NULL). */
+size_t dl_down_residual_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt);
+dl_status dl_down_residual(const void* a, const void* w_down, const float* residual, float* out,
+                           int32_t T, int32_t H, int32_t I, dl_dtype dt, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Whole layer.  Workspace for any call with T <= max_tokens, B <= max_batch,
+ * every prefill length <= max_seqlen and every decode context length <=
+ * max_context_len.
+ */
+size_t dl_layer_workspace_size(const dl_layer_dims* d, int32_t max_tokens, int32_t max_batch,
+                               int32_t max_seqlen, int32_t max_context_len, dl_mode m);
+
+/*
+ * Prefill of B packed sequences (T tokens in total).
+ *   hidden_in [T][H] fp32 -> hidden_out [T][H] fp32 (must not alias).
+ *   positions [T] (restart at 0 in every sequence), seq_of_token [T],
+ *   cu_seqlens [B+1]; every token's K/V is also written to the cache.
+ * Attention reads K/V straight from the projection output.
+ */
+dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
+                           const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                           float* hidden_out, const int32_t* positions,
+                           const int32_t* seq_of_token, const int32_t* cu_seqlens, int32_t B,
+                           int32_t T, int32_t max_seqlen, const dl_kv_cache* cache,
+                           const int32_t* block_table, int32_t max_blocks_per_seq, dl_mode m,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step: one new token per sequence.
+ *   hidden_in [B][H] fp32 -> hidden_out [B][H] fp32 (must not alias);
+ *   positions [B] = context_lens - 1; context_lens [B] counts the new token.
+ * The new K/V are written to the cache first, then attention runs over the
+ * whole cached context (ascend-transformer-boost page, "KVCache management":
+ * update the cache in place, then attend over the full cache).
+ */
+dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
+                          const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                          float* hidden_out, const int32_t* positions,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                          const dl_kv_cache* cache, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DL_LAYER_H */

@@ -1,0 +1,311 @@
+"""Per-kernel parity of the HIP library against the CPU oracle (GPU).
+
+Small shapes that still span several tiles and a ragged tail; the oracle
+runs in its bf16-storage mode on the GPU's own bf16 inputs (fp32 mode for
+fp32 kernels).  Integer and copy work is compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_decoder_layer_residual_amd import binding as dl
+from transformer_decoder_layer_residual_amd import inputs as gen
+
+from _util import (DEV, assert_bf16_close, assert_f32_close, bf, dev_as, dev_bf16, dev_cache,
+                   dev_f32, dev_i32, host, host_bits)
+
+pytestmark = pytest.mark.gpu
+R = np.random.default_rng(99)
+DTYPES = [torch.bfloat16, torch.float32]
+
+
+def rnd(*shape, scale=1.0, dtype=torch.bfloat16):
+    a = (R.standard_normal(shape) * scale).astype(np.float32)
+    return bf(a) if dtype == torch.bfloat16 else a
+
+
+def check(gpu, ref, dtype, what):
+    if dtype == torch.bfloat16:
+        return assert_bf16_close(gpu, ref, what)
+    return assert_f32_close(gpu, ref, what, max_abs=1e-3, rel=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (+ residual)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T,H", [(1, 256), (37, 4096), (5, 8192), (130, 1024)])
+def test_rmsnorm(dtype, T, H):
+    print(f"rmsnorm {dtype} T={T} H={H}", flush=True)
+    x = R.standard_normal((T, H)).astype(np.float32)
+    g = rnd(H, dtype=dtype) * 0 + bf(R.uniform(0.5, 1.5, H))
+    out = torch.empty(T, H, dtype=dtype, device=DEV)
+    dl.dl_rmsnorm_residual(dev_f32(x), dev_as(g, dtype), out, 1e-5)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    check(host(out), oracle.rmsnorm(x, g, 1e-5, mode=mode), dtype, "rmsnorm")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T,H", [(3, 256), (64, 4096), (17, 8192)])
+def test_rmsnorm_residual(dtype, T, H):
+    print(f"rmsnorm_residual {dtype} T={T} H={H}", flush=True)
+    o = rnd(T, H, dtype=dtype)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    g = bf(R.uniform(0.5, 1.5, H))
+    out = torch.empty(T, H, dtype=dtype, device=DEV)
+    rin = dev_f32(r)
+    hout = torch.empty_like(rin)
+    dl.dl_rmsnorm_residual(dev_as(o, dtype), dev_as(g, dtype), out, 1e-5, residual_in=rin,
+                           residual_out=hout)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    n_ref, h_ref = oracle.rmsnorm(o, g, 1e-5, resid=r, mode=mode)
+    assert np.array_equal(host(hout), h_ref)            # one fp32 add: exact
+    check(host(out), n_ref, dtype, "rmsnorm_residual")
+    # in-place residual (residual_out aliases residual_in)
+    dl.dl_rmsnorm_residual(dev_as(o, dtype), dev_as(g, dtype), out, 1e-5, residual_in=rin,
+                           residual_out=rin)
+    assert np.array_equal(host(rin), h_ref)
+
+
+# ---------------------------------------------------------------------------
+# projections: exact on small integers, close on random data
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [
+    (1, 256, 64), (5, 512, 200), (16, 1024, 256), (33, 768, 520), (64, 4096, 512),
+    (200, 1024, 4096), (600, 2048, 256), (2048, 16384, 320), (100, 96, 688),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_linear_exact_small_integers(dtype, M, N, K):
+    print(f"linear int {dtype} {M}x{N}x{K}", flush=True)
+    x = R.integers(-3, 4, (M, K)).astype(np.float32)
+    w = R.integers(-3, 4, (N, K)).astype(np.float32)
+    out = torch.empty(M, N, dtype=dtype, device=DEV)
+    dl.dl_linear(dev_as(x, dtype), dev_as(w, dtype), out)
+    rows = np.unique(np.concatenate([np.arange(min(M, 40)), R.integers(0, M, 24), [M - 1]]))
+    ref = oracle.linear(x[rows], w)
+    got = host(out)[rows]
+    if dtype == torch.bfloat16:
+        ref = bf(ref)     # |sum| < 2^24: exact in fp32; the bf16 store rounds once
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 256, 4096), (300, 1024, 1000), (2048, 4096, 512)])
+def test_linear_random_bf16(M, N, K):
+    print(f"linear rnd {M}x{N}x{K}", flush=True)
+    x = rnd(M, K)
+    w = rnd(N, K, scale=0.02)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dl.dl_linear(dev_bf16(x), dev_bf16(w), out)
+    rows = np.unique(np.concatenate([np.arange(min(M, 16)), R.integers(0, M, 16)]))
+    assert_bf16_close(host(out)[rows], oracle.linear(x[rows], w, round_bf16=True), "linear")
+
+
+QKV_CASES = [  # T, H, Hq, Hkv, D
+    (1, 256, 4, 4, 64), (37, 512, 8, 2, 128), (64, 1024, 8, 8, 128), (300, 512, 4, 1, 64),
+    (700, 1024, 8, 2, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T,H,Hq,Hkv,D", QKV_CASES)
+def test_qkv_rope(dtype, T, H, Hq, Hkv, D):
+    print(f"qkv_rope {dtype} T={T} H={H} {Hq}/{Hkv}x{D}", flush=True)
+    theta = 1e4
+    x = rnd(T, H, dtype=dtype)
+    wq, wk, wv = (rnd(h * D, H, scale=0.05, dtype=dtype) for h in (Hq, Hkv, Hkv))
+    pos = R.integers(0, 5000, T).astype(np.int32)
+    max_pos = 5000
+    cs = torch.empty(max_pos, D, device=DEV)
+    dl.dl_rope_table_fill(cs, max_pos, D, theta)
+    q = torch.empty(T, Hq, D, dtype=dtype, device=DEV)
+    k = torch.empty(T, Hkv, D, dtype=dtype, device=DEV)
+    v = torch.empty(T, Hkv, D, dtype=dtype, device=DEV)
+    dl.dl_qkv_rope(dev_as(x, dtype), dev_as(wq, dtype), dev_as(wk, dtype), dev_as(wv, dtype),
+                   dev_i32(pos), cs, q, k, v)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    rq, rk, rv = oracle.qkv_rope(x, wq, wk, wv, pos, theta, Hq, Hkv, D, mode=mode)
+    check(host(q), rq, dtype, "q")
+    check(host(k), rk, dtype, "k")
+    check(host(v), rv, dtype, "v")
+
+
+def test_rope_position_zero_and_table():
+    D, max_pos = 128, 40000
+    cs = torch.empty(max_pos, D, device=DEV)
+    dl.dl_rope_table_fill(cs, max_pos, D, 1e4)
+    tab = host(cs).reshape(max_pos, D // 2, 2).astype(np.float64)
+    assert np.all(tab[0, :, 0] == 1.0) and np.all(tab[0, :, 1] == 0.0)
+    np.testing.assert_allclose(tab[:, :, 0] ** 2 + tab[:, :, 1] ** 2, 1.0, atol=3e-7)
+    # angles taken in fp64: position 32767, pair 0 rotates by 32767 rad
+    assert tab[32767, 0, 0] == np.float32(np.cos(32767.0))
+    assert tab[32767, 0, 1] == np.float32(np.sin(32767.0))
+    # identity at position 0 through the fused epilogue: q equals the plain projection
+    T, H = 8, 256
+    x = rnd(T, H)
+    w = rnd(D, H, scale=0.05)
+    q = torch.empty(T, 1, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    dl.dl_qkv_rope(dev_bf16(x), dev_bf16(w), dev_bf16(w), dev_bf16(w), dev_i32(np.zeros(T)), cs,
+                   q, k, v)
+    assert torch.equal(q, v) and torch.equal(k, v)
+
+
+# ---------------------------------------------------------------------------
+# FFN
+# ---------------------------------------------------------------------------
+
+FFN_CASES = [(1, 256, 688), (29, 512, 1376), (64, 1024, 2048), (520, 512, 1024)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T,H,I", FFN_CASES)
+def test_gate_up_silu_and_down(dtype, T, H, I):
+    print(f"ffn {dtype} T={T} H={H} I={I}", flush=True)
+    x = rnd(T, H, dtype=dtype)
+    wg, wu = (rnd(I, H, scale=0.05, dtype=dtype) for _ in range(2))
+    wd = rnd(H, I, scale=0.05, dtype=dtype)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    a = torch.empty(T, I, dtype=dtype, device=DEV)
+    dl.dl_gate_up_silu(dev_as(x, dtype), dev_as(wg, dtype), dev_as(wu, dtype), a)
+    check(host(a), oracle.swiglu(x, wg, wu, mode=mode), dtype, "a")
+    # stage 2 on the GPU's own a
+    ag = host(a)
+    y = torch.empty(T, H, device=DEV)
+    dl.dl_down_residual(a, dev_as(wd, dtype), y, residual=dev_f32(r))
+    tol = dict(max_abs=3e-2, rel=1e-2) if dtype == torch.bfloat16 else dict(max_abs=1e-3, rel=1e-5)
+    assert_f32_close(host(y), oracle.down_residual(ag, wd, r), "down+resid", **tol)
+    # whole FFN
+    y2 = torch.empty(T, H, device=DEV)
+    dl.dl_ffn_swiglu(dev_as(x, dtype), dev_as(wg, dtype), dev_as(wu, dtype), dev_as(wd, dtype),
+                     y2, residual=dev_f32(r))
+    assert torch.equal(y, y2)      # same kernels, same order
+    assert_f32_close(host(y2), oracle.ffn(x, wg, wu, wd, r, mode=mode), "ffn", **tol)
+
+
+# ---------------------------------------------------------------------------
+# reshape_and_cache: bit-exact, sentinels untouched
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg_id", [1, 4])
+def test_reshape_and_cache_bit_exact(cfg_id):
+    cfg = gen.CONFIGS[cfg_id]
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    lens = [1, cfg.block_size - 1, cfg.block_size, cfg.block_size + 1, 3 * cfg.block_size + 5]
+    pb = gen.packed(lens)
+    bt = gen.block_table(cfg, pb.lens)
+    kbits, vbits = gen.empty_cache(cfg, bt.num_blocks)
+    k = rnd(pb.T, cfg.n_kv_heads, cfg.head_dim, dtype=dtype)
+    v = rnd(pb.T, cfg.n_kv_heads, cfg.head_dim, dtype=dtype)
+    kc, vc = dev_cache(kbits), dev_cache(vbits)
+    dl.dl_reshape_and_cache(dev_as(k, dtype), dev_as(v, dtype), dev_i32(pb.seq_of_token),
+                            dev_i32(pb.positions), dev_i32(bt.table), kc, vc)
+    okc, ovc = gen.cache_to_f32(kbits).copy(), gen.cache_to_f32(vbits).copy()
+    oracle.reshape_and_cache(k, v, pb.seq_of_token, pb.positions, bt.table, okc, ovc)
+    got_k, got_v = host_bits(kc), host_bits(vc)
+    want_k = gen.bf16_bits(okc) if dtype == torch.bfloat16 else okc.view(np.uint32)
+    want_v = gen.bf16_bits(ovc) if dtype == torch.bfloat16 else ovc.view(np.uint32)
+    if dtype == torch.bfloat16:   # NaN sentinel bits survive the f32 round trip unchanged
+        want_k = np.where(np.isnan(okc), kbits, want_k)
+        want_v = np.where(np.isnan(ovc), vbits, want_v)
+    assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [  # lens, Hq, Hkv, D
+    ([32], 4, 4, 64), ([1, 7, 130, 64], 4, 2, 128), ([300, 129], 8, 1, 128), ([257], 2, 2, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("lens,Hq,Hkv,D", PREFILL_CASES)
+def test_attn_prefill(dtype, lens, Hq, Hkv, D):
+    print(f"attn_prefill {dtype} {lens} {Hq}/{Hkv}x{D}", flush=True)
+    pb = gen.packed(lens)
+    q = rnd(pb.T, Hq, D, dtype=dtype)
+    k = rnd(pb.T, Hkv, D, dtype=dtype)
+    v = rnd(pb.T, Hkv, D, dtype=dtype)
+    out = torch.empty(pb.T, Hq, D, dtype=dtype, device=DEV)
+    dl.dl_attn_prefill(dev_as(q, dtype), dev_as(k, dtype), dev_as(v, dtype),
+                       dev_i32(pb.cu_seqlens), pb.max_seqlen, out)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    ref = oracle.attn_prefill(q, k, v, pb.cu_seqlens, mode=mode)
+    if dtype == torch.bfloat16:
+        assert_bf16_close(host(out), ref, "attn_prefill")
+    else:
+        assert_f32_close(host(out), ref, "attn_prefill", max_abs=1e-4, rel=1e-5)
+
+
+def test_attn_prefill_identical_keys_mean_and_first_row():
+    S, Hq, D = 100, 2, 128
+    q = rnd(S, Hq, D)
+    k = np.broadcast_to(rnd(D), (S, 1, D)).copy()
+    v = rnd(S, 1, D)
+    out = torch.empty(S, Hq, D, dtype=torch.bfloat16, device=DEV)
+    dl.dl_attn_prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32([0, S]), S, out)
+    got = host(out)
+    assert np.array_equal(got[0, 0], v[0, 0]) and np.array_equal(got[0, 1], v[0, 0])
+    mean = np.cumsum(v[:, 0].astype(np.float64), 0) / np.arange(1, S + 1)[:, None]
+    assert_bf16_close(got[:, 1], bf(mean), "mean of v")
+
+
+def _decode_setup(cfg, B, ctx, Hq, Hkv, D, dtype, identity=False):
+    import dataclasses
+    c = dataclasses.replace(cfg, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                            dtype="bf16" if dtype == torch.bfloat16 else "f32")
+    bt = gen.block_table(c, ctx, identity=identity)
+    kbits, vbits = gen.synthetic_cache(c, bt, np.asarray(ctx) + 1)   # fill 0..ctx-1
+    return c, bt, kbits, vbits
+
+
+DECODE_CASES = [  # B, ctx list, Hq, Hkv, D, BS
+    (1, [1], 4, 4, 64, 16), (3, [5, 16, 17], 4, 4, 64, 16), (4, [130, 1, 700, 2049], 8, 1, 128, 128),
+    (5, [127, 128, 129, 300, 64], 32, 8, 128, 128), (2, [4096, 3000], 8, 8, 128, 128),
+    (3, [33, 64, 65], 8, 4, 64, 32),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("B,ctx,Hq,Hkv,D,BS", DECODE_CASES)
+def test_attn_decode_paged(dtype, B, ctx, Hq, Hkv, D, BS):
+    print(f"attn_decode {dtype} ctx={ctx} {Hq}/{Hkv}x{D} BS={BS}", flush=True)
+    import dataclasses
+    cfg = dataclasses.replace(gen.CONFIGS[4], block_size=BS)
+    c, bt, kbits, vbits = _decode_setup(cfg, B, ctx, Hq, Hkv, D, dtype)
+    ctx = np.asarray(ctx, np.int32)
+    q = rnd(B, Hq, D, dtype=dtype)
+    out = torch.empty(B, Hq, D, dtype=dtype, device=DEV)
+    kc, vc = dev_cache(kbits), dev_cache(vbits)
+    dl.dl_attn_decode_paged(dev_as(q, dtype), kc, vc, dev_i32(bt.table), dev_i32(ctx),
+                            int(ctx.max()), out)
+    mode = oracle.BF16 if dtype == torch.bfloat16 else oracle.EXACT
+    ref = oracle.attn_decode_paged(q, gen.cache_to_f32(kbits), gen.cache_to_f32(vbits), bt.table,
+                                   ctx, mode=mode)
+    if dtype == torch.bfloat16:
+        assert_bf16_close(host(out), ref, "attn_decode")
+    else:
+        assert_f32_close(host(out), ref, "attn_decode", max_abs=1e-4, rel=1e-5)
+
+
+def test_attn_decode_permutation_bit_identical():
+    cfg = gen.CONFIGS[4]
+    ctx = np.array([513, 128, 1000, 7], np.int32)
+    outs = []
+    for identity in (True, False):
+        c, bt, kbits, vbits = _decode_setup(cfg, 4, ctx, 32, 8, 128, torch.bfloat16, identity)
+        q = rnd(4, 32, 128) if identity else q
+        out = torch.empty(4, 32, 128, dtype=torch.bfloat16, device=DEV)
+        dl.dl_attn_decode_paged(dev_bf16(q), dev_cache(kbits), dev_cache(vbits), dev_i32(bt.table),
+                                dev_i32(ctx), int(ctx.max()), out)
+        outs.append(host_bits(out))
+    assert np.array_equal(outs[0], outs[1])

@@ -1,0 +1,247 @@
+// attn_prefill.hip -- causal, variable-length, grouped-query flash attention
+// for prefill (gfx950 MFMA).
+//
+// What it computes: for every packed sequence b (rows cu_seqlens[b] ..
+// cu_seqlens[b+1]-1), every query head h and every query row i, the softmax of
+// scale * q_i . k_j over the keys j <= i of the same sequence, applied to V.
+// K/V head = h / (Hq / Hkv).  Prefill sends the whole sequence through a
+// single attention kernel that never writes the score matrix to memory (ATB
+// fusion-strategy page, "Attention fusion"; ops-transformer Llama2-7B page,
+// "KV cache and operators": prefill runs the full sequence through
+// FlashAttention).
+//
+// Layout: q [T][Hq][D], k/v [T][Hkv][D], out [T][Hq][D].
+//
+// Mapping: one workgroup = 4 waves x QW query rows of one head; keys are
+// streamed in tiles of 64 through LDS (K row-major, V transposed so the PV
+// operand reads are contiguous).  The MFMA computes S^T = K Q^T so each lane
+// owns one query column: the row statistics of the online softmax reduce in
+// registers plus two cross-lane steps, P^T feeds the PV MFMA straight from
+// the score registers (the key order inside an MFMA k-group is permuted the
+// same way for both operands), and O^T accumulates with one query per lane,
+// which makes the rescale by exp2(m_old - m_new) a per-lane multiply.
+#include "dl_internal.hpp"
+
+namespace dl {
+
+__device__ __forceinline__ void make_frag(Frag<bf16>& f, f32x4 a, f32x4 b) {
+  f.v = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+               (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+__device__ __forceinline__ void make_frag(Frag<float>& f, f32x4 a, f32x4 b) {
+  f.lo = a;
+  f.hi = b;
+}
+__device__ __forceinline__ void load_frag2(Frag<bf16>& f, const bf16* p0, const bf16* p1) {
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(p0);
+  const bf16x4 y = *reinterpret_cast<const bf16x4*>(p1);
+  f.v = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+__device__ __forceinline__ void load_frag2(Frag<float>& f, const float* p0, const float* p1) {
+  f.lo = *reinterpret_cast<const f32x4*>(p0);
+  f.hi = *reinterpret_cast<const f32x4*>(p1);
+}
+
+template <typename T>
+struct Pair2 {
+  typedef T type __attribute__((ext_vector_type(2)));
+};
+
+constexpr int kPfWaves = 4;
+constexpr int kPfBKV = 64;
+
+template <typename T, int D, int QW>
+__global__ void __launch_bounds__(kPfWaves * kWave)
+attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                    const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2,
+                    T* __restrict__ out, int n_qtiles) {
+  constexpr int NT = kPfWaves * kWave, BQ = kPfWaves * QW, BKV = kPfBKV;
+  constexpr int QS = QW / 16, KTS = BKV / 16, DC = D / 32, DS = D / 16, KC = BKV / 32;
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int KLS = D + VE;        // padded K row (16 B)
+  constexpr int VLS = BKV + VE;      // padded V^T row (16 B)
+  __shared__ __attribute__((aligned(16))) T Ks[BKV * KLS];
+  __shared__ __attribute__((aligned(16))) T Vt[D * VLS];
+
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int qt = n_qtiles - 1 - (int)blockIdx.x;  // heavy (late) tiles first
+  const int t0 = cu[b], S = cu[b + 1] - t0;
+  const int q_begin = qt * BQ;
+  if (q_begin >= S) return;
+  const int g = h / (Hq / Hkv);
+  const int kv_end = min(S, q_begin + BQ);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const int qw0 = q_begin + wave * QW;
+
+  Frag<T> qf[QS][DC];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int qi = qw0 + qs * 16 + fr;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      if (qi < S)
+        qf[qs][dc].load(q + ((int64_t)(t0 + qi) * Hq + h) * D + dc * 32 + 8 * fg);
+      else
+        qf[qs][dc].zero();
+    }
+  }
+
+  f32x4 o[DS][QS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) o[ds][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_i[QS], l_i[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    m_i[qs] = -INFINITY;
+    l_i[qs] = 0.f;
+  }
+
+  const u32x4 zero = {0, 0, 0, 0};
+  for (int kt = 0; kt < nkv; ++kt) {
+    const int kv0 = kt * BKV;
+    __syncthreads();
+    // K tile, row-major
+    for (int i = tid; i < BKV * (D / VE); i += NT) {
+      const int key = i / (D / VE), c = i % (D / VE);
+      const u32x4 val = (kv0 + key < kv_end)
+                            ? ld16(k + ((int64_t)(t0 + kv0 + key) * Hkv + g) * D + c * VE)
+                            : zero;
+      st16(Ks + key * KLS + c * VE, val);
+    }
+    // V tile, transposed: each thread takes two adjacent keys and VE d-values
+    for (int i = tid; i < (BKV / 2) * (D / VE); i += NT) {
+      const int kp = i % (BKV / 2), c = i / (BKV / 2);
+      const int key0 = 2 * kp;
+      const u32x4 a = (kv0 + key0 < kv_end)
+                          ? ld16(v + ((int64_t)(t0 + kv0 + key0) * Hkv + g) * D + c * VE)
+                          : zero;
+      const u32x4 bb = (kv0 + key0 + 1 < kv_end)
+                           ? ld16(v + ((int64_t)(t0 + kv0 + key0 + 1) * Hkv + g) * D + c * VE)
+                           : zero;
+      T ea[VE], eb[VE];
+      __builtin_memcpy(ea, &a, 16);
+      __builtin_memcpy(eb, &bb, 16);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        typename Pair2<T>::type pr = {ea[e], eb[e]};
+        *reinterpret_cast<typename Pair2<T>::type*>(Vt + (c * VE + e) * VLS + key0) = pr;
+      }
+    }
+    __syncthreads();
+
+    // S^T = K Q^T  (rows: keys, cols: queries)
+    f32x4 s[KTS][QS];
+#pragma unroll
+    for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) s[ks][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      Frag<T> kf[KTS];
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks) kf[ks].load(Ks + (ks * 16 + fr) * KLS + dc * 32 + 8 * fg);
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) s[ks][qs] = mfma_k32(kf[ks], qf[qs][dc], s[ks][qs]);
+    }
+
+    // causal mask, scale (log2 domain), online softmax per query column
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      const int qi = qw0 + qs * 16 + fr;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kv0 + ks * 16 + 4 * fg + j;
+          const float val = (key <= qi && key < kv_end) ? s[ks][qs][j] * scale_log2 : -INFINITY;
+          s[ks][qs][j] = val;
+          mx = fmaxf(mx, val);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_i[qs], mx);
+      const float alpha = exp2f(m_i[qs] - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = exp2f(s[ks][qs][j] - m_new);
+          s[ks][qs][j] = p;
+          ls += p;
+        }
+      l_i[qs] = l_i[qs] * alpha + ls;
+      m_i[qs] = m_new;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) o[ds][qs] *= alpha;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      Frag<T> pf[QS];
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) make_frag(pf[qs], s[2 * kc][qs], s[2 * kc + 1][qs]);
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        Frag<T> vf;
+        const T* row = Vt + (ds * 16 + fr) * VLS + kc * 32 + 4 * fg;
+        load_frag2(vf, row, row + 16);
+#pragma unroll
+        for (int qs = 0; qs < QS; ++qs) o[ds][qs] = mfma_k32(vf, pf[qs], o[ds][qs]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    float l = l_i[qs];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = 1.0f / l;
+    const int qi = qw0 + qs * 16 + fr;
+    if (qi < S) {
+      T* dst = out + ((int64_t)(t0 + qi) * Hq + h) * D + 4 * fg;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        store4(dst + ds * 16, o[ds][qs][0] * inv, o[ds][qs][1] * inv, o[ds][qs][2] * inv,
+               o[ds][qs][3] * inv);
+    }
+  }
+}
+
+template <typename T>
+hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_seqlens, int B,
+                        int max_seqlen, int Hq, int Hkv, int D, float scale, T* out,
+                        hipStream_t st) {
+  constexpr int QW = 32;
+  constexpr int BQ = kPfWaves * QW;
+  if (B == 0 || max_seqlen == 0) return hipSuccess;
+  const int n_qtiles = (max_seqlen + BQ - 1) / BQ;
+  const float sl2 = scale * 1.4426950408889634f;
+  dim3 grid(n_qtiles, Hq, B), block(kPfWaves * kWave);
+  if (D == 128)
+    hipLaunchKernelGGL((attn_prefill_kernel<T, 128, QW>), grid, block, 0, st, q, k, v, cu_seqlens,
+                       Hq, Hkv, sl2, out, n_qtiles);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_prefill_kernel<T, 64, QW>), grid, block, 0, st, q, k, v, cu_seqlens,
+                       Hq, Hkv, sl2, out, n_qtiles);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template hipError_t attn_prefill<bf16>(const bf16*, const bf16*, const bf16*, const int32_t*, int,
+                                       int, int, int, int, float, bf16*, hipStream_t);
+template hipError_t attn_prefill<float>(const float*, const float*, const float*, const int32_t*,
+                                        int, int, int, int, int, float, float*, hipStream_t);
+
+}  // namespace dl

@@ -1,0 +1,714 @@
+// capi.hip -- the extern "C" boundary: argument validation, workspace
+// planning and carving, and the layer composition (fused and kernel-per-op).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/dl_layer.h"
+#include "dl_internal.hpp"
+
+using namespace dl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dl_status fail(dl_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dl_status fail(dl_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+dl_status ok() {
+  g_last_error.clear();
+  return DL_OK;
+}
+
+dl_status hip_fail(hipError_t e, const char* where) {
+  return fail(DL_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define DL_HIP(call, where)                      \
+  do {                                           \
+    hipError_t e_ = (call);                      \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(dl_dtype dt) { return dt == DL_BF16 ? 2 : 4; }
+
+// ---- shared checks ---------------------------------------------------------
+#define CHECK_PTR(p)                                                          \
+  do {                                                                        \
+    if (!(p)) return fail(DL_ERR_INVALID_ARG, "%s must not be NULL", #p);    \
+    if (!aligned16(p)) return fail(DL_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define CHECK_PTR_OPT(p)                                                      \
+  do {                                                                        \
+    if ((p) && !aligned16(p)) return fail(DL_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define CHECK_IDX(p)                                                          \
+  do {                                                                        \
+    if (!(p)) return fail(DL_ERR_INVALID_ARG, "%s must not be NULL", #p);    \
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0)                           \
+      return fail(DL_ERR_ALIGNMENT, "%s is not 4-byte aligned", #p);         \
+  } while (0)
+
+dl_status check_dtype(dl_dtype dt) {
+  if (dt != DL_F32 && dt != DL_BF16) return fail(DL_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  return DL_OK;
+}
+
+dl_status check_heads(int Hq, int Hkv, int D) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0) return fail(DL_ERR_INVALID_ARG, "heads/head_dim must be positive");
+  if (Hq % Hkv) return fail(DL_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  const int g = Hq / Hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(DL_ERR_UNSUPPORTED, "Hq/Hkv = %d not in {1,2,4,8}", g);
+  if (D != 64 && D != 128) return fail(DL_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", D);
+  return DL_OK;
+}
+
+dl_status check_hidden(int H) {
+  if (H <= 0) return fail(DL_ERR_INVALID_ARG, "hidden must be positive");
+  if (H % 32 || H > 8192) return fail(DL_ERR_UNSUPPORTED, "hidden %d must be a multiple of 32 and <= 8192", H);
+  return DL_OK;
+}
+
+dl_status check_inter(int I) {
+  if (I <= 0) return fail(DL_ERR_INVALID_ARG, "intermediate must be positive");
+  if (I % 16) return fail(DL_ERR_UNSUPPORTED, "intermediate %d must be a multiple of 16", I);
+  return DL_OK;
+}
+
+dl_status check_bs(int BS) {
+  if (BS != 16 && BS != 32 && BS != 64 && BS != 128)
+    return fail(DL_ERR_UNSUPPORTED, "block_size %d not in {16,32,64,128}", BS);
+  return DL_OK;
+}
+
+#define TRY(expr)                  \
+  do {                             \
+    dl_status s_ = (expr);         \
+    if (s_ != DL_OK) return s_;    \
+  } while (0)
+
+// ---- GEMM plans used by each step -----------------------------------------
+GemmPlan plan_qkv(int M, int H, int Hq, int Hkv, int D, dl_dtype dt) {
+  return plan_gemm(M, (Hq + 2 * Hkv) * D, H, dt == DL_F32, true);
+}
+GemmPlan plan_lin(int M, int N, int K, dl_dtype dt) { return plan_gemm(M, N, K, dt == DL_F32, false); }
+GemmPlan plan_gu(int M, int H, int I, dl_dtype dt) { return plan_gemm(M, 2 * I, H, dt == DL_F32, true); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- layer workspace layout -------------------------------------------------
+enum Buf { kN1, kQ, kK, kV, kAttn, kO, kH, kN2, kA, kPart, kDec, kS, kP, kG, kU, kSG, kDd, kNBuf };
+
+struct Layout {
+  size_t off[kNBuf];
+  size_t size[kNBuf];
+  size_t total;
+};
+
+size_t part_bytes(const dl_layer_dims* d, int M, dl_mode m) {
+  const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
+            I = d->intermediate;
+  const dl_dtype dt = d->dtype;
+  size_t p = 0;
+  if (m == DL_FUSED) {
+    p = std::max(p, plan_qkv(M, H, Hq, Hkv, D, dt).ws_bytes);
+    p = std::max(p, plan_gu(M, H, I, dt).ws_bytes);
+  } else {
+    p = std::max(p, plan_lin(M, Hq * D, H, dt).ws_bytes);
+    p = std::max(p, plan_lin(M, Hkv * D, H, dt).ws_bytes);
+    p = std::max(p, plan_lin(M, I, H, dt).ws_bytes);
+  }
+  p = std::max(p, plan_lin(M, H, Hq * D, dt).ws_bytes);
+  p = std::max(p, plan_lin(M, H, I, dt).ws_bytes);
+  return p;
+}
+
+// is_decode: T = B tokens, S_or_ctx = max context; else S_or_ctx = max_seqlen
+Layout layout(const dl_layer_dims* d, int T, int B, int S_or_ctx, bool is_decode, dl_mode m,
+              size_t part) {
+  const size_t es = esize(d->dtype);
+  const size_t H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
+               I = d->intermediate;
+  Layout L{};
+  L.size[kN1] = T * H * es;
+  L.size[kQ] = T * Hq * D * es;
+  L.size[kK] = T * Hkv * D * es;
+  L.size[kV] = T * Hkv * D * es;
+  L.size[kAttn] = T * Hq * D * es;
+  L.size[kO] = T * H * es;
+  L.size[kH] = T * H * 4;
+  L.size[kN2] = T * H * es;
+  L.size[kA] = T * I * es;
+  L.size[kPart] = part;
+  L.size[kDec] = is_decode && m == DL_FUSED
+                     ? plan_decode(B, (int)Hq, (int)Hkv, (int)D, S_or_ctx, d->block_size).ws_bytes
+                     : 0;
+  if (m == DL_UNFUSED) {
+    const size_t rows = is_decode ? (size_t)B * Hq : (size_t)B * Hq * S_or_ctx;
+    L.size[kS] = rows * S_or_ctx * 4;
+    L.size[kP] = rows * S_or_ctx * es;
+    L.size[kG] = T * I * es;
+    L.size[kU] = T * I * es;
+    L.size[kSG] = T * I * es;
+    L.size[kDd] = T * H * 4;
+  }
+  size_t o = 0;
+  for (int i = 0; i < kNBuf; ++i) {
+    L.off[i] = o;
+    o += align256(L.size[i]);
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, const Layout& L, Buf b) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + L.off[b]);
+}
+
+dl_status check_dims(const dl_layer_dims* d) {
+  if (!d) return fail(DL_ERR_INVALID_ARG, "dims must not be NULL");
+  TRY(check_dtype(d->dtype));
+  TRY(check_hidden(d->hidden));
+  TRY(check_heads(d->n_q_heads, d->n_kv_heads, d->head_dim));
+  TRY(check_inter(d->intermediate));
+  TRY(check_bs(d->block_size));
+  if (!(d->rms_eps >= 0.f)) return fail(DL_ERR_INVALID_ARG, "rms_eps must be >= 0");
+  if ((d->n_q_heads * d->head_dim) % 32)
+    return fail(DL_ERR_UNSUPPORTED, "Hq*D must be a multiple of 32");
+  return DL_OK;
+}
+
+dl_status check_weights(const dl_layer_weights* w) {
+  if (!w) return fail(DL_ERR_INVALID_ARG, "weights must not be NULL");
+  CHECK_PTR(w->ln1_gamma);
+  CHECK_PTR(w->w_q);
+  CHECK_PTR(w->w_k);
+  CHECK_PTR(w->w_v);
+  CHECK_PTR(w->w_o);
+  CHECK_PTR(w->ln2_gamma);
+  CHECK_PTR(w->w_gate);
+  CHECK_PTR(w->w_up);
+  CHECK_PTR(w->w_down);
+  return DL_OK;
+}
+
+dl_status check_cache(const dl_kv_cache* c) {
+  if (!c) return fail(DL_ERR_INVALID_ARG, "cache must not be NULL");
+  CHECK_PTR(c->k_cache);
+  CHECK_PTR(c->v_cache);
+  if (c->num_blocks <= 0) return fail(DL_ERR_INVALID_ARG, "cache num_blocks must be positive");
+  return DL_OK;
+}
+
+// ---- layer bodies ------------------------------------------------------------
+template <typename T>
+dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const float* cs,
+                     int max_pos, const float* x, float* y, const int32_t* pos, const int32_t* seq,
+                     const int32_t* cu, const int32_t* ctx, int B, int Tn, int S_or_ctx,
+                     bool is_decode, const dl_kv_cache* cache, const int32_t* bt, int maxblk,
+                     dl_mode m, void* ws, const Layout& L, hipStream_t st) {
+  const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
+            I = d->intermediate, BS = d->block_size;
+  const dl_dtype dt = d->dtype;
+  const float scale = 1.0f / sqrtf((float)D);
+  T* n1 = at<T>(ws, L, kN1);
+  T* q = at<T>(ws, L, kQ);
+  T* k = at<T>(ws, L, kK);
+  T* v = at<T>(ws, L, kV);
+  T* attn = at<T>(ws, L, kAttn);
+  T* o = at<T>(ws, L, kO);
+  float* h = at<float>(ws, L, kH);
+  T* n2 = at<T>(ws, L, kN2);
+  T* a = at<T>(ws, L, kA);
+  void* part = at<void>(ws, L, kPart);
+  const T* g1 = static_cast<const T*>(w->ln1_gamma);
+  const T* g2 = static_cast<const T*>(w->ln2_gamma);
+  const T* wq = static_cast<const T*>(w->w_q);
+  const T* wk = static_cast<const T*>(w->w_k);
+  const T* wv = static_cast<const T*>(w->w_v);
+  const T* wo = static_cast<const T*>(w->w_o);
+  const T* wg = static_cast<const T*>(w->w_gate);
+  const T* wu = static_cast<const T*>(w->w_up);
+  const T* wd = static_cast<const T*>(w->w_down);
+  T* kc = static_cast<T*>(cache->k_cache);
+  T* vc = static_cast<T*>(cache->v_cache);
+
+  DL_HIP((rmsnorm_residual<float, T>(x, nullptr, nullptr, g1, n1, Tn, H, d->rms_eps, st)), "norm1");
+  if (m == DL_FUSED) {
+    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, k, v, Tn, H, Hq, Hkv, D,
+                            plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st), "qkv_rope");
+  } else {
+    DL_HIP((gemm_linear<T, T>(n1, wq, q, Tn, Hq * D, H, plan_lin(Tn, Hq * D, H, dt), part, st)), "q");
+    DL_HIP((gemm_linear<T, T>(n1, wk, k, Tn, Hkv * D, H, plan_lin(Tn, Hkv * D, H, dt), part, st)), "k");
+    DL_HIP((gemm_linear<T, T>(n1, wv, v, Tn, Hkv * D, H, plan_lin(Tn, Hkv * D, H, dt), part, st)), "v");
+    DL_HIP(unf_rope<T>(q, pos, cs, max_pos, Tn, Hq, D, st), "rope q");
+    DL_HIP(unf_rope<T>(k, pos, cs, max_pos, Tn, Hkv, D, st), "rope k");
+  }
+  DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
+                              cache->num_blocks, st), "reshape_and_cache");
+  if (!is_decode) {
+    if (m == DL_FUSED) {
+      DL_HIP(attn_prefill<T>(q, k, v, cu, B, S_or_ctx, Hq, Hkv, D, scale, attn, st), "attn_prefill");
+    } else {
+      float* S = at<float>(ws, L, kS);
+      T* P = at<T>(ws, L, kP);
+      DL_HIP(unf_scores<T>(q, k, cu, B, S_or_ctx, Hq, Hkv, D, scale, S, st), "scores");
+      DL_HIP(unf_softmax<T>(S, P, cu, true, B, S_or_ctx, Hq, S_or_ctx, st), "softmax");
+      DL_HIP(unf_pv<T>(P, v, cu, B, S_or_ctx, Hq, Hkv, D, attn, st), "pv");
+    }
+  } else {
+    if (m == DL_FUSED) {
+      const DecodePlan dp = plan_decode(B, Hq, Hkv, D, S_or_ctx, BS);
+      DL_HIP(attn_decode_paged<T>(q, kc, vc, bt, maxblk, ctx, B, Hq, Hkv, D, BS, scale, attn, dp,
+                                  at<void>(ws, L, kDec), cache->num_blocks, st), "attn_decode");
+    } else {
+      DL_HIP(unf_dec_attn<T>(q, kc, vc, bt, maxblk, ctx, S_or_ctx, B, Hq, Hkv, D, BS, scale,
+                             at<float>(ws, L, kS), at<T>(ws, L, kP), attn, cache->num_blocks, st),
+             "dec_attn");
+    }
+  }
+  DL_HIP((gemm_linear<T, T>(attn, wo, o, Tn, H, Hq * D, plan_lin(Tn, H, Hq * D, dt), part, st)), "o_proj");
+  if (m == DL_FUSED) {
+    DL_HIP((rmsnorm_residual<T, T>(o, x, h, g2, n2, Tn, H, d->rms_eps, st)), "norm2");
+    DL_HIP(gemm_swiglu<T>(n2, wg, wu, a, Tn, H, I, plan_gu(Tn, H, I, dt), part, st), "gate_up");
+    DL_HIP(gemm_linear_resid<T>(a, wd, h, y, Tn, H, I, plan_lin(Tn, H, I, dt), part, st), "down");
+  } else {
+    T* g = at<T>(ws, L, kG);
+    T* u = at<T>(ws, L, kU);
+    T* sg = at<T>(ws, L, kSG);
+    float* dd = at<float>(ws, L, kDd);
+    const int64_t nth = (int64_t)Tn * H, nti = (int64_t)Tn * I;
+    DL_HIP(unf_add<T>(x, o, h, nth, st), "add1");
+    DL_HIP((rmsnorm_residual<float, T>(h, nullptr, nullptr, g2, n2, Tn, H, d->rms_eps, st)), "norm2");
+    DL_HIP((gemm_linear<T, T>(n2, wg, g, Tn, I, H, plan_lin(Tn, I, H, dt), part, st)), "gate");
+    DL_HIP((gemm_linear<T, T>(n2, wu, u, Tn, I, H, plan_lin(Tn, I, H, dt), part, st)), "up");
+    DL_HIP(unf_silu<T>(g, sg, nti, st), "silu");
+    DL_HIP(unf_mul<T>(sg, u, a, nti, st), "mul");
+    DL_HIP((gemm_linear<T, float>(a, wd, dd, Tn, H, I, plan_lin(Tn, H, I, dt), part, st)), "down");
+    DL_HIP(unf_add<float>(h, dd, y, nth, st), "add2");
+  }
+  return ok();
+}
+
+}  // namespace
+
+// ============================================================================
+// extern "C"
+// ============================================================================
+extern "C" {
+
+const char* dl_status_string(dl_status s) {
+  switch (s) {
+    case DL_OK: return "DL_OK";
+    case DL_ERR_INVALID_ARG: return "DL_ERR_INVALID_ARG";
+    case DL_ERR_UNSUPPORTED: return "DL_ERR_UNSUPPORTED";
+    case DL_ERR_ALIGNMENT: return "DL_ERR_ALIGNMENT";
+    case DL_ERR_WORKSPACE: return "DL_ERR_WORKSPACE";
+    case DL_ERR_HIP: return "DL_ERR_HIP";
+  }
+  return "DL_ERR_UNKNOWN";
+}
+
+const char* dl_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dl_abi_version(void) { return 1; }
+
+dl_status dl_rope_table_fill(float* cos_sin, int32_t max_pos, int32_t head_dim, double theta,
+                             void* stream) {
+  CHECK_PTR(cos_sin);
+  if (max_pos < 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be >= 0");
+  if (head_dim <= 0 || head_dim % 8) return fail(DL_ERR_UNSUPPORTED, "head_dim must be a positive multiple of 8");
+  if (!(theta > 0.0)) return fail(DL_ERR_INVALID_ARG, "theta must be > 0");
+  DL_HIP(rope_table_fill(cos_sin, max_pos, head_dim, theta, (hipStream_t)stream), "rope_table");
+  return ok();
+}
+
+dl_status dl_rmsnorm_residual(const void* x, dl_dtype x_dtype, const float* residual_in,
+                              float* residual_out, const void* gamma, void* out, int32_t T,
+                              int32_t H, float eps, dl_dtype out_dtype, void* stream) {
+  TRY(check_dtype(x_dtype));
+  TRY(check_dtype(out_dtype));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  TRY(check_hidden(H));
+  if (!(eps >= 0.f)) return fail(DL_ERR_INVALID_ARG, "eps must be >= 0");
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(gamma);
+  CHECK_PTR(out);
+  CHECK_PTR_OPT(residual_in);
+  if (residual_in) CHECK_PTR(residual_out);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (x_dtype == DL_F32 && out_dtype == DL_BF16)
+    e = rmsnorm_residual<float, bf16>((const float*)x, residual_in, residual_out, (const bf16*)gamma, (bf16*)out, T, H, eps, st);
+  else if (x_dtype == DL_BF16 && out_dtype == DL_BF16)
+    e = rmsnorm_residual<bf16, bf16>((const bf16*)x, residual_in, residual_out, (const bf16*)gamma, (bf16*)out, T, H, eps, st);
+  else if (x_dtype == DL_F32 && out_dtype == DL_F32)
+    e = rmsnorm_residual<float, float>((const float*)x, residual_in, residual_out, (const float*)gamma, (float*)out, T, H, eps, st);
+  else
+    e = rmsnorm_residual<bf16, float>((const bf16*)x, residual_in, residual_out, (const float*)gamma, (float*)out, T, H, eps, st);
+  DL_HIP(e, "rmsnorm");
+  return ok();
+}
+
+size_t dl_qkv_rope_workspace_size(int32_t T, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                                  dl_dtype dt) {
+  if (T <= 0 || H <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return 0;
+  return plan_qkv(T, H, Hq, Hkv, D, dt).ws_bytes;
+}
+
+dl_status dl_qkv_rope(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                      const int32_t* positions, const float* cos_sin, int32_t max_pos, void* q,
+                      void* k, void* v, int32_t T, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                      dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  TRY(check_heads(Hq, Hkv, D));
+  if (H <= 0 || H % 8) return fail(DL_ERR_UNSUPPORTED, "H must be a positive multiple of 8");
+  if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w_q);
+  CHECK_PTR(w_k);
+  CHECK_PTR(w_v);
+  CHECK_IDX(positions);
+  CHECK_PTR(cos_sin);
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  const GemmPlan pl = plan_qkv(T, H, Hq, Hkv, D, dt);
+  if (pl.ws_bytes > ws_bytes || (pl.ws_bytes && !ws))
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR_OPT(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? gemm_qkv_rope<bf16>((const bf16*)x, (const bf16*)w_q, (const bf16*)w_k, (const bf16*)w_v, positions, cos_sin, max_pos, (bf16*)q, (bf16*)k, (bf16*)v, T, H, Hq, Hkv, D, pl, ws, st)
+      : gemm_qkv_rope<float>((const float*)x, (const float*)w_q, (const float*)w_k, (const float*)w_v, positions, cos_sin, max_pos, (float*)q, (float*)k, (float*)v, T, H, Hq, Hkv, D, pl, ws, st);
+  DL_HIP(e, "qkv_rope");
+  return ok();
+}
+
+dl_status dl_reshape_and_cache(const void* k, const void* v, const int32_t* seq_of_token,
+                               const int32_t* positions, const int32_t* block_table,
+                               int32_t max_blocks_per_seq, const dl_kv_cache* cache, int32_t T,
+                               int32_t Hkv, int32_t D, int32_t BS, dl_dtype dt, void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0 || Hkv <= 0) return fail(DL_ERR_INVALID_ARG, "bad T/Hkv");
+  if (D != 64 && D != 128) return fail(DL_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", D);
+  TRY(check_bs(BS));
+  if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  TRY(check_cache(cache));
+  if (T == 0) return ok();
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  if (seq_of_token) CHECK_IDX(seq_of_token);
+  CHECK_IDX(positions);
+  CHECK_IDX(block_table);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? reshape_and_cache<bf16>((const bf16*)k, (const bf16*)v, seq_of_token, positions, block_table, max_blocks_per_seq, (bf16*)cache->k_cache, (bf16*)cache->v_cache, T, Hkv, D, BS, cache->num_blocks, st)
+      : reshape_and_cache<float>((const float*)k, (const float*)v, seq_of_token, positions, block_table, max_blocks_per_seq, (float*)cache->k_cache, (float*)cache->v_cache, T, Hkv, D, BS, cache->num_blocks, st);
+  DL_HIP(e, "reshape_and_cache");
+  return ok();
+}
+
+dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t max_seqlen,
+                          int32_t Hq, int32_t Hkv, int32_t D, float scale, void* out, dl_dtype dt,
+                          void* stream) {
+  TRY(check_dtype(dt));
+  TRY(check_heads(Hq, Hkv, D));
+  if (B < 0 || T < 0 || max_seqlen < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
+  if (B == 0 || T == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  CHECK_IDX(cu_seqlens);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? attn_prefill<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)v, cu_seqlens, B, max_seqlen, Hq, Hkv, D, scale, (bf16*)out, st)
+      : attn_prefill<float>((const float*)q, (const float*)k, (const float*)v, cu_seqlens, B, max_seqlen, Hq, Hkv, D, scale, (float*)out, st);
+  DL_HIP(e, "attn_prefill");
+  return ok();
+}
+
+size_t dl_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                     int32_t max_context_len, int32_t BS) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || max_context_len <= 0) return 0;
+  return plan_decode(B, Hq, Hkv, D, max_context_len, BS).ws_bytes;
+}
+
+dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, float scale,
+                               void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  TRY(check_heads(Hq, Hkv, D));
+  TRY(check_bs(BS));
+  if (B < 0) return fail(DL_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_context_len <= 0) return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * BS < max_context_len)
+    return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq * BS must cover max_context_len");
+  TRY(check_cache(cache));
+  if (B == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(out);
+  CHECK_IDX(block_table);
+  CHECK_IDX(context_lens);
+  const DecodePlan pl = plan_decode(B, Hq, Hkv, D, max_context_len, BS);
+  if (!ws || ws_bytes < pl.ws_bytes)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? attn_decode_paged<bf16>((const bf16*)q, (const bf16*)cache->k_cache, (const bf16*)cache->v_cache, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (bf16*)out, pl, ws, cache->num_blocks, st)
+      : attn_decode_paged<float>((const float*)q, (const float*)cache->k_cache, (const float*)cache->v_cache, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (float*)out, pl, ws, cache->num_blocks, st);
+  DL_HIP(e, "attn_decode_paged");
+  return ok();
+}
+
+size_t dl_linear_workspace_size(int32_t M, int32_t N, int32_t K, dl_dtype dt) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return plan_lin(M, N, K, dt).ws_bytes;
+}
+
+dl_status dl_linear(const void* x, const void* w, void* out, int32_t M, int32_t N, int32_t K,
+                    dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  if (M < 0 || N <= 0 || K <= 0) return fail(DL_ERR_INVALID_ARG, "bad M/N/K");
+  if (N % 16 || K % 8) return fail(DL_ERR_UNSUPPORTED, "N must be a multiple of 16 and K of 8");
+  if (M == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w);
+  CHECK_PTR(out);
+  const GemmPlan pl = plan_lin(M, N, K, dt);
+  if (pl.ws_bytes > ws_bytes || (pl.ws_bytes && !ws))
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR_OPT(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? gemm_linear<bf16, bf16>((const bf16*)x, (const bf16*)w, (bf16*)out, M, N, K, pl, ws, st)
+      : gemm_linear<float, float>((const float*)x, (const float*)w, (float*)out, M, N, K, pl, ws, st);
+  DL_HIP(e, "linear");
+  return ok();
+}
+
+size_t dl_gate_up_silu_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt) {
+  if (T <= 0 || H <= 0 || I <= 0) return 0;
+  return plan_gu(T, H, I, dt).ws_bytes;
+}
+
+dl_status dl_gate_up_silu(const void* x, const void* w_gate, const void* w_up, void* a, int32_t T,
+                          int32_t H, int32_t I, dl_dtype dt, void* ws, size_t ws_bytes,
+                          void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  if (H <= 0 || H % 8) return fail(DL_ERR_UNSUPPORTED, "H must be a positive multiple of 8");
+  TRY(check_inter(I));
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w_gate);
+  CHECK_PTR(w_up);
+  CHECK_PTR(a);
+  const GemmPlan pl = plan_gu(T, H, I, dt);
+  if (pl.ws_bytes > ws_bytes || (pl.ws_bytes && !ws))
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR_OPT(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? gemm_swiglu<bf16>((const bf16*)x, (const bf16*)w_gate, (const bf16*)w_up, (bf16*)a, T, H, I, pl, ws, st)
+      : gemm_swiglu<float>((const float*)x, (const float*)w_gate, (const float*)w_up, (float*)a, T, H, I, pl, ws, st);
+  DL_HIP(e, "gate_up_silu");
+  return ok();
+}
+
+size_t dl_down_residual_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt) {
+  if (T <= 0 || H <= 0 || I <= 0) return 0;
+  return plan_lin(T, H, I, dt).ws_bytes;
+}
+
+dl_status dl_down_residual(const void* a, const void* w_down, const float* residual, float* out,
+                           int32_t T, int32_t H, int32_t I, dl_dtype dt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  TRY(check_hidden(H));
+  TRY(check_inter(I));
+  if (I % 8) return fail(DL_ERR_UNSUPPORTED, "I must be a multiple of 8");
+  if (T == 0) return ok();
+  CHECK_PTR(a);
+  CHECK_PTR(w_down);
+  CHECK_PTR_OPT(residual);
+  CHECK_PTR(out);
+  const GemmPlan pl = plan_lin(T, H, I, dt);
+  if (pl.ws_bytes > ws_bytes || (pl.ws_bytes && !ws))
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR_OPT(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (residual) {
+    e = dt == DL_BF16
+        ? gemm_linear_resid<bf16>((const bf16*)a, (const bf16*)w_down, residual, out, T, H, I, pl, ws, st)
+        : gemm_linear_resid<float>((const float*)a, (const float*)w_down, residual, out, T, H, I, pl, ws, st);
+  } else {
+    e = dt == DL_BF16
+        ? gemm_linear<bf16, float>((const bf16*)a, (const bf16*)w_down, out, T, H, I, pl, ws, st)
+        : gemm_linear<float, float>((const float*)a, (const float*)w_down, out, T, H, I, pl, ws, st);
+  }
+  DL_HIP(e, "down_residual");
+  return ok();
+}
+
+size_t dl_ffn_workspace_size(int32_t T, int32_t H, int32_t I, dl_dtype dt) {
+  if (T <= 0 || H <= 0 || I <= 0) return 0;
+  const size_t a = align256((size_t)T * I * esize(dt));
+  return a + std::max(plan_gu(T, H, I, dt).ws_bytes, plan_lin(T, H, I, dt).ws_bytes);
+}
+
+dl_status dl_ffn_swiglu(const void* x, const void* w_gate, const void* w_up, const void* w_down,
+                        const float* residual, float* out, int32_t T, int32_t H, int32_t I,
+                        dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  TRY(check_hidden(H));
+  TRY(check_inter(I));
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w_gate);
+  CHECK_PTR(w_up);
+  CHECK_PTR(w_down);
+  CHECK_PTR_OPT(residual);
+  CHECK_PTR(out);
+  const size_t need = dl_ffn_workspace_size(T, H, I, dt);
+  if (!ws || ws_bytes < need)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, need);
+  CHECK_PTR(ws);
+  void* a = ws;
+  void* part = static_cast<char*>(ws) + align256((size_t)T * I * esize(dt));
+  hipStream_t st = (hipStream_t)stream;
+  if (dt == DL_BF16) {
+    DL_HIP(gemm_swiglu<bf16>((const bf16*)x, (const bf16*)w_gate, (const bf16*)w_up, (bf16*)a, T, H, I, plan_gu(T, H, I, dt), part, st), "gate_up");
+    DL_HIP((residual ? gemm_linear_resid<bf16>((const bf16*)a, (const bf16*)w_down, residual, out, T, H, I, plan_lin(T, H, I, dt), part, st)
+                     : gemm_linear<bf16, float>((const bf16*)a, (const bf16*)w_down, out, T, H, I, plan_lin(T, H, I, dt), part, st)), "down");
+  } else {
+    DL_HIP(gemm_swiglu<float>((const float*)x, (const float*)w_gate, (const float*)w_up, (float*)a, T, H, I, plan_gu(T, H, I, dt), part, st), "gate_up");
+    DL_HIP((residual ? gemm_linear_resid<float>((const float*)a, (const float*)w_down, residual, out, T, H, I, plan_lin(T, H, I, dt), part, st)
+                     : gemm_linear<float, float>((const float*)a, (const float*)w_down, out, T, H, I, plan_lin(T, H, I, dt), part, st)), "down");
+  }
+  return ok();
+}
+
+size_t dl_layer_workspace_size(const dl_layer_dims* d, int32_t max_tokens, int32_t max_batch,
+                               int32_t max_seqlen, int32_t max_context_len, dl_mode m) {
+  if (check_dims(d) != DL_OK || max_tokens < 0 || max_batch < 0) return 0;
+  if (m != DL_FUSED && m != DL_UNFUSED) return 0;
+  // split-K partial needs are not monotonic in M: take the max over every M
+  // up to 512 and the largest sizes.
+  size_t part = 0;
+  const int mt = std::max(max_tokens, max_batch);
+  for (int M = 1; M <= std::min(mt, 512); ++M) part = std::max(part, part_bytes(d, M, m));
+  part = std::max(part, part_bytes(d, std::max(mt, 1), m));
+  size_t need = 0;
+  if (max_tokens > 0 && max_batch > 0)
+    need = std::max(need, layout(d, max_tokens, max_batch, std::max(max_seqlen, 1), false, m, part).total);
+  if (max_batch > 0 && max_context_len > 0)
+    need = std::max(need, layout(d, max_batch, max_batch, max_context_len, true, m, part).total);
+  return need;
+}
+
+dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
+                           const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                           float* hidden_out, const int32_t* positions,
+                           const int32_t* seq_of_token, const int32_t* cu_seqlens, int32_t B,
+                           int32_t T, int32_t max_seqlen, const dl_kv_cache* cache,
+                           const int32_t* block_table, int32_t max_blocks_per_seq, dl_mode m,
+                           void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dims(d));
+  TRY(check_weights(w));
+  TRY(check_cache(cache));
+  if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (B < 0 || T < 0 || max_seqlen < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
+  if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
+  if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (T == 0 || B == 0) return ok();
+  if (max_seqlen <= 0 || max_seqlen > T) return fail(DL_ERR_INVALID_ARG, "max_seqlen must be in [1, T]");
+  CHECK_PTR(cos_sin);
+  CHECK_PTR(hidden_in);
+  CHECK_PTR(hidden_out);
+  if (hidden_in == hidden_out) return fail(DL_ERR_INVALID_ARG, "hidden_out must not alias hidden_in");
+  CHECK_IDX(positions);
+  CHECK_IDX(seq_of_token);
+  CHECK_IDX(cu_seqlens);
+  CHECK_IDX(block_table);
+  const size_t part = part_bytes(d, T, m);
+  const Layout L = layout(d, T, B, max_seqlen, false, m, part);
+  if (!ws || ws_bytes < L.total)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, L.total);
+  CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (d->dtype == DL_BF16)
+    return layer_body<bf16>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, seq_of_token,
+                            cu_seqlens, nullptr, B, T, max_seqlen, false, cache, block_table,
+                            max_blocks_per_seq, m, ws, L, st);
+  return layer_body<float>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, seq_of_token,
+                           cu_seqlens, nullptr, B, T, max_seqlen, false, cache, block_table,
+                           max_blocks_per_seq, m, ws, L, st);
+}
+
+dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
+                          const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                          float* hidden_out, const int32_t* positions,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                          const dl_kv_cache* cache, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
+                          void* stream) {
+  TRY(check_dims(d));
+  TRY(check_weights(w));
+  TRY(check_cache(cache));
+  if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (B < 0) return fail(DL_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
+  if (max_context_len <= 0) return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * d->block_size < max_context_len)
+    return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq * BS must cover max_context_len");
+  if (B == 0) return ok();
+  CHECK_PTR(cos_sin);
+  CHECK_PTR(hidden_in);
+  CHECK_PTR(hidden_out);
+  if (hidden_in == hidden_out) return fail(DL_ERR_INVALID_ARG, "hidden_out must not alias hidden_in");
+  CHECK_IDX(positions);
+  CHECK_IDX(context_lens);
+  CHECK_IDX(block_table);
+  const size_t part = part_bytes(d, B, m);
+  const Layout L = layout(d, B, B, max_context_len, true, m, part);
+  if (!ws || ws_bytes < L.total)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, L.total);
+  CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (d->dtype == DL_BF16)
+    return layer_body<bf16>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, nullptr, nullptr,
+                            context_lens, B, B, max_context_len, true, cache, block_table,
+                            max_blocks_per_seq, m, ws, L, st);
+  return layer_body<float>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, nullptr, nullptr,
+                           context_lens, B, B, max_context_len, true, cache, block_table,
+                           max_blocks_per_seq, m, ws, L, st);
+}
+
+}  // extern "C"

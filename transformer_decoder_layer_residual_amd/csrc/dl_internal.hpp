@@ -1,0 +1,115 @@
+// dl_internal.hpp -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dl_common.hpp"
+
+namespace dl {
+
+// ---------------------------------------------------------------------------
+// GEMM planning.  Every projection is C = X W^T with X [M][K] activations and
+// W [N][K] weights.  Output columns are processed in "pairs": a tile of BN
+// logical columns holds P = BN/2 pair-columns, and column j of the first half
+// is paired with column j of the second half (RoPE partners, gate/up partners;
+// plain GEMMs just store both halves).  A plan fixes the tile shape and the
+// K split; split plans write fp32 partial sums to the workspace and a second
+// kernel reduces them and applies the epilogue.
+// ---------------------------------------------------------------------------
+enum GemmCfg : int {
+  kCfg256 = 0,   // BM 256, BN 256, 4 waves (2x2), wave tile 128x128
+  kCfg128 = 1,   // BM 128, BN 128, 4 waves (2x2), wave tile 64x64
+  kCfg64 = 2,    // BM 64,  BN 128, 4 waves (1x4), wave tile 64x32
+  kCfg16 = 3,    // BM 16,  BN 128, 4 waves (1x4), wave tile 16x32
+  kCfg32s = 4,   // BM 32,  BN 32,  2 waves (2x1), wave tile 16x32 (small/odd shapes)
+  kCfgCount = 5
+};
+
+struct GemmPlan {
+  int cfg;
+  int BM, BN;
+  int splits;        // number of K slices (1 = direct epilogue)
+  int k_per_split;   // multiple of the K tile
+  size_t ws_bytes;   // fp32 partials when splits > 1
+};
+
+// N: logical output columns.  paired: the epilogue needs pair partners, so
+// P = BN/2 must divide N/2; plain GEMMs accept a ragged last tile (N % 16 == 0).
+GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired);
+
+// Workspace-free variants share kernels; these return hipError_t.
+template <typename T>
+hipError_t gemm_qkv_rope(const T* x, const T* wq, const T* wk, const T* wv, const int32_t* pos,
+                         const float* cos_sin, int max_pos, T* q, T* k, T* v, int M, int H,
+                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st);
+template <typename T, typename To>
+hipError_t gemm_linear(const T* x, const T* w, To* out, int M, int N, int K, const GemmPlan& pl,
+                       void* ws, hipStream_t st);
+template <typename T>
+hipError_t gemm_linear_resid(const T* x, const T* w, const float* resid, float* out, int M, int N,
+                             int K, const GemmPlan& pl, void* ws, hipStream_t st);
+template <typename T>
+hipError_t gemm_swiglu(const T* x, const T* wg, const T* wu, T* a, int M, int H, int I,
+                       const GemmPlan& pl, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Other kernels
+// ---------------------------------------------------------------------------
+hipError_t rope_table_fill(float* cos_sin, int max_pos, int D, double theta, hipStream_t st);
+
+template <typename Tin, typename Tout>
+hipError_t rmsnorm_residual(const Tin* x, const float* resid_in, float* resid_out, const Tout* gamma,
+                            Tout* out, int T, int H, float eps, hipStream_t st);
+
+template <typename T>
+hipError_t reshape_and_cache(const T* k, const T* v, const int32_t* seq_of_token,
+                             const int32_t* pos, const int32_t* block_table, int max_blocks,
+                             T* k_cache, T* v_cache, int T_, int Hkv, int D, int BS,
+                             int num_blocks, hipStream_t st);
+
+template <typename T>
+hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_seqlens, int B,
+                        int max_seqlen, int Hq, int Hkv, int D, float scale, T* out,
+                        hipStream_t st);
+
+struct DecodePlan {
+  int chunk_blocks;  // KV blocks per split
+  int max_splits;    // splits per sequence at max_context_len
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int BS);
+
+template <typename T>
+hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
+                             const int32_t* block_table, int max_blocks,
+                             const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                             float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
+                             hipStream_t st);
+
+// Kernel-per-op baseline pieces (the unfused chain).
+template <typename T>
+hipError_t unf_rope(T* u, const int32_t* pos, const float* cos_sin, int max_pos, int T_, int nh,
+                    int D, hipStream_t st);
+template <typename T>
+hipError_t unf_scores(const T* q, const T* k, const int32_t* cu_seqlens, int B, int S_max,
+                      int Hq, int Hkv, int D, float scale, float* S, hipStream_t st);
+template <typename T>
+hipError_t unf_softmax(const float* S, T* P, const int32_t* lens, bool lens_are_cu, int B,
+                       int S_max, int Hq, int rows_per_head, hipStream_t st);
+template <typename T>
+hipError_t unf_pv(const T* P, const T* v, const int32_t* cu_seqlens, int B, int S_max, int Hq,
+                  int Hkv, int D, T* out, hipStream_t st);
+template <typename T>
+hipError_t unf_dec_attn(const T* q, const T* kc, const T* vc, const int32_t* bt, int max_blocks,
+                        const int32_t* ctx, int ctx_max, int B, int Hq, int Hkv, int D, int BS,
+                        float scale, float* S, T* P, T* out, int num_blocks, hipStream_t st);
+template <typename T>
+hipError_t unf_add(const float* a, const T* b, float* out, int64_t n, hipStream_t st);
+template <typename T>
+hipError_t unf_silu(const T* g, T* out, int64_t n, hipStream_t st);
+template <typename T>
+hipError_t unf_mul(const T* a, const T* b, T* out, int64_t n, hipStream_t st);
+
+}  // namespace dl

@@ -1,0 +1,479 @@
+// gemm.hip -- bf16/fp32 MFMA projection GEMMs with fused epilogues (gfx950).
+//
+// Every projection of the layer is C = X W^T: X [M][K] activations, W [N][K]
+// weights in [out_features][in_features] layout (the FFN weight shapes given on
+// the ascend-transformer-boost fusion page, section "fusion operator matrix").
+// Both operands are K-contiguous, so 16-byte global loads land directly in the
+// MFMA operand layout.  The weight tile is the MFMA's first operand and the
+// activation tile its second; each lane therefore ends up owning four
+// consecutive output columns of one row, which gives vector stores.
+//
+// Output columns are organised in pairs (see dl_internal.hpp): a BN-wide tile
+// holds P = BN/2 pair-columns; column j (j < P) and column j + P are owned by
+// the same lane.  That lets the epilogues need no data exchange:
+//   * QKV + RoPE: pair = (i, i + D/2) of one head -- the rotary pairs of the
+//     merged Q/K/V projection with the rotary embedding applied on its output
+//     (ops-transformer Llama2-7B page, "single-layer operator call chain");
+//   * gate/up + SiLU*mul: pair = (gate row j, up row j) -- MergedMatMul(GateUp)
+//     then SiLU and the gate x up product (same paragraph);
+//   * down + residual: y = h + acc in fp32 (residual add fused into the last
+//     dense layer, ATB fusion-strategy page, "MLP fusion");
+//   * plain: O-projection and the unfused chain (N may end in a partial
+//     tile; its missing weight rows read as zero and its stores are dropped).
+//
+// Pipeline: global -> registers -> LDS (double buffered, one barrier per K
+// tile), MFMA 16x16x32 bf16 (or 16x16x4 fp32) from LDS, fp32 accumulation.
+// Tile order is XCD-aware: consecutive workgroup ids are spread round-robin
+// over the 8 XCDs, so the id is remapped to give every XCD a contiguous run of
+// tiles, walked M-first in groups so neighbours share weight and activation
+// tiles in that XCD's L2.
+#include "dl_internal.hpp"
+
+namespace dl {
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * kWave;
+  static constexpr int MS = BM / (16 * WM);  // 16-row subtiles per wave
+  static constexpr int NS = BN / (16 * WN);  // 16-col subtiles per wave
+  static_assert(MS >= 1 && NS >= 2 && NS % 2 == 0, "bad tile");
+};
+
+template <typename T>
+struct KTile {
+  static constexpr int BK = 128 / sizeof(T);            // 128 bytes of K per row
+  static constexpr int VE = 16 / sizeof(T);             // elements per 16 B vector
+  static constexpr int LS = BK + 16 / sizeof(T);        // padded LDS row (144 B)
+};
+
+// ---------------------------------------------------------------------------
+// weight-row maps: logical column r of tile tn -> pointer to the weight row
+// ---------------------------------------------------------------------------
+template <typename T>
+struct MapPlain {
+  const T* W;
+  int K, BN, N;
+  __device__ const T* row(int tn, int r) const {
+    const int n = tn * BN + r;
+    return n < N ? W + (int64_t)n * K : nullptr;  // ragged last tile: zero rows
+  }
+};
+
+template <typename T>
+struct MapSwiglu {
+  const T *Wg, *Wu;
+  int K, P;
+  __device__ const T* row(int tn, int r) const {
+    return r < P ? Wg + ((int64_t)tn * P + r) * K : Wu + ((int64_t)tn * P + (r - P)) * K;
+  }
+};
+
+template <typename T>
+struct MapQKV {
+  const T *Wq, *Wk, *Wv;
+  int K, Hq, Hkv, D, P;
+  __device__ const T* row(int tn, int r) const {
+    const int half = D / 2;
+    const int second = r >= P;
+    const int pc = tn * P + (second ? r - P : r);
+    const int head = pc / half, c = pc - head * half;
+    const int in_head = second * half + c;
+    if (head < Hq) return Wq + ((int64_t)head * D + in_head) * K;
+    if (head < Hq + Hkv) return Wk + ((int64_t)(head - Hq) * D + in_head) * K;
+    return Wv + ((int64_t)(head - Hq - Hkv) * D + in_head) * K;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// epilogues: (row m, tile tn, first-half column j (multiple of 4), 4 values of
+// columns j..j+3 and 4 values of their partners j+P..j+P+3)
+// ---------------------------------------------------------------------------
+// Plain store; columns at or beyond N (the ragged last tile) are dropped.
+// N is a multiple of 16, so a group of 4 columns is either all in or all out.
+template <typename To>
+struct EpiPlain {
+  To* out;
+  int ldo, BN, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int n = tn * BN + j;
+    To* p = out + (int64_t)m * ldo + n;
+    if (n < ldo) store4(p, a[0], a[1], a[2], a[3]);
+    if (n + P < ldo) store4(p + P, b[0], b[1], b[2], b[3]);
+  }
+};
+
+struct EpiResid {
+  float* out;
+  const float* resid;
+  int ldo, BN, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int n = tn * BN + j;
+    const int64_t o = (int64_t)m * ldo + n;
+    if (n < ldo) {
+      const f32x4 r0 = *reinterpret_cast<const f32x4*>(resid + o);
+      store4(out + o, r0[0] + a[0], r0[1] + a[1], r0[2] + a[2], r0[3] + a[3]);
+    }
+    if (n + P < ldo) {
+      const f32x4 r1 = *reinterpret_cast<const f32x4*>(resid + o + P);
+      store4(out + o + P, r1[0] + b[0], r1[1] + b[1], r1[2] + b[2], r1[3] + b[3]);
+    }
+  }
+};
+
+template <typename To>
+struct EpiSwiglu {
+  To* out;
+  int I, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 g, f32x4 u) const {
+    To* p = out + (int64_t)m * I + (int64_t)tn * P + j;
+    store4(p, silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2], silu(g[3]) * u[3]);
+  }
+};
+
+// Rotate-half RoPE on q and k heads; v passes through.  cos_sin is
+// [max_pos][D/2][2] fp32 (cos, sin) built from fp64 angles.
+template <typename To>
+struct EpiRope {
+  To *q, *k, *v;
+  const int32_t* pos;
+  const float* cs;
+  int Hq, Hkv, D, P, max_pos;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int half = D / 2;
+    const int pc = tn * P + j;
+    const int head = pc / half, c = pc - head * half;
+    To* dst;
+    bool rot = true;
+    if (head < Hq) {
+      dst = q + ((int64_t)m * Hq + head) * D;
+    } else if (head < Hq + Hkv) {
+      dst = k + ((int64_t)m * Hkv + (head - Hq)) * D;
+    } else {
+      dst = v + ((int64_t)m * Hkv + (head - Hq - Hkv)) * D;
+      rot = false;
+    }
+    if (rot) {
+      const int p = min(max(pos[m], 0), max_pos - 1);  // out-of-table positions clamp
+      const float* cp = cs + ((int64_t)p * half + c) * 2;
+      f32x4 c0 = *reinterpret_cast<const f32x4*>(cp);      // cos c, sin c, cos c+1, sin c+1
+      f32x4 c1 = *reinterpret_cast<const f32x4*>(cp + 4);  // cos c+2, sin c+2, cos c+3, sin c+3
+      float co[4] = {c0[0], c0[2], c1[0], c1[2]};
+      float si[4] = {c0[1], c0[3], c1[1], c1[3]};
+      float o1[4], o2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o1[e] = a[e] * co[e] - b[e] * si[e];
+        o2[e] = b[e] * co[e] + a[e] * si[e];
+      }
+      store4(dst + c, o1[0], o1[1], o1[2], o1[3]);
+      store4(dst + half + c, o2[0], o2[1], o2[2], o2[3]);
+    } else {
+      store4(dst + c, a[0], a[1], a[2], a[3]);
+      store4(dst + half + c, b[0], b[1], b[2], b[3]);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <typename T, class C, class Map, class Epi>
+__global__ void __launch_bounds__(C::NT)
+gemm_kernel(const T* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m, int tiles_n,
+            int kps, float* __restrict__ partial, int NL) {
+  constexpr int BM = C::BM, BN = C::BN, NT = C::NT, MS = C::MS, NS = C::NS, WN = C::WN;
+  constexpr int BK = KTile<T>::BK, VE = KTile<T>::VE, LS = KTile<T>::LS;
+  constexpr int RSTEP = NT / 8;                        // rows covered per load pass
+  constexpr int A_IT = (BM + RSTEP - 1) / RSTEP;
+  constexpr int W_IT = (BN + RSTEP - 1) / RSTEP;
+  constexpr int P = BN / 2;
+  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * LS];
+
+  // ---- tile coordinates (XCD-aware, M-grouped) ----
+  int bid = blockIdx.x;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int gsz = GM * tiles_n;
+  const int first_m = (bid / gsz) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % gsz) % gm;
+  const int tn = (bid % gsz) / gm;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int chunk = t & 7, r0 = t >> 3;
+
+  const int k_begin = blockIdx.y * kps;
+  const int k_end = min(K, k_begin + kps);
+  const int nkt = (k_end - k_begin + BK - 1) / BK;
+
+  const T* xrow[A_IT];
+  bool xok[A_IT];
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int r = r0 + i * RSTEP;
+    const int m = tm * BM + r;
+    xok[i] = (r < BM) && (m < M);
+    xrow[i] = X + (int64_t)(xok[i] ? m : 0) * K + chunk * VE;
+  }
+  const T* wrow[W_IT];
+  bool wok[W_IT];
+#pragma unroll
+  for (int i = 0; i < W_IT; ++i) {
+    const int r = r0 + i * RSTEP;
+    const T* base = (r < BN) ? map.row(tn, r) : nullptr;  // nullptr: zero row
+    wok[i] = base != nullptr;
+    wrow[i] = wok[i] ? base + chunk * VE : X;  // never offset a null row pointer
+  }
+
+  u32x4 ra[A_IT], rw[W_IT];
+  const u32x4 zero = {0, 0, 0, 0};
+  auto gload = [&](int k0) {
+    const bool kin = (k0 + chunk * VE) < k_end;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) ra[i] = (xok[i] && kin) ? ld16(xrow[i] + k0) : zero;
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) rw[i] = (wok[i] && kin) ? ld16(wrow[i] + k0) : zero;
+  };
+  auto sstore = [&](int buf) {
+    T* As = smem[buf];
+    T* Ws = As + BM * LS;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+      const int r = r0 + i * RSTEP;
+      if (r < BM) st16(As + r * LS + chunk * VE, ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) {
+      const int r = r0 + i * RSTEP;
+      if (r < BN) st16(Ws + r * LS + chunk * VE, rw[i]);
+    }
+  };
+
+  f32x4 acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  if (nkt > 0) {
+    gload(k_begin);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nkt; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nkt) gload(k_begin + (it + 1) * BK);
+    const T* As = smem[cur];
+    const T* Ws = As + BM * LS;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      Frag<T> wf[NS], xf[MS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int nsub = (s < NS / 2) ? wn * (NS / 2) + s : BN / 32 + wn * (NS / 2) + (s - NS / 2);
+        wf[s].load(Ws + (nsub * 16 + fr) * LS + kk + fk);
+      }
+#pragma unroll
+      for (int i = 0; i < MS; ++i) xf[i].load(As + ((wm * MS + i) * 16 + fr) * LS + kk + fk);
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[i][s] = mfma_k32(wf[s], xf[i], acc[i][s]);
+    }
+    if (it + 1 < nkt) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int m = tm * BM + (wm * MS + i) * 16 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+      const int j = (wn * (NS / 2) + s) * 16 + 4 * (lane >> 4);
+      if (partial) {
+        float* p = partial + ((int64_t)blockIdx.y * M + m) * NL + (int64_t)tn * BN + j;
+        store4(p, acc[i][s][0], acc[i][s][1], acc[i][s][2], acc[i][s][3]);
+        const f32x4 b = acc[i][s + NS / 2];
+        store4(p + P, b[0], b[1], b[2], b[3]);
+      } else {
+        epi(m, tn, j, acc[i][s], acc[i][s + NS / 2]);
+      }
+    }
+  }
+}
+
+// Deterministic split-K reduction (fixed split order) followed by the
+// epilogue.  One thread per (row, tile, group of 4 first-half columns).
+// Partials are [split][M][NP] with NP = tiles * BN (padded to whole tiles).
+template <class Epi>
+__global__ void __launch_bounds__(256)
+splitk_reduce(const float* __restrict__ partial, int splits, int M, int NP, int BN, Epi epi) {
+  const int P = BN / 2, gpt = P / 4, tiles = NP / BN;
+  const int NL = NP;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)M * tiles * gpt;
+  if (idx >= total) return;
+  const int g = (int)(idx % gpt);
+  const int64_t rest = idx / gpt;
+  const int tn = (int)(rest % tiles);
+  const int m = (int)(rest / tiles);
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = partial + ((int64_t)s * M + m) * NL + (int64_t)tn * BN + 4 * g;
+    a += *reinterpret_cast<const f32x4*>(p);
+    b += *reinterpret_cast<const f32x4*>(p + P);
+  }
+  epi(m, tn, 4 * g, a, b);
+}
+
+// ---------------------------------------------------------------------------
+// planning and launch
+// ---------------------------------------------------------------------------
+static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32};
+static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32};
+
+GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
+  GemmPlan pl{};
+  const int bk = is_f32 ? 32 : 64;
+  auto fits = [&](int c) { return !paired || (N / 2) % (kCfgBN[c] / 2) == 0; };
+  auto tiles_n = [&](int c) { return (N + kCfgBN[c] - 1) / kCfgBN[c]; };
+  auto tiles = [&](int c) { return ((M + kCfgBM[c] - 1) / kCfgBM[c]) * tiles_n(c); };
+  int cfg;
+  if (is_f32) {
+    cfg = kCfg32s;
+  } else if (M >= 512) {
+    cfg = (fits(kCfg256) && tiles(kCfg256) >= 512) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
+  } else if (M > 16) {
+    cfg = fits(kCfg64) ? kCfg64 : kCfg32s;
+  } else {
+    cfg = fits(kCfg16) ? kCfg16 : kCfg32s;
+  }
+  pl.cfg = cfg;
+  pl.BM = kCfgBM[cfg];
+  pl.BN = kCfgBN[cfg];
+  const int nt = tiles(cfg);
+  const int ktiles = (K + bk - 1) / bk;
+  int splits = 1;
+  if (M <= 256) {
+    // weight-streaming shapes: enough workgroups to keep HBM busy
+    const int want = (1024 + nt - 1) / nt;
+    splits = want < 1 ? 1 : want;
+    const int max_splits = ktiles / 4 > 0 ? ktiles / 4 : 1;
+    if (splits > max_splits) splits = max_splits;
+  } else if (nt < 128) {
+    const int want = (256 + nt - 1) / nt;
+    const int max_splits = ktiles / 8 > 0 ? ktiles / 8 : 1;
+    splits = want < max_splits ? want : max_splits;
+  }
+  int kps = ((ktiles + splits - 1) / splits) * bk;
+  splits = (K + kps - 1) / kps;
+  pl.k_per_split = kps;
+  pl.splits = splits;
+  pl.ws_bytes = splits > 1 ? (size_t)splits * (size_t)M * (size_t)tiles_n(cfg) * kCfgBN[cfg] * sizeof(float) : 0;
+  return pl;
+}
+
+template <typename T, class C, class Map, class Epi>
+static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi& epi, int NL,
+                             const GemmPlan& pl, void* ws, hipStream_t st) {
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (NL + C::BN - 1) / C::BN;
+  const int NP = tiles_n * C::BN;
+  float* partial = pl.splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  dim3 grid(tiles_m * tiles_n, pl.splits);
+  hipLaunchKernelGGL((gemm_kernel<T, C, Map, Epi>), grid, dim3(C::NT), 0, st, x, M, K, map, epi,
+                     tiles_m, tiles_n, pl.k_per_split, partial, NP);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t work = (int64_t)M * tiles_n * (C::BN / 8);
+  const int blocks = (int)((work + 255) / 256);
+  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3(blocks), dim3(256), 0, st, partial, pl.splits, M,
+                     NP, C::BN, epi);
+  return hipGetLastError();
+}
+
+typedef Tile<256, 256, 2, 2> T256;
+typedef Tile<128, 128, 2, 2> T128;
+typedef Tile<64, 128, 1, 4> T64;
+typedef Tile<16, 128, 1, 4> T16;
+typedef Tile<32, 32, 2, 1> T32s;
+
+// Map and epilogue objects need BN / P, which depend on the tile; the factory
+// lambdas receive (BN, P) and build them.
+template <typename T, class MakeMap, class MakeEpi>
+static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl, void* ws,
+                           hipStream_t st, MakeMap mk_map, MakeEpi mk_epi) {
+  if constexpr (sizeof(T) == 4) {
+    if (pl.cfg != kCfg32s) return hipErrorInvalidValue;
+    return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
+  } else {
+    switch (pl.cfg) {
+      case kCfg256: return launch_cfg<T, T256>(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, pl, ws, st);
+      case kCfg128: return launch_cfg<T, T128>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
+      case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
+      case kCfg16: return launch_cfg<T, T16>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
+      case kCfg32s: return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t gemm_qkv_rope(const T* x, const T* wq, const T* wk, const T* wv, const int32_t* pos,
+                         const float* cos_sin, int max_pos, T* q, T* k, T* v, int M, int H,
+                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st) {
+  const int NL = (Hq + 2 * Hkv) * D;
+  return dispatch<T>(
+      x, M, H, NL, pl, ws, st,
+      [&](int, int P) { return MapQKV<T>{wq, wk, wv, H, Hq, Hkv, D, P}; },
+      [&](int, int P) { return EpiRope<T>{q, k, v, pos, cos_sin, Hq, Hkv, D, P, max_pos}; });
+}
+
+template <typename T, typename To>
+hipError_t gemm_linear(const T* x, const T* w, To* out, int M, int N, int K, const GemmPlan& pl,
+                       void* ws, hipStream_t st) {
+  return dispatch<T>(
+      x, M, K, N, pl, ws, st, [&](int BN, int) { return MapPlain<T>{w, K, BN, N}; },
+      [&](int BN, int P) { return EpiPlain<To>{out, N, BN, P}; });
+}
+
+template <typename T>
+hipError_t gemm_linear_resid(const T* x, const T* w, const float* resid, float* out, int M, int N,
+                             int K, const GemmPlan& pl, void* ws, hipStream_t st) {
+  return dispatch<T>(
+      x, M, K, N, pl, ws, st, [&](int BN, int) { return MapPlain<T>{w, K, BN, N}; },
+      [&](int BN, int P) { return EpiResid{out, resid, N, BN, P}; });
+}
+
+template <typename T>
+hipError_t gemm_swiglu(const T* x, const T* wg, const T* wu, T* a, int M, int H, int I,
+                       const GemmPlan& pl, void* ws, hipStream_t st) {
+  return dispatch<T>(
+      x, M, H, 2 * I, pl, ws, st, [&](int, int P) { return MapSwiglu<T>{wg, wu, H, P}; },
+      [&](int, int P) { return EpiSwiglu<T>{a, I, P}; });
+}
+
+#define DL_INST(T)                                                                              \
+  template hipError_t gemm_qkv_rope<T>(const T*, const T*, const T*, const T*, const int32_t*, \
+                                       const float*, int, T*, T*, T*, int, int, int, int, int, \
+                                       const GemmPlan&, void*, hipStream_t);                   \
+  template hipError_t gemm_linear<T, T>(const T*, const T*, T*, int, int, int, const GemmPlan&, \
+                                        void*, hipStream_t);                                    \
+  template hipError_t gemm_linear_resid<T>(const T*, const T*, const float*, float*, int, int,  \
+                                           int, const GemmPlan&, void*, hipStream_t);          \
+  template hipError_t gemm_swiglu<T>(const T*, const T*, const T*, T*, int, int, int,           \
+                                     const GemmPlan&, void*, hipStream_t);
+
+DL_INST(bf16)
+DL_INST(float)
+template hipError_t gemm_linear<bf16, float>(const bf16*, const bf16*, float*, int, int, int,
+                                             const GemmPlan&, void*, hipStream_t);
+
+}  // namespace dl

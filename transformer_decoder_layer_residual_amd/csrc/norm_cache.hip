@@ -1,0 +1,169 @@
+// norm_cache.hip -- RMSNorm (optionally fused with the residual add), the
+// RoPE cos/sin table, and reshape-and-cache into paged KV blocks.
+#include "dl_internal.hpp"
+
+namespace dl {
+
+// ---------------------------------------------------------------------------
+// RMSNorm + residual.  One workgroup per token row; the row stays in
+// registers between the statistics pass and the scaling pass, so x (and the
+// residual) are read once and h / out written once.
+//   resid_in == nullptr:  out = gamma * x / sqrt(mean(x^2) + eps)
+//   otherwise:            h = x + resid_in (fp32) -> resid_out,
+//                         out = gamma * h / sqrt(mean(h^2) + eps)
+// (Llama RMSNorm in the layer chain of the ops-transformer Llama2-7B page;
+// norm fused with the residual add per the "fusion operator matrix" section of
+// the ascend-transformer-boost page.)
+// ---------------------------------------------------------------------------
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxVec = 8;  // 4-element vectors per thread: H <= 8192
+
+template <typename T>
+__device__ __forceinline__ f32x4 ld4f(const T* p) {
+  float o[4];
+  load4(p, o);
+  return f32x4{o[0], o[1], o[2], o[3]};
+}
+
+template <typename Tin, typename Tout>
+__global__ void __launch_bounds__(kNormThreads)
+rmsnorm_kernel(const Tin* __restrict__ x, const float* __restrict__ rin, float* __restrict__ rout,
+               const Tout* __restrict__ gamma, Tout* __restrict__ out, int H, float eps) {
+  __shared__ float red[kNormThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const int nv = H / 4;
+  const int tid = threadIdx.x;
+  f32x4 h[kNormMaxVec];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int v = tid + i * kNormThreads;
+    if (v < nv) {
+      f32x4 a = ld4f(x + row * H + 4 * v);
+      if (rin) {
+        const f32x4 r = *reinterpret_cast<const f32x4*>(rin + row * H + 4 * v);
+        a = a + r;
+        *reinterpret_cast<f32x4*>(rout + row * H + 4 * v) = a;
+      }
+      h[i] = a;
+      ss += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < kNormMaxVec; ++i) {
+    const int v = tid + i * kNormThreads;
+    if (v < nv) {
+      const f32x4 g = ld4f(gamma + 4 * v);
+      store4(out + row * H + 4 * v, g[0] * (h[i][0] * inv), g[1] * (h[i][1] * inv),
+             g[2] * (h[i][2] * inv), g[3] * (h[i][3] * inv));
+    }
+  }
+}
+
+template <typename Tin, typename Tout>
+hipError_t rmsnorm_residual(const Tin* x, const float* resid_in, float* resid_out,
+                            const Tout* gamma, Tout* out, int T, int H, float eps,
+                            hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout>), dim3(T), dim3(kNormThreads), 0, st, x,
+                     resid_in, resid_out, gamma, out, H, eps);
+  return hipGetLastError();
+}
+
+template hipError_t rmsnorm_residual<float, bf16>(const float*, const float*, float*, const bf16*,
+                                                  bf16*, int, int, float, hipStream_t);
+template hipError_t rmsnorm_residual<bf16, bf16>(const bf16*, const float*, float*, const bf16*,
+                                                 bf16*, int, int, float, hipStream_t);
+template hipError_t rmsnorm_residual<float, float>(const float*, const float*, float*,
+                                                   const float*, float*, int, int, float,
+                                                   hipStream_t);
+template hipError_t rmsnorm_residual<bf16, float>(const bf16*, const float*, float*, const float*,
+                                                  float*, int, int, float, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// RoPE table: cos_sin[p][i] = (cos, sin)(p * theta^(-2i/D)), angle in fp64.
+// (Rotate-half pairing; the pages name the rotary embedding but print no
+// formula, so the common Llama form is taken.)
+// ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(float* cs, int max_pos, int half, int D, double theta) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)max_pos * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double w = pow(theta, -2.0 * (double)i / (double)D);
+  const double phi = (double)p * w;
+  cs[2 * idx] = (float)cos(phi);
+  cs[2 * idx + 1] = (float)sin(phi);
+}
+
+hipError_t rope_table_fill(float* cs, int max_pos, int D, double theta, hipStream_t st) {
+  const int half = D / 2;
+  const int64_t n = (int64_t)max_pos * half;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cs,
+                     max_pos, half, D, theta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Reshape-and-cache: token t (sequence s, position p) of kv head g goes to
+// block block_table[s][p / BS], slot p % BS of the [num_blocks][Hkv][BS][D]
+// cache (ATB KV-cache page, "KV cache memory bottleneck": paged blocks
+// addressed through block_table, ReshapeAndCache writing step K/V).
+// One thread per 16-byte vector; a pure copy, so the result is bit-exact.
+// Out-of-range table entries are skipped (the write is dropped) instead of
+// faulting.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void reshape_and_cache_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                         const int32_t* __restrict__ seq_of_token,
+                                         const int32_t* __restrict__ pos,
+                                         const int32_t* __restrict__ block_table, int max_blocks,
+                                         T* __restrict__ kc, T* __restrict__ vc, int T_, int Hkv,
+                                         int D, int BS, int num_blocks) {
+  constexpr int VE = 16 / sizeof(T);
+  const int vpr = D / VE;  // vectors per head row
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T_ * Hkv * vpr;
+  if (idx >= total) return;
+  const int c = (int)(idx % vpr);
+  const int64_t tg = idx / vpr;
+  const int g = (int)(tg % Hkv);
+  const int t = (int)(tg / Hkv);
+  const int s = seq_of_token ? seq_of_token[t] : t, p = pos[t];
+  if (p < 0 || p / BS >= max_blocks) return;
+  const int blk = block_table[(int64_t)s * max_blocks + p / BS];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int64_t dst = (((int64_t)blk * Hkv + g) * BS + (p % BS)) * D + c * VE;
+  const int64_t src = ((int64_t)t * Hkv + g) * D + c * VE;
+  st16(kc + dst, ld16(k + src));
+  st16(vc + dst, ld16(v + src));
+}
+
+template <typename T>
+hipError_t reshape_and_cache(const T* k, const T* v, const int32_t* seq_of_token,
+                             const int32_t* pos, const int32_t* block_table, int max_blocks,
+                             T* k_cache, T* v_cache, int T_, int Hkv, int D, int BS,
+                             int num_blocks, hipStream_t st) {
+  const int64_t n = (int64_t)T_ * Hkv * (D / (16 / (int)sizeof(T)));
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((reshape_and_cache_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                     0, st, k, v, seq_of_token, pos, block_table, max_blocks, k_cache, v_cache,
+                     T_, Hkv, D, BS, num_blocks);
+  return hipGetLastError();
+}
+
+template hipError_t reshape_and_cache<bf16>(const bf16*, const bf16*, const int32_t*,
+                                            const int32_t*, const int32_t*, int, bf16*, bf16*,
+                                            int, int, int, int, int, hipStream_t);
+template hipError_t reshape_and_cache<float>(const float*, const float*, const int32_t*,
+                                             const int32_t*, const int32_t*, int, float*, float*,
+                                             int, int, int, int, int, hipStream_t);
+
+}  // namespace dl
