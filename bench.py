@@ -1,0 +1,276 @@
+#!/usr/bin/env python
+"""Decoder-layer benchmark on one MI355X.
+
+Step = one dl_layer_prefill call on the Llama-2-7B-shaped layer (hidden 4096,
+32 heads x 128, intermediate 11008, bf16) over one 2048-token sequence: input
+RMSNorm, merged QKV GEMM + RoPE, reshape-and-cache, causal flash attention,
+O-projection, RMSNorm fused with the residual add, gate/up GEMM + SiLU*mul,
+down GEMM + residual.  value = prefill tokens/s of the layer.
+
+Beside it the JSON line carries:
+  roofline      the gate/up GEMM (the layer's largest kernel), timed with HIP
+                events on the stream it is launched on, against bf16 MFMA peak;
+  layer         whole-step flops and the fraction of peak;
+  decode        one decode step of the same layer shape at batch 64 with
+                context lengths U{128..4096} over a paged cache (tokens/s and
+                the paged attention kernel against HBM peak);
+  cpu_baseline  the CPU oracle on a bounded prefix of the same prefill.
+
+Inputs are resident in HBM before the timed region; weights and activations
+are seeded synthetic data.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoder-layer tokens/s (prefill, decode) + % of HBM/MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "transformer_decoder_layer_residual_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, n, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n   # ms per launch
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="prefix length of the CPU-oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this layer is "
+              "built and measured on a single MI355X, see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_decoder_layer_residual_amd import binding as dl
+    from transformer_decoder_layer_residual_amd import inputs as gen
+    from transformer_decoder_layer_residual_amd.harness import (DeviceLayer, cache_dev, i32,
+                                                                to_dev)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dl.lib()   # fail loudly now if the HIP library is missing
+    stream = torch.cuda.current_stream()
+    mode = dl.DL_FUSED if args.mode == "fused" else dl.DL_UNFUSED
+
+    # ------------------------------------------------------------------ prefill
+    cfg = gen.CONFIGS[2]
+    pb = gen.prefill_batch(cfg)
+    T = pb.T
+    log(f"[bench] generating {cfg.name} inputs")
+    t0 = time.time()
+    w_host = gen.weights(cfg)
+    x_host = gen.hidden(cfg, T)
+    bt = gen.block_table(cfg, pb.lens)
+    kbits, vbits = gen.empty_cache(cfg, bt.num_blocks)
+    # one RoPE table long enough for the prefill and for 4096-token decode contexts
+    layer = DeviceLayer.build(cfg, max_pos=max(T, 4096), w_host=w_host)
+    x = to_dev(x_host, torch.float32)
+    y = torch.empty_like(x)
+    kc, vc = cache_dev(kbits), cache_dev(vbits)
+    btd = i32(bt.table)
+    pos, seq, cu = i32(pb.positions), i32(pb.seq_of_token), i32(pb.cu_seqlens)
+    ws_bytes = dl.dl_layer_workspace_size(layer.dims, T, pb.B, pb.max_seqlen, 0, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; workspace {ws_bytes / 2**20:.0f} MiB")
+
+    def step():
+        dl.dl_layer_prefill(layer.dims, layer.w, layer.cs, x, y, pos, seq, cu, pb.max_seqlen, kc,
+                            vc, btd, mode=mode, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_launches(step, args.steps, stream)
+    tok_s = T / (ms * 1e-3)
+    H, Hq, D, I = cfg.hidden, cfg.n_q_heads, cfg.head_dim, cfg.intermediate
+    Hkv = cfg.n_kv_heads
+    gemm_flops = 2.0 * T * H * ((Hq + 2 * Hkv) * D + Hq * D + 2 * I + I)
+    attn_flops = 4.0 * Hq * D * float((pb.lens.astype(np.int64) * (pb.lens + 1) // 2).sum())
+    layer_flops = gemm_flops + attn_flops
+    log(f"[bench] prefill: {ms:.3f} ms/step, {tok_s:,.0f} tokens/s, "
+        f"{layer_flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s")
+
+    # dominant kernel: gate/up GEMM with the SiLU*mul epilogue, on the layer's
+    # own normalised activations
+    s = layer.steps_prefill(x, pb, cache_dev(kbits), cache_dev(vbits), btd)
+    a_out = torch.empty(T, I, dtype=torch.bfloat16, device="cuda:0")
+    gu_ws_n = dl.lib().dl_gate_up_silu_workspace_size(T, H, I, dl.DL_BF16)
+    gu_ws = torch.empty(max(gu_ws_n, 1), dtype=torch.uint8, device="cuda:0")
+
+    def gateup():
+        dl.dl_gate_up_silu(s["n2"], layer.w["wg"], layer.w["wu"], a_out, ws=gu_ws)
+
+    for _ in range(3):
+        gateup()
+    gu_ms = time_launches(gateup, max(args.steps, 20), stream)
+    gu_flops = 2.0 * T * (2 * I) * H
+    gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
+    gu_traffic = load_traffic("gemm_gateup_silu_prefill", source_sha("gemm.hip", "dl_common.hpp"))
+    log(f"[bench] gate/up GEMM: {gu_ms:.3f} ms, {gu_tf:.0f} TFLOP/s "
+        f"({100 * gu_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    del s
+
+    result = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) activations)",
+        "config": {"workload": "llama2-7b-layer-prefill", "batch": 1, "seq_len": T,
+                   "hidden": H, "heads": f"{Hq}/{Hkv}x{D}", "intermediate": I,
+                   "mode": args.mode},
+        "roofline": {"bound": "mfma", "kernel": "gemm gate/up + SiLU*mul",
+                     "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": gu_traffic,
+                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4)},
+        "layer": {"flops_per_step": layer_flops,
+                  "achieved_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
+                  "frac_of_bf16_peak": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                             4)},
+    }
+    del ws, kc, vc
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        dcfg = gen.CONFIGS[3]          # same layer shape (and weights) as the prefill
+        ctx = gen.decode_context_lens(dcfg)
+        B = ctx.size
+        log(f"[bench] generating {dcfg.name} cache (B={B}, mean ctx {ctx.mean():.0f})")
+        dbt = gen.block_table(dcfg, ctx)
+        dkb, dvb = gen.synthetic_cache(dcfg, dbt, ctx)
+        dkc, dvc = cache_dev(dkb), cache_dev(dvb)
+        del dkb, dvb
+        dbtd = i32(dbt.table)
+        xd = to_dev(gen.hidden(dcfg, B), torch.float32)
+        yd = torch.empty_like(xd)
+        max_ctx = int(ctx.max())
+        dpos, dctx = i32(ctx - 1), i32(ctx)
+        dws_n = dl.dl_layer_workspace_size(layer.dims, B, B, 0, max_ctx, mode)
+        dws = torch.empty(dws_n, dtype=torch.uint8, device="cuda:0")
+
+        def dstep():
+            dl.dl_layer_decode(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, dkc,
+                               dvc, dbtd, mode=mode, ws=dws)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        dms = time_launches(dstep, args.steps, stream)
+        # dominant kernel: paged decode attention (split + combine)
+        q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda:0").normal_()
+        ao = torch.empty_like(q)
+        aws_n = dl.lib().dl_attn_decode_workspace_size(B, Hq, Hkv, D, max_ctx, dcfg.block_size)
+        aws = torch.empty(aws_n, dtype=torch.uint8, device="cuda:0")
+
+        def dattn():
+            dl.dl_attn_decode_paged(q, dkc, dvc, dbtd, dctx, max_ctx, ao, ws=aws)
+
+        for _ in range(3):
+            dattn()
+        a_ms = time_launches(dattn, max(args.steps, 20), stream)
+        kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv * D * 2
+        a_bytes = kv_bytes + 2.0 * B * Hq * D * 2
+        a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+        w_bytes = 2.0 * (H * (Hq + 2 * Hkv) * D + Hq * D * H + 3 * H * I)
+        step_bytes = w_bytes + kv_bytes
+        result["decode"] = {
+            "workload": "llama2-7b-layer-decode", "batch": B,
+            "context": "uniform 128..4096 (mean %.0f)" % ctx.mean(),
+            "value": round(B / (dms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(dms, 4),
+            "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
+                         "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(a_gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("attn_decode_paged",
+                                                 source_sha("attn_decode.hip")),
+                         "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
+        }
+        log(f"[bench] decode: {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} tokens/s; attention "
+            f"{a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
+        del dkc, dvc, dws, aws
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ cpu baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(args.cpu_tokens, T)
+        sub = gen.packed([n])
+        log(f"[bench] CPU oracle on the first {n} tokens")
+        t0 = time.time()
+        oracle.layer_prefill(cfg.dims(), w_host, x_host[:n], sub.positions, sub.seq_of_token,
+                             sub.cu_seqlens, mode=oracle.EXACT)
+        dt = time.time() - t0
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        result["cpu_baseline"] = {
+            "value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n} of the {T} prefill tokens, same weights, exact fp32/fp64 "
+                      f"mode, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,8 @@ the layer itself.  Both the GPU path and the CPU oracle are fed from here.
 
 Recipe (shapes from the five workload configurations):
   * every random tensor comes from numpy default_rng(SeedSequence(
-    [config_id, tensor_id, step])), so any tensor can be regenerated alone;
+    [config_id, tensor_id, step, block])), one stream per 2^22-element block
+    of the flattened tensor, so any tensor can be regenerated alone;
   * the seven projection matrices are N(0, 0.02^2); RMSNorm gammas are 1
     (unit tests may ask for U(0.5, 1.5) so a dropped gamma is visible);
   * hidden states are N(0, 1); in bf16 configurations every draw is rounded
@@ -20,6 +21,8 @@ Recipe (shapes from the five workload configurations):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -73,19 +76,53 @@ CONFIGS = {
 }
 
 
-def rng(config_id: int, tensor_id: int, step: int = 0) -> np.random.Generator:
-    return np.random.default_rng(np.random.SeedSequence([config_id, tensor_id, step]))
+def rng(config_id: int, tensor_id: int, step: int = 0, chunk: int = -1) -> np.random.Generator:
+    key = [config_id, tensor_id, step] if chunk < 0 else [config_id, tensor_id, step, chunk]
+    return np.random.default_rng(np.random.SeedSequence(key))
+
+
+_CHUNK = 1 << 22
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+def _standard_normal(config_id: int, tensor_id: int, step: int, shape) -> np.ndarray:
+    """N(0,1) float32 draws; element block c (of 2^22) comes from its own
+    stream rng(config_id, tensor_id, step, c), so blocks fill in parallel."""
+    out = np.empty(shape, np.float32)
+    flat = out.reshape(-1)
+
+    def fill(c):
+        s = c * _CHUNK
+        e = min(flat.size, s + _CHUNK)
+        flat[s:e] = rng(config_id, tensor_id, step, c).standard_normal(e - s, dtype=np.float32)
+
+    list(_pool().map(fill, range((flat.size + _CHUNK - 1) // _CHUNK)))
+    return out
 
 
 def to_bf16_values(a: np.ndarray) -> np.ndarray:
-    """Nearest bf16 value (ties to even) of each float32, returned as float32."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32)
-    r = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) & np.uint32(0xFFFF0000))
-    nan = np.isnan(a)
-    if nan.any():
-        r = np.where(nan, (u | np.uint32(0x00400000)) & np.uint32(0xFFFF0000), r)
-    return r.astype(np.uint32).view(np.float32)
+    """Nearest bf16 value (ties to even) of each float32, returned as float32.
+    Works in place on a private float32 copy, in chunks to bound temporaries."""
+    out = np.array(a, dtype=np.float32, copy=True, order="C")
+    u = out.reshape(-1).view(np.uint32)
+    step = 1 << 24
+    for s in range(0, u.size, step):
+        c = u[s:s + step]
+        nan = np.isnan(c.view(np.float32))
+        lsb = (c >> np.uint32(16)) & np.uint32(1)
+        c += np.uint32(0x7FFF)
+        c += lsb
+        c &= np.uint32(0xFFFF0000)
+        if nan.any():
+            c[nan] = np.uint32(0x7FC00000)
+    return out
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -97,11 +134,27 @@ def bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def _round_bf16_inplace(a: np.ndarray) -> np.ndarray:
+    """In-place nearest-bf16 rounding (ties to even) of finite float32 draws,
+    in parallel blocks."""
+    u = a.reshape(-1).view(np.uint32)
+
+    def rnd(c):
+        v = u[c * _CHUNK:(c + 1) * _CHUNK]
+        lsb = (v >> np.uint32(16)) & np.uint32(1)
+        v += np.uint32(0x7FFF)
+        v += lsb
+        v &= np.uint32(0xFFFF0000)
+
+    list(_pool().map(rnd, range((u.size + _CHUNK - 1) // _CHUNK)))
+    return a
+
+
 def _normal(cfg: LayerConfig, tensor_id: int, shape, sigma: float, step: int = 0):
-    a = rng(cfg.config_id, tensor_id, step).standard_normal(shape, dtype=np.float32)
+    a = _standard_normal(cfg.config_id, tensor_id, step, shape)
     if sigma != 1.0:
         a *= np.float32(sigma)
-    return to_bf16_values(a) if cfg.dtype == "bf16" else a
+    return _round_bf16_inplace(a) if cfg.dtype == "bf16" else a
 
 
 def weights(cfg: LayerConfig, gamma: str = "ones") -> dict:
@@ -222,11 +275,10 @@ def synthetic_cache(cfg: LayerConfig, bt: BlockTable, context_lens, case: int = 
             continue
         nblk = (prior + BS - 1) // BS
         for which, cache, tid in ((0, kc, T_KCACHE), (1, vc, T_VCACHE)):
-            vals = rng(cfg.config_id, tid, 1000 * case + b).standard_normal(
-                (nblk * BS, Hkv, D), dtype=np.float32)
+            vals = _standard_normal(cfg.config_id, tid, 1000 * case + b, (nblk * BS, Hkv, D))
             vals *= np.float32(sigma)
             if cfg.dtype == "bf16":
-                bits = bf16_bits(to_bf16_values(vals))
+                bits = bf16_bits(_round_bf16_inplace(vals))
             else:
                 bits = vals.view(np.uint32)
             bits = bits.reshape(nblk, BS, Hkv, D).transpose(0, 2, 1, 3)
