@@ -76,6 +76,7 @@ def test_rmsnorm_residual(dtype, T, H):
 GEMM_SHAPES = [
     (1, 256, 64), (5, 512, 200), (16, 1024, 256), (33, 768, 520), (64, 4096, 512),
     (200, 1024, 4096), (600, 2048, 256), (2048, 16384, 320), (100, 96, 688),
+    (700, 22000, 200),   # 256x256 prefill tile: M tail, ragged N, K tail
 ]
 
 
@@ -309,3 +310,41 @@ def test_attn_decode_permutation_bit_identical():
                                 dev_i32(ctx), int(ctx.max()), out)
         outs.append(host_bits(out))
     assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------------------
+# the 256x256 prefill tile through the paired epilogues (sampled rows)
+# ---------------------------------------------------------------------------
+
+def _rows(M):
+    return np.unique(np.concatenate([np.arange(8), R.integers(0, M, 40), [M - 1]]))
+
+
+def test_qkv_rope_large_tile():
+    T, H, Hq, Hkv, D = 2048, 256, 32, 16, 128      # 8 x 32 tiles of 256
+    print(f"qkv_rope large T={T}", flush=True)
+    x = rnd(T, H)
+    wq, wk, wv = (rnd(h * D, H, scale=0.05) for h in (Hq, Hkv, Hkv))
+    pos = R.integers(0, 4096, T).astype(np.int32)
+    cs = torch.empty(4096, D, device=DEV)
+    dl.dl_rope_table_fill(cs, 4096, D, 1e4)
+    q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    dl.dl_qkv_rope(dev_bf16(x), dev_bf16(wq), dev_bf16(wk), dev_bf16(wv), dev_i32(pos), cs, q, k, v)
+    rows = _rows(T)
+    rq, rk, rv = oracle.qkv_rope(x[rows], wq, wk, wv, pos[rows], 1e4, Hq, Hkv, D, mode=oracle.BF16)
+    assert_bf16_close(host(q)[rows], rq, "q")
+    assert_bf16_close(host(k)[rows], rk, "k")
+    assert_bf16_close(host(v)[rows], rv, "v")
+
+
+def test_gate_up_large_tile_with_tails():
+    T, H, I = 1000, 200, 16384                     # 4 x 128 tiles; M and K tails
+    print(f"gate/up large T={T} H={H} I={I}", flush=True)
+    x = rnd(T, H)
+    wg, wu = (rnd(I, H, scale=0.05) for _ in range(2))
+    a = torch.empty(T, I, dtype=torch.bfloat16, device=DEV)
+    dl.dl_gate_up_silu(dev_bf16(x), dev_bf16(wg), dev_bf16(wu), a)
+    rows = _rows(T)
+    assert_bf16_close(host(a)[rows], oracle.swiglu(x[rows], wg, wu, mode=oracle.BF16), "a")

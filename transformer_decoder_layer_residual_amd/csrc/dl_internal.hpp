@@ -19,7 +19,7 @@ namespace dl {
 // kernel reduces them and applies the epilogue.
 // ---------------------------------------------------------------------------
 enum GemmCfg : int {
-  kCfg256 = 0,   // BM 256, BN 256, 4 waves (2x2), wave tile 128x128
+  kCfg256 = 0,   // BM 256, BN 256, 8 waves (2x4), wave tile 128x64 (bf16 prefill)
   kCfg128 = 1,   // BM 128, BN 128, 4 waves (2x2), wave tile 64x64
   kCfg64 = 2,    // BM 64,  BN 128, 4 waves (1x4), wave tile 64x32
   kCfg16 = 3,    // BM 16,  BN 128, 4 waves (1x4), wave tile 16x32

@@ -309,6 +309,127 @@ gemm_kernel(const T* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large prefill tile: 256 x 256 x 64, 8 waves (2 x 4), wave tile 128 x 64.
+// Loads are branch-free (rows past M or N are clamped to valid memory; their
+// results are never stored) and only the last K tile, when K is not a
+// multiple of 64, takes the zero-filling path.  MFMA fragments of the next
+// 32-wide k step are read from LDS while the current step's MFMAs run.
+// ---------------------------------------------------------------------------
+template <class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
+                int tiles_n) {
+  constexpr int BM = 256, BN = 256, BK = 64, WN = 4, NT = 512;
+  constexpr int MS = BM / (16 * 2), NS = BN / (16 * WN);
+  constexpr int LS = BK + 8;
+  constexpr int RSTEP = NT / 8;
+  constexpr int A_IT = BM / RSTEP, W_IT = BN / RSTEP;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][(BM + BN) * LS];
+
+  int bid = blockIdx.x;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int gsz = GM * tiles_n;
+  const int first_m = (bid / gsz) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % gsz) % gm;
+  const int tn = (bid % gsz) / gm;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int chunk = t & 7, r0 = t >> 3;
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
+
+  const bf16* xp[A_IT];
+  const bf16* wp[W_IT];
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int m = min(tm * BM + r0 + i * RSTEP, M - 1);  // clamped: rows >= M never stored
+    xp[i] = X + (int64_t)m * K + chunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < W_IT; ++i) {
+    const bf16* b = map.row(tn, r0 + i * RSTEP);
+    wp[i] = (b ? b : X) + chunk * 8;  // missing rows read valid memory; never stored
+  }
+  const int nkt = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
+  u32x4 ra[A_IT], rw[W_IT];
+  const u32x4 zero = {0, 0, 0, 0};
+  auto gload = [&](int k0, bool masked) {
+    if (!masked) {
+#pragma unroll
+      for (int i = 0; i < A_IT; ++i) ra[i] = ld16(xp[i] + k0);
+#pragma unroll
+      for (int i = 0; i < W_IT; ++i) rw[i] = ld16(wp[i] + k0);
+    } else {
+      const bool kin = k0 + chunk * 8 < K;
+#pragma unroll
+      for (int i = 0; i < A_IT; ++i) ra[i] = kin ? ld16(xp[i] + k0) : zero;
+#pragma unroll
+      for (int i = 0; i < W_IT; ++i) rw[i] = kin ? ld16(wp[i] + k0) : zero;
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16* As = smem[buf];
+    bf16* Ws = As + BM * LS;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) st16(As + (r0 + i * RSTEP) * LS + chunk * 8, ra[i]);
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) st16(Ws + (r0 + i * RSTEP) * LS + chunk * 8, rw[i]);
+  };
+  Frag<bf16> fx[2][MS], fw[2][NS];
+  auto lds_frags = [&](int buf, int kk, int set) {
+    const bf16* As = smem[buf];
+    const bf16* Ws = As + BM * LS;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int nsub = (s < NS / 2) ? wn * (NS / 2) + s : BN / 32 + wn * (NS / 2) + (s - NS / 2);
+      fw[set][s].load(Ws + (nsub * 16 + fr) * LS + kk + fk);
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i) fx[set][i].load(As + ((wm * MS + i) * 16 + fr) * LS + kk + fk);
+  };
+  f32x4 acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc[i][s] = mfma_k32(fw[set][s], fx[set][i], acc[i][s]);
+  };
+
+  gload(0, nkt == 1 && ktail);
+  sstore(0);
+  __syncthreads();
+  lds_frags(0, 0, 0);
+  for (int it = 0; it < nkt; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nkt) gload((it + 1) * BK, (it + 2 == nkt) && ktail);
+    lds_frags(cur, 32, 1);
+    mfmas(0);
+    mfmas(1);
+    if (it + 1 < nkt) sstore(cur ^ 1);
+    __syncthreads();
+    if (it + 1 < nkt) lds_frags(cur ^ 1, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int m = tm * BM + (wm * MS + i) * 16 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int s = 0; s < NS / 2; ++s) {
+      const int j = (wn * (NS / 2) + s) * 16 + 4 * (lane >> 4);
+      epi(m, tn, j, acc[i][s], acc[i][s + NS / 2]);
+    }
+  }
+}
+
 // Deterministic split-K reduction (fixed split order) followed by the
 // epilogue.  One thread per (row, tile, group of 4 first-half columns).
 // Partials are [split][M][NP] with NP = tiles * BN (padded to whole tiles).
@@ -349,7 +470,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   if (is_f32) {
     cfg = kCfg32s;
   } else if (M >= 512) {
-    cfg = (fits(kCfg256) && tiles(kCfg256) >= 512) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
+    cfg = (fits(kCfg256) && tiles(kCfg256) >= 256) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
   } else if (M > 16) {
     cfg = fits(kCfg64) ? kCfg64 : kCfg32s;
   } else {
@@ -367,7 +488,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
     splits = want < 1 ? 1 : want;
     const int max_splits = ktiles / 4 > 0 ? ktiles / 4 : 1;
     if (splits > max_splits) splits = max_splits;
-  } else if (nt < 128) {
+  } else if (nt < 128 && cfg != kCfg256) {
     const int want = (256 + nt - 1) / nt;
     const int max_splits = ktiles / 8 > 0 ? ktiles / 8 : 1;
     splits = want < max_splits ? want : max_splits;
@@ -399,7 +520,15 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
   return hipGetLastError();
 }
 
-typedef Tile<256, 256, 2, 2> T256;
+template <class Map, class Epi>
+static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
+                             hipStream_t st) {
+  const int tiles_m = (M + 255) / 256, tiles_n = (NL + 255) / 256;
+  hipLaunchKernelGGL((gemm_big_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st, x, M,
+                     K, map, epi, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 typedef Tile<128, 128, 2, 2> T128;
 typedef Tile<64, 128, 1, 4> T64;
 typedef Tile<16, 128, 1, 4> T16;
@@ -415,7 +544,7 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
     return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
   } else {
     switch (pl.cfg) {
-      case kCfg256: return launch_cfg<T, T256>(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, pl, ws, st);
+      case kCfg256: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st);
       case kCfg128: return launch_cfg<T, T128>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg16: return launch_cfg<T, T16>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
