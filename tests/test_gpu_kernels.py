@@ -339,6 +339,29 @@ def test_qkv_rope_large_tile():
     assert_bf16_close(host(v)[rows], rv, "v")
 
 
+def test_gate_up_pingpong_tile():
+    T, H, I = 1000, 256, 16384                     # 4 x 128 tiles of 256 x 256, M tail
+    print(f"gate/up ping-pong T={T} H={H} I={I}", flush=True)
+    x = rnd(T, H)
+    wg, wu = (rnd(I, H, scale=0.05) for _ in range(2))
+    a = torch.empty(T, I, dtype=torch.bfloat16, device=DEV)
+    dl.dl_gate_up_silu(dev_bf16(x), dev_bf16(wg), dev_bf16(wu), a)
+    rows = _rows(T)
+    assert_bf16_close(host(a)[rows], oracle.swiglu(x[rows], wg, wu, mode=oracle.BF16), "a")
+
+
+def test_down_residual_pingpong_128_tile():
+    T, H, I = 520, 1024, 2048                      # 128-row ping-pong tiles, M tail
+    print(f"down ping-pong-128 T={T}", flush=True)
+    a = rnd(T, I)
+    wd = rnd(H, I, scale=0.05)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    y = torch.empty(T, H, device=DEV)
+    dl.dl_down_residual(dev_bf16(a), dev_bf16(wd), y, residual=dev_f32(r))
+    rows = _rows(T)
+    assert_f32_close(host(y)[rows], oracle.down_residual(a[rows], wd, r[rows]), "down")
+
+
 def test_gate_up_large_tile_with_tails():
     T, H, I = 1000, 200, 16384                     # 4 x 128 tiles; M and K tails
     print(f"gate/up large T={T} H={H} I={I}", flush=True)

@@ -123,6 +123,14 @@ __device__ __forceinline__ f32x4 mfma_k32(const Frag<float>& a, const Frag<float
   return c;
 }
 
+// 32x32x16 bf16 MFMA: lane l holds 8 consecutive k (from k = 8*(l/32)) of row
+// l % 32 for both operands; output lane l holds C[8*i + 4*(l/32) + j][l % 32]
+// in element 4*i + j (i, j = 0..3), rows over the first operand.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // Store 4 consecutive floats as T.
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};

@@ -19,12 +19,14 @@ namespace dl {
 // kernel reduces them and applies the epilogue.
 // ---------------------------------------------------------------------------
 enum GemmCfg : int {
-  kCfg256 = 0,   // BM 256, BN 256, 8 waves (2x4), wave tile 128x64 (bf16 prefill)
+  kCfg256 = 0,   // BM 256, BN 256, 8 waves: ping-pong kernel (K % 64 == 0) or the
+                 // double-buffered big-tile kernel (K tail); bf16 prefill
   kCfg128 = 1,   // BM 128, BN 128, 4 waves (2x2), wave tile 64x64
   kCfg64 = 2,    // BM 64,  BN 128, 4 waves (1x4), wave tile 64x32
   kCfg16 = 3,    // BM 16,  BN 128, 4 waves (1x4), wave tile 16x32
   kCfg32s = 4,   // BM 32,  BN 32,  2 waves (2x1), wave tile 16x32 (small/odd shapes)
-  kCfgCount = 5
+  kCfgPP128 = 5, // BM 128, BN 256, 8 waves: ping-pong kernel (K % 64 == 0), bf16
+  kCfgCount = 6
 };
 
 struct GemmPlan {

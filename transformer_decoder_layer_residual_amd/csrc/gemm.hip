@@ -310,21 +310,24 @@ gemm_kernel(const T* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m
 }
 
 // ---------------------------------------------------------------------------
-// Large prefill tile: 256 x 256 x 64, 8 waves (2 x 4), wave tile 128 x 64.
+// Large prefill tile: 256 x 256 x 64, 8 waves (2 x 4), wave tile 128 x 64 made
+// of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16 (the bf16 MFMA shape that
+// sustains close to the chip's peak; 16x16x32 issues at well under half of it).
 // Loads are branch-free (rows past M or N are clamped to valid memory; their
 // results are never stored) and only the last K tile, when K is not a
 // multiple of 64, takes the zero-filling path.  MFMA fragments of the next
-// 32-wide k step are read from LDS while the current step's MFMAs run.
+// 16-wide k step are read from LDS while the current step's MFMAs run.
 // ---------------------------------------------------------------------------
 template <class Map, class Epi>
 __global__ void __launch_bounds__(512, 1)
 gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
                 int tiles_n) {
   constexpr int BM = 256, BN = 256, BK = 64, WN = 4, NT = 512;
-  constexpr int MS = BM / (16 * 2), NS = BN / (16 * WN);
+  constexpr int MS = BM / (32 * 2), NS = BN / (32 * WN);  // 4 x 2 blocks of 32x32
   constexpr int LS = BK + 8;
   constexpr int RSTEP = NT / 8;
   constexpr int A_IT = BM / RSTEP, W_IT = BN / RSTEP;
+  static_assert(NS == 2, "one first-half and one partner block per wave");
   __shared__ __attribute__((aligned(16))) bf16 smem[2][(BM + BN) * LS];
 
   int bid = blockIdx.x;
@@ -340,7 +343,7 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int chunk = t & 7, r0 = t >> 3;
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
 
   const bf16* xp[A_IT];
   const bf16* wp[W_IT];
@@ -380,28 +383,31 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 #pragma unroll
     for (int i = 0; i < W_IT; ++i) st16(Ws + (r0 + i * RSTEP) * LS + chunk * 8, rw[i]);
   };
-  Frag<bf16> fx[2][MS], fw[2][NS];
-  auto lds_frags = [&](int buf, int kk, int set) {
+  bf16x8 fx[2][MS], fw[2][NS];
+  auto lds_frags = [&](int buf, int ks, int set) {
     const bf16* As = smem[buf];
     const bf16* Ws = As + BM * LS;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int nsub = (s < NS / 2) ? wn * (NS / 2) + s : BN / 32 + wn * (NS / 2) + (s - NS / 2);
-      fw[set][s].load(Ws + (nsub * 16 + fr) * LS + kk + fk);
+      const int nsub = (s == 0) ? wn : BN / 64 + wn;  // 32-col blocks: first half, partner half
+      fw[set][s] = *reinterpret_cast<const bf16x8*>(Ws + (nsub * 32 + fr) * LS + ks * 16 + fk);
     }
 #pragma unroll
-    for (int i = 0; i < MS; ++i) fx[set][i].load(As + ((wm * MS + i) * 16 + fr) * LS + kk + fk);
+    for (int i = 0; i < MS; ++i)
+      fx[set][i] = *reinterpret_cast<const bf16x8*>(As + ((wm * MS + i) * 32 + fr) * LS + ks * 16 + fk);
   };
-  f32x4 acc[MS][NS];
+  f32x16 acc[MS][NS];
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
   auto mfmas = [&](int set) {
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc[i][s] = mfma_k32(fw[set][s], fx[set][i], acc[i][s]);
+      for (int s = 0; s < NS; ++s) acc[i][s] = mfma_32x32x16(fw[set][s], fx[set][i], acc[i][s]);
   };
 
   gload(0, nkt == 1 && ktail);
@@ -411,22 +417,187 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
   for (int it = 0; it < nkt; ++it) {
     const int cur = it & 1;
     if (it + 1 < nkt) gload((it + 1) * BK, (it + 2 == nkt) && ktail);
-    lds_frags(cur, 32, 1);
-    mfmas(0);
-    mfmas(1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) lds_frags(cur, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+    }
     if (it + 1 < nkt) sstore(cur ^ 1);
     __syncthreads();
     if (it + 1 < nkt) lds_frags(cur ^ 1, 0, 0);
   }
+  // epilogue: lane owns column m = ... + (lane & 31) and rows n = 8*i + 4*(lane/32) + j
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    const int m = tm * BM + (wm * MS + i) * 16 + fr;
+    const int m = tm * BM + (wm * MS + i) * 32 + fr;
     if (m >= M) continue;
 #pragma unroll
-    for (int s = 0; s < NS / 2; ++s) {
-      const int j = (wn * (NS / 2) + s) * 16 + 4 * (lane >> 4);
-      epi(m, tn, j, acc[i][s], acc[i][s + NS / 2]);
+    for (int g = 0; g < 4; ++g) {
+      const int j = wn * 32 + 8 * g + 4 * (lane >> 5);
+      const f32x4 a = {acc[i][0][4 * g], acc[i][0][4 * g + 1], acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]};
+      const f32x4 b = {acc[i][1][4 * g], acc[i][1][4 * g + 1], acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]};
+      epi(m, tn, j, a, b);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong prefill tile: BM x 256 x 64, 8 waves in two groups of 4.
+//
+// Group g computes output rows [128 g, 128 g + 128) of the tile; each wave a
+// 64 x 128 block (2 x 4 blocks of 32 x 32, v_mfma_f32_32x32x16_bf16).  The
+// groups run one barrier phase apart: while one group issues its 32 MFMAs for
+// k-tile t, the other reads all its MFMA fragments of the next k-tile from
+// LDS and issues global->LDS loads, so each SIMD (one wave of each group)
+// always has a wave feeding the matrix pipe.
+//   group 0: MEM(t) in phase 2t+1, COMP(t) in phase 2t+2
+//   group 1: MEM(t) in phase 2t+2, COMP(t) in phase 2t+3
+// K-tiles live in two LDS stages; tile t+2 is loaded into tile t's stage in
+// phase 2t+3 (after both groups read tile t) and waited for at the end of
+// phase 2t+4, before either group reads it.
+// Global->LDS loads go straight to LDS (global_load_lds_dwordx4, 1 KB per wave
+// instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
+// so the 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int pp_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BM, class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
+               int tiles_n) {
+  constexpr int BN = 256, BK = 64;
+  constexpr int ROWB = BK * 2;                      // 128 bytes per LDS row
+  constexpr int STAGE = (BM + BN) * ROWB;           // 64 KB (BM 256) or 48 KB (BM 128)
+  constexpr int MS = BM / 128, NS = 4;              // 32x32 blocks per wave
+  constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
+  constexpr int LI = RPW / 8;                       // load instructions per wave per stage
+  constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  int bid = blockIdx.x;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int gsz = GM * tiles_n;
+  const int first_m = (bid / gsz) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % gsz) % gm;
+  const int tn = (bid % gsz) / gm;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int grp = wave >> 2, wig = wave & 3;        // group, wave in group
+  const int wm = wig >> 1, wn = wig & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
+  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), 8 rows per instruction.
+  const unsigned char* src[LI];
+#pragma unroll
+  for (int i = 0; i < LI; ++i) {
+    const int row = wave * RPW + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ pp_swz(row);         // logical chunk this lane fetches
+    const bf16* base;
+    if (row < BM) {
+      base = X + (int64_t)min(tm * BM + row, M - 1) * K;   // rows >= M: valid, never stored
+    } else {
+      const bf16* b = map.row(tn, row - BM);
+      base = b ? b : X;                                     // missing rows: valid, never stored
+    }
+    src[i] = reinterpret_cast<const unsigned char*>(base) + c * 16;
+  }
+  auto issue_loads = [&](int kt) {
+    unsigned char* dst = smem + (kt & 1) * STAGE + wave * RPW * ROWB;
+    const int64_t koff = (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < LI; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[i] + koff),
+          (__attribute__((address_space(3))) void*)(dst + i * 8 * ROWB), 16, 0, 0);
+  };
+
+  // ---- fragments (all 4 k16 steps of a k-tile)
+  bf16x8 fx[4][MS], fw[4][NS];
+  auto read_frags = [&](int kt) {
+    const unsigned char* st = smem + (kt & 1) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks * 2 + fh;                    // logical 16 B chunk
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const int r = grp * GR + wm * WR + i * 32 + fr;
+        fx[ks][i] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz(r)) << 4));
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int blk = (s < 2) ? 2 * wn + s : 4 + 2 * wn + (s - 2);  // first half, partners
+        const int r = BM + blk * 32 + fr;
+        fw[ks][s] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz(r)) << 4));
+      }
+    }
+  };
+  f32x16 acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
+  auto compute = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[i][s] = mfma_32x32x16(fw[ks][s], fx[ks][i], acc[i][s]);
+  };
+#define DL_PHASE_END()                                     \
+  do {                                                     \
+    __builtin_amdgcn_sched_barrier(0);                     \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    __builtin_amdgcn_sched_barrier(0);                     \
+  } while (0)
+#define DL_WAIT_LOADS() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+
+  const int nkt = K / BK;
+  issue_loads(0);
+  if (nkt > 1) issue_loads(1);
+  DL_WAIT_LOADS();
+  DL_PHASE_END();                                   // phase 1 begins
+  if (grp == 1) DL_PHASE_END();                     // group 1 starts one phase later
+  for (int kt = 0; kt < nkt; ++kt) {
+    // MEM(kt)
+    read_frags(kt);
+    if (grp == 0) {
+      if (kt >= 1 && kt + 1 < nkt) issue_loads(kt + 1);
+    } else {
+      DL_WAIT_LOADS();                              // tile kt+1 (issued in COMP(kt-1))
+    }
+    DL_PHASE_END();
+    // COMP(kt)
+    if (grp == 1 && kt + 2 < nkt) issue_loads(kt + 2);
+    compute();
+    if (grp == 0) DL_WAIT_LOADS();                  // tile kt+1 (issued in MEM(kt))
+    DL_PHASE_END();
+  }
+  if (grp == 0) DL_PHASE_END();                     // balance group 1's extra barrier
+#undef DL_PHASE_END
+#undef DL_WAIT_LOADS
+
+  // epilogue: lane owns column m and rows n = 8 q + 4 (lane / 32) + j of each block
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int m = tm * BM + grp * GR + wm * WR + i * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = (2 * wn + b) * 32 + 8 * q + 4 * fh;
+        const f32x4 lo = {acc[i][b][4 * q], acc[i][b][4 * q + 1], acc[i][b][4 * q + 2], acc[i][b][4 * q + 3]};
+        const f32x4 hi = {acc[i][b + 2][4 * q], acc[i][b + 2][4 * q + 1], acc[i][b + 2][4 * q + 2],
+                          acc[i][b + 2][4 * q + 3]};
+        epi(m, tn, j, lo, hi);
+      }
   }
 }
 
@@ -457,8 +628,8 @@ splitk_reduce(const float* __restrict__ partial, int splits, int M, int NP, int 
 // ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
-static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32};
-static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32};
+static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32, 128};
+static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32, 256};
 
 GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   GemmPlan pl{};
@@ -469,6 +640,9 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   int cfg;
   if (is_f32) {
     cfg = kCfg32s;
+  } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
+    // ping-pong kernel; 256-row tiles when they fill the chip, else 128
+    cfg = tiles(kCfg256) >= 256 ? kCfg256 : kCfgPP128;
   } else if (M >= 512) {
     cfg = (fits(kCfg256) && tiles(kCfg256) >= 256) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
   } else if (M > 16) {
@@ -482,13 +656,16 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   const int nt = tiles(cfg);
   const int ktiles = (K + bk - 1) / bk;
   int splits = 1;
-  if (M <= 256) {
+  const bool single_pass = (cfg == kCfg256 || cfg == kCfgPP128);  // no split-K variant
+  if (single_pass) {
+    splits = 1;
+  } else if (M <= 256) {
     // weight-streaming shapes: enough workgroups to keep HBM busy
     const int want = (1024 + nt - 1) / nt;
     splits = want < 1 ? 1 : want;
     const int max_splits = ktiles / 4 > 0 ? ktiles / 4 : 1;
     if (splits > max_splits) splits = max_splits;
-  } else if (nt < 128 && cfg != kCfg256) {
+  } else if (nt < 128) {
     const int want = (256 + nt - 1) / nt;
     const int max_splits = ktiles / 8 > 0 ? ktiles / 8 : 1;
     splits = want < max_splits ? want : max_splits;
@@ -522,10 +699,21 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
 
 template <class Map, class Epi>
 static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
-                             hipStream_t st) {
-  const int tiles_m = (M + 255) / 256, tiles_n = (NL + 255) / 256;
-  hipLaunchKernelGGL((gemm_big_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st, x, M,
-                     K, map, epi, tiles_m, tiles_n);
+                             hipStream_t st, int bm = 256) {
+  const int tiles_n = (NL + 255) / 256;
+  if (K % 64 == 0 && bm == 128) {
+    const int tiles_m = (M + 127) / 128;
+    hipLaunchKernelGGL((gemm_pp_kernel<128, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
+                       x, M, K, map, epi, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
+  const int tiles_m = (M + 255) / 256;
+  if (K % 64 == 0)
+    hipLaunchKernelGGL((gemm_pp_kernel<256, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
+                       x, M, K, map, epi, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st, x,
+                       M, K, map, epi, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -544,7 +732,8 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
     return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
   } else {
     switch (pl.cfg) {
-      case kCfg256: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st);
+      case kCfg256: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 256);
+      case kCfgPP128: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 128);
       case kCfg128: return launch_cfg<T, T128>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg16: return launch_cfg<T, T16>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
