@@ -16,12 +16,13 @@
 //     results);
 //   * the whole query group (Hq/Hkv heads sharing the kv head) is handled by
 //     the workgroup, so each K/V byte serves all of them;
-//   * each KV block is streamed into LDS with coalesced 16-byte loads, while
-//     the next block's loads are already in flight in registers;
-//   * scores: BS tokens x (256/BS) threads per token, each thread covering a
-//     D-slice for all group heads, combined with lane shuffles;
-//   * online softmax in the log2 domain per head; PV accumulates 4 output
-//     columns x all group heads per thread;
+//   * each KV block is read straight into registers with 16-byte loads (a
+//     block of one head is one contiguous BS x D run), and the next block's
+//     loads are in flight while the current one is processed;
+//   * scores: each thread holds a 16-byte slice of a token row; partial dots
+//     of all group heads are reduced over the token's lanes with shuffles;
+//   * online softmax in the log2 domain, kept per wave over the tokens the
+//     wave owns, so the block loop needs no barrier; waves merge once;
 //   * each split writes (o, m, l) in fp32; a second kernel combines the
 //     splits in fixed order.
 #include "dl_internal.hpp"
@@ -53,20 +54,20 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
                    const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ ctx,
                    int Hq, int Hkv, int BS, float scale_log2, int chunk_blocks, int max_splits,
                    float* __restrict__ ws, int num_blocks) {
+  // Register-resident streaming: thread t owns 16-byte chunk c = t % LPT of
+  // tokens tok = t / LPT + TPI * i (i = 0 .. NI-1) of every KV block, for K
+  // and V alike.  Scores are reduced over the LPT lanes of a token with lane
+  // shuffles; every wave keeps its own online softmax (m, l, o) over the
+  // tokens it owns, so the block loop has no workgroup barrier; the four
+  // waves are merged once at the end of the split.
   constexpr int NT = kDecThreads, VE = 16 / sizeof(T);
-  constexpr int KLS = D + VE;          // padded LDS row
-  constexpr int U = D / 4;             // PV units (4 columns each)
-  constexpr int TG = NT / U;           // token groups in PV
-  constexpr int VPB_MAX = kDecMaxBS * (D / VE);          // 16 B vectors per K block
-  constexpr int LD_IT = (VPB_MAX + NT - 1) / NT;          // per thread, per tensor
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  T* Ks = reinterpret_cast<T*>(smem_raw);
-  T* Vs = Ks + kDecMaxBS * KLS;
-  float* Ps = reinterpret_cast<float*>(Vs + kDecMaxBS * KLS);  // [G][BS]
-  float* Qs = Ps + G * kDecMaxBS;                              // [G][D]
-  float* st = Qs + G * D;                                      // m[G], l[G], alpha[G]
-  float* red = reinterpret_cast<float*>(smem_raw);             // [TG][G][D], aliases Ks/Vs
-  static_assert(TG > 1 && TG * G * D * 4 <= 2 * kDecMaxBS * KLS * (int)sizeof(T), "red alias");
+  constexpr int LPT = D / VE;                 // lanes per token row
+  constexpr int TPI = NT / LPT;               // tokens per load step (whole workgroup)
+  constexpr int NI = (kDecMaxBS + TPI - 1) / TPI;
+  constexpr int NWV = NT / kWave;
+  constexpr bool PREFETCH = G <= 2;           // register budget: double-buffer small groups
+  __shared__ float red_m[NWV][G], red_l[NWV][G];
+  __shared__ __attribute__((aligned(16))) float red_o[NWV][G][D];
 
   const int b = blockIdx.z, g = blockIdx.y, split = blockIdx.x;
   // lengths beyond the table or the host-declared maximum are clamped, so a
@@ -77,148 +78,154 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   if (blk_begin >= nblk) return;
   const int blk_end = min(nblk, blk_begin + chunk_blocks);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid % LPT, tok0 = tid / LPT;
 
-  for (int i = tid; i < G * D; i += NT)
-    Qs[i] = to_f32(q[((int64_t)b * Hq + g * G) * D + i]) * scale_log2;
-  if (tid < G) {
-    st[tid] = -INFINITY;
-    st[G + tid] = 0.f;
+  // this thread's slice of the (pre-scaled) query of every head in the group
+  float qf[G][VE];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float tmp[VE];
+    unpack16(ld16(q + ((int64_t)b * Hq + g * G + h) * D + c * VE), tmp, T());
+#pragma unroll
+    for (int e = 0; e < VE; ++e) qf[h][e] = tmp[e] * scale_log2;
+  }
+  float m[G], l[G], o[G][VE];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[h][e] = 0.f;
   }
 
-  const int vpb = BS * (D / VE);
-  u32x4 rk[LD_IT], rv[LD_IT];
+  u32x4 kr[NI], vr[NI];
   auto gload = [&](int blk) {
     int phys = bt[(int64_t)b * max_blocks + blk];
     phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;  // invalid entry: no fault
-    const int64_t base = (((int64_t)phys * Hkv + g) * BS) * D;
+    const int64_t base = (((int64_t)phys * Hkv + g) * BS) * D + c * VE;
 #pragma unroll
-    for (int i = 0; i < LD_IT; ++i) {
-      const int vi = tid + i * NT;
-      if (vi < vpb) {
-        rk[i] = ld16(kc + base + (int64_t)vi * VE);
-        rv[i] = ld16(vc + base + (int64_t)vi * VE);
-      }
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < LD_IT; ++i) {
-      const int vi = tid + i * NT;
-      if (vi < vpb) {
-        const int tok = vi / (D / VE), c = vi % (D / VE);
-        st16(Ks + tok * KLS + c * VE, rk[i]);
-        st16(Vs + tok * KLS + c * VE, rv[i]);
+    for (int i = 0; i < NI; ++i) {
+      const int tok = tok0 + i * TPI;
+      if (tok < BS) {
+        kr[i] = ld16(kc + base + (int64_t)tok * D);
+        vr[i] = ld16(vc + base + (int64_t)tok * D);
       }
     }
   };
 
-  // PV ownership
-  const int u = tid % U, tg = tid / U;
-  float o[G][4];
-#pragma unroll
-  for (int i = 0; i < G; ++i) o[i][0] = o[i][1] = o[i][2] = o[i][3] = 0.f;
-
-  // score ownership
-  const int tpt = NT / BS;           // threads per token (power of 2)
-  const int dpt = D / tpt;           // D-slice per thread (multiple of 4)
-  const int stok = tid / tpt, part = tid % tpt;
-
-  gload(blk_begin);
+  if (PREFETCH) gload(blk_begin);
   for (int blk = blk_begin; blk < blk_end; ++blk) {
-    __syncthreads();  // previous block fully consumed (and Qs / stats visible)
-    sstore();
-    if (blk + 1 < blk_end) gload(blk + 1);
-    __syncthreads();
+    if (!PREFETCH) gload(blk);
+    u32x4 kcur[NI], vcur[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kcur[i] = kr[i];
+      vcur[i] = vr[i];
+    }
+    if (PREFETCH && blk + 1 < blk_end) gload(blk + 1);   // next block in flight during the math
     const int ntok = min(BS, n - blk * BS);
 
-    // scores
-    {
-      float acc[G];
+    float sc[NI][G];
 #pragma unroll
-      for (int i = 0; i < G; ++i) acc[i] = 0.f;
-      const T* kr = Ks + stok * KLS + part * dpt;
-      const float* qr = Qs + part * dpt;
-      for (int e = 0; e < dpt; e += 4) {
-        float kv[4];
-        load4(kr + e, kv);
+    for (int i = 0; i < NI; ++i) {
+      float kv[VE];
+      unpack16(kcur[i], kv, T());
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(qr + i * D + e);
-          acc[i] += qv[0] * kv[0] + qv[1] * kv[1] + qv[2] * kv[2] + qv[3] * kv[3];
-        }
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc += qf[h][e] * kv[e];
+        sc[i][h] = acc;
       }
-      for (int off = tpt >> 1; off > 0; off >>= 1)
-#pragma unroll
-        for (int i = 0; i < G; ++i) acc[i] += __shfl_xor(acc[i], off, kWave);
-      if (part == 0)
-#pragma unroll
-        for (int i = 0; i < G; ++i) Ps[i * kDecMaxBS + stok] = stok < ntok ? acc[i] : -INFINITY;
     }
-    __syncthreads();
-
-    // online softmax, one wave per head
-    for (int i = wave; i < G; i += NT / kWave) {
+    // reduce partial dots over the LPT lanes of each token
+#pragma unroll
+    for (int off = LPT / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[i][h] += __shfl_xor(sc[i][h], off, kWave);
+    // mask, then the wave's online softmax over its tokens of this block
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
       float mx = -INFINITY;
-      for (int t = lane; t < BS; t += kWave) mx = fmaxf(mx, Ps[i * kDecMaxBS + t]);
-      mx = wave_max(mx);
-      const float m_old = st[i];
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-      for (int t = lane; t < BS; t += kWave) {
-        const float p = exp2f(Ps[i * kDecMaxBS + t] - m_new);
-        Ps[i * kDecMaxBS + t] = p;
-        sum += p;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int tok = tok0 + i * TPI;
+        if (!(tok < ntok)) sc[i][h] = -INFINITY;
+        mx = fmaxf(mx, sc[i][h]);
       }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        const float alpha = exp2f(m_old - m_new);
-        st[i] = m_new;
-        st[G + i] = st[G + i] * alpha + sum;
-        st[2 * G + i] = alpha;
+#pragma unroll
+      for (int off = LPT; off < kWave; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+      const float m_new = fmaxf(m[h], mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m[h] - m_new);
+      m[h] = m_new;
+      l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[h][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float pi = sc[i][h] == -INFINITY ? 0.f : exp2f(sc[i][h] - m_new);
+        sc[i][h] = pi;
+        l[h] += pi;     // per-lane partial; lanes of one token all add the same p
       }
     }
-    __syncthreads();
-
-    // PV
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float a = st[2 * G + i];
-      o[i][0] *= a;
-      o[i][1] *= a;
-      o[i][2] *= a;
-      o[i][3] *= a;
-    }
-    for (int t = tg; t < ntok; t += TG) {
-      float vv[4];
-      load4(Vs + t * KLS + 4 * u, vv);
+    for (int i = 0; i < NI; ++i) {
+      const int tok = tok0 + i * TPI;
+      if (tok < ntok) {
+        float vv[VE];
+        unpack16(vcur[i], vv, T());
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float p = Ps[i * kDecMaxBS + t];
-        o[i][0] += p * vv[0];
-        o[i][1] += p * vv[1];
-        o[i][2] += p * vv[2];
-        o[i][3] += p * vv[3];
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) o[h][e] += sc[i][h] * vv[e];
       }
     }
   }
 
-  // reduce PV partials over token groups (fixed order), write the split
-  __syncthreads();  // Ks / Vs no longer read: reuse them for the reduction
+  // merge the token lanes of each wave (fixed order), then the waves
 #pragma unroll
-  for (int i = 0; i < G; ++i)
-    *reinterpret_cast<f32x4*>(red + (tg * G + i) * D + 4 * u) =
-        f32x4{o[i][0], o[i][1], o[i][2], o[i][3]};
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1) {
+      l[h] += __shfl_xor(l[h], off, kWave);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[h][e] += __shfl_xor(o[h][e], off, kWave);
+    }
+  }
+  // lanes 0 .. LPT-1 now hold the wave's o slices; every lane of a token
+  // group carried the same l, so lane 0's value is the wave's sum
+  if (lane < LPT) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (c == 0) {
+        red_m[wave][h] = m[h];
+        red_l[wave][h] = l[h];
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) red_o[wave][h][c * VE + e] = o[h][e];
+    }
+  }
   __syncthreads();
   const int64_t row0 = ((int64_t)b * Hq + g * G) * max_splits + split;
   for (int idx = tid; idx < G * D; idx += NT) {
-    const int i = idx / D, d = idx % D;
-    float sacc = 0.f;
-    for (int z = 0; z < TG; ++z) sacc += red[(z * G + i) * D + d];
-    float* dst = ws + (row0 + (int64_t)i * max_splits) * (D + 2);
-    dst[d] = sacc;
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, red_m[w][h]);
+    float oa = 0.f, la = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float sw = red_m[w][h] == -INFINITY ? 0.f : exp2f(red_m[w][h] - M);
+      oa += sw * red_o[w][h][d];
+      la += sw * red_l[w][h];
+    }
+    float* dst = ws + (row0 + (int64_t)h * max_splits) * (D + 2);
+    dst[d] = oa;
     if (d == 0) {
-      dst[D] = st[i];
-      dst[D + 1] = st[G + i];
+      dst[D] = M;
+      dst[D + 1] = la;
     }
   }
 }
@@ -249,18 +256,8 @@ static hipError_t launch_dec(const T* q, const T* kc, const T* vc, const int32_t
                              int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int BS,
                              float sl2, const DecodePlan& pl, float* ws, int num_blocks,
                              hipStream_t st) {
-  constexpr int KLS = D + 16 / sizeof(T);
-  const size_t lds = 2 * (size_t)kDecMaxBS * KLS * sizeof(T) +
-                     sizeof(float) * ((size_t)G * kDecMaxBS + (size_t)G * D + 3 * G);
-  static bool attr_set = false;  // one attribute call per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_decode_kernel<T, D, G>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   dim3 grid(pl.max_splits, Hkv, B);
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kDecThreads), lds, st, q, kc, vc,
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kDecThreads), 0, st, q, kc, vc,
                      bt, max_blocks, ctx, Hq, Hkv, BS, sl2, pl.chunk_blocks, pl.max_splits, ws,
                      num_blocks);
   return hipGetLastError();
