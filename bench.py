@@ -22,7 +22,6 @@ are seeded synthetic data.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,17 +39,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(*names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "transformer_decoder_layer_residual_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(kernel_key: str, sha: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.json), used only if it was taken on the current kernel
+    source; else None."""
+    from transformer_decoder_layer_residual_amd import profiling
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
@@ -58,7 +51,8 @@ def load_traffic(kernel_key: str, sha: str):
         rec = json.load(open(p)).get(kernel_key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != sha:
+    srcs = profiling.KERNELS[kernel_key][1]
+    if not rec or rec.get("source_sha") != profiling.source_sha(*srcs):
         return None
     return rec.get("bytes_per_launch")
 
@@ -160,7 +154,7 @@ def main():
     gu_ms = time_launches(gateup, max(args.steps, 20), stream)
     gu_flops = 2.0 * T * (2 * I) * H
     gu_tf = gu_flops / (gu_ms * 1e-3) / 1e12
-    gu_traffic = load_traffic("gemm_gateup_silu_prefill", source_sha("gemm.hip", "dl_common.hpp"))
+    gu_traffic = load_traffic("gemm_gateup_silu_prefill")
     log(f"[bench] gate/up GEMM: {gu_ms:.3f} ms, {gu_tf:.0f} TFLOP/s "
         f"({100 * gu_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
     del s
@@ -245,8 +239,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
                          "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(a_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": load_traffic("attn_decode_paged",
-                                                 source_sha("attn_decode.hip")),
+                         "traffic": load_traffic("attn_decode_paged"),
                          "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         }
         log(f"[bench] decode: {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} tokens/s; attention "

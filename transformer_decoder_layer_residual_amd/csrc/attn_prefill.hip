@@ -218,6 +218,196 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel on v_mfma_f32_32x32x16_bf16.  4 waves x 32 queries; KV tiles of
+// 64 keys double-buffered in LDS, the next tile's loads in registers while the
+// current tile is processed (one barrier per tile).  S^T = K Q^T puts one
+// query per lane column (rows of the 32x32 block are keys 8i + 4(l/32) + j),
+// so the row statistics need one cross-lane step; P^T feeds the PV MFMA from
+// the score registers with the key order of its k-slots matched by the V^T
+// reads.  Waves skip tiles entirely above their causal diagonal.  Blocks are
+// ordered so that every q-tile of a head runs on the same XCD (K/V of a head
+// stay in that XCD's L2), heaviest q-tiles first.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                         const bf16* __restrict__ v, const int32_t* __restrict__ cu, int Hq,
+                         int Hkv, float scale_log2, bf16* __restrict__ out, int n_qtiles,
+                         int n_heads_total) {
+  constexpr int BQ = 128, BKV = 64, QW = 32;
+  constexpr int KLS = D + 8;          // padded K row (elements)
+  constexpr int VLS = BKV + 8;        // padded V^T row
+  constexpr int DK = D / 16;          // k16 steps over D
+  constexpr int DB = D / 32;          // 32-row blocks of O^T
+  constexpr int K_IT = BKV * (D / 8) / 256;           // 16-byte K loads per thread
+  constexpr int V_IT = (BKV / 2) * (D / 8) / 256;     // key-pair V loads per thread
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKV * KLS];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VLS];
+
+  // ---- block -> (q-tile, head): XCD-aware when the head count allows
+  const int L = blockIdx.x;
+  int qt, hh;
+  if ((n_heads_total & 7) == 0) {
+    const int xcd = L & 7, idx = L >> 3;
+    const int hpx = n_heads_total >> 3;                 // heads per XCD
+    qt = n_qtiles - 1 - idx / hpx;                      // heaviest first
+    hh = xcd * hpx + idx % hpx;
+  } else {
+    qt = n_qtiles - 1 - L / n_heads_total;
+    hh = L % n_heads_total;
+  }
+  const int b = hh / Hq, h = hh % Hq;
+  const int t0 = cu[b], S = cu[b + 1] - t0;
+  const int q_begin = qt * BQ;
+  if (q_begin >= S) return;
+  const int g = h / (Hq / Hkv);
+  const int kv_end = min(S, q_begin + BQ);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int qw0 = q_begin + wave * QW;
+  const int qi = qw0 + fr;                              // this lane's query
+
+  bf16x8 qf[DK];
+#pragma unroll
+  for (int ds = 0; ds < DK; ++ds) {
+    if (qi < S)
+      qf[ds] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)(t0 + qi) * Hq + h) * D + ds * 16 + 8 * fh);
+    else
+      qf[ds] = bf16x8{};
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m_i = -INFINITY, l_i = 0.f;
+
+  // ---- K/V tile loads (registers) and LDS stores
+  u32x4 kreg[K_IT], vreg[V_IT][2];
+  const u32x4 zero = {0, 0, 0, 0};
+  auto gload = [&](int kt) {
+    const int kv0 = kt * BKV;
+#pragma unroll
+    for (int i = 0; i < K_IT; ++i) {
+      const int e = tid + i * 256, key = e / (D / 8), c = e % (D / 8);
+      kreg[i] = (kv0 + key < kv_end)
+                    ? ld16(k + ((int64_t)(t0 + kv0 + key) * Hkv + g) * D + c * 8) : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < V_IT; ++i) {
+      const int e = tid + i * 256, kp = e % (BKV / 2), c = e / (BKV / 2);
+      const int key0 = kv0 + 2 * kp;
+      vreg[i][0] = (key0 < kv_end) ? ld16(v + ((int64_t)(t0 + key0) * Hkv + g) * D + c * 8) : zero;
+      vreg[i][1] = (key0 + 1 < kv_end) ? ld16(v + ((int64_t)(t0 + key0 + 1) * Hkv + g) * D + c * 8) : zero;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < K_IT; ++i) {
+      const int e = tid + i * 256, key = e / (D / 8), c = e % (D / 8);
+      st16(&Ks[buf][key * KLS + c * 8], kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < V_IT; ++i) {
+      const int e = tid + i * 256, kp = e % (BKV / 2), c = e / (BKV / 2);
+      bf16 a[8], bb[8];
+      __builtin_memcpy(a, &vreg[i][0], 16);
+      __builtin_memcpy(bb, &vreg[i][1], 16);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<bf16x2*>(&Vt[buf][(c * 8 + x) * VLS + 2 * kp]) = bf16x2{a[x], bb[x]};
+      }
+    }
+  };
+
+  gload(0);
+  sstore(0);
+  if (nkv > 1) gload(1);
+  __syncthreads();
+  for (int kt = 0; kt < nkv; ++kt) {
+    const int cur = kt & 1;
+    const int kv0 = kt * BKV;
+    if (kv0 <= qw0 + QW - 1) {           // otherwise every key of the tile is in this wave's future
+      // S^T = K Q^T: two 32-key blocks
+      f32x16 sc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < DK; ++ds) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][(kb * 32 + fr) * KLS + ds * 16 + 8 * fh]);
+          sc[kb] = mfma_32x32x16(kf, qf[ds], sc[kb]);
+        }
+      }
+      // mask + online softmax (log2 domain) for this lane's query
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+          const float val = (key <= qi && key < kv_end) ? sc[kb][e] * scale_log2 : -INFINITY;
+          sc[kb][e] = val;
+          mx = fmaxf(mx, val);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_i, mx);
+      const float alpha = exp2f(m_i - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(sc[kb][e] - m_new);
+          sc[kb][e] = p;
+          ls += p;
+        }
+      l_i = l_i * alpha + ls;
+      m_i = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 pf = {(bf16)sc[kb][8 * s2], (bf16)sc[kb][8 * s2 + 1], (bf16)sc[kb][8 * s2 + 2],
+                             (bf16)sc[kb][8 * s2 + 3], (bf16)sc[kb][8 * s2 + 4], (bf16)sc[kb][8 * s2 + 5],
+                             (bf16)sc[kb][8 * s2 + 6], (bf16)sc[kb][8 * s2 + 7]};
+          const int kbase = kb * 32 + 16 * s2 + 4 * fh;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16* row = &Vt[cur][(db * 32 + fr) * VLS + kbase];
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
+            const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[db] = mfma_32x32x16(vf, pf, o[db]);
+          }
+        }
+    }
+    if (kt + 1 < nkv) sstore(cur ^ 1);
+    __syncthreads();
+    if (kt + 2 < nkv) gload(kt + 2);
+  }
+
+  float l = l_i + __shfl_xor(l_i, 32, kWave);
+  const float inv = 1.0f / l;
+  if (qi < S) {
+    bf16* dst = out + ((int64_t)(t0 + qi) * Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store4(dst + db * 32 + 8 * i + 4 * fh, o[db][4 * i] * inv, o[db][4 * i + 1] * inv,
+               o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+  }
+}
+
 template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_seqlens, int B,
                         int max_seqlen, int Hq, int Hkv, int D, float scale, T* out,
@@ -227,6 +417,19 @@ hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_se
   if (B == 0 || max_seqlen == 0) return hipSuccess;
   const int n_qtiles = (max_seqlen + BQ - 1) / BQ;
   const float sl2 = scale * 1.4426950408889634f;
+  if constexpr (sizeof(T) == 2) {
+    const int nh = B * Hq;
+    dim3 grid(n_qtiles * nh), block(256);
+    if (D == 128)
+      hipLaunchKernelGGL((attn_prefill_bf16_kernel<128>), grid, block, 0, st, q, k, v, cu_seqlens,
+                         Hq, Hkv, sl2, out, n_qtiles, nh);
+    else if (D == 64)
+      hipLaunchKernelGGL((attn_prefill_bf16_kernel<64>), grid, block, 0, st, q, k, v, cu_seqlens,
+                         Hq, Hkv, sl2, out, n_qtiles, nh);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   dim3 grid(n_qtiles, Hq, B), block(kPfWaves * kWave);
   if (D == 128)
     hipLaunchKernelGGL((attn_prefill_kernel<T, 128, QW>), grid, block, 0, st, q, k, v, cu_seqlens,

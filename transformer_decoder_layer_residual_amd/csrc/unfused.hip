@@ -104,19 +104,50 @@ template <typename T>
 __global__ void __launch_bounds__(64)
 unf_softmax_kernel(const float* __restrict__ S, T* __restrict__ P, const int32_t* __restrict__ lens,
                    int lens_are_cu, int S_max, int Hq, int rows_per_head) {
+  // Rows of up to 64 x kHeld floats are read once and kept in registers;
+  // longer rows take an online (max, sum) pass and a write pass.
+  constexpr int kHeld = 64;
   const int b = blockIdx.z, h = blockIdx.y, i = blockIdx.x;
   const int n = min(lens_are_cu ? lens[b + 1] - lens[b] : lens[b], S_max);
   if (rows_per_head > 1 && i >= n) return;
   const int64_t row = (((int64_t)b * Hq + h) * rows_per_head + i) * S_max;
   const int lane = threadIdx.x;
-  float mx = -INFINITY;
-  for (int j = lane; j < n; j += 64) mx = fmaxf(mx, S[row + j]);
-  mx = wave_max(mx);
-  float sum = 0.f;
-  for (int j = lane; j < n; j += 64) sum += __expf(S[row + j] - mx);
-  sum = wave_sum(sum);
-  const float inv = 1.0f / sum;
-  for (int j = lane; j < n; j += 64) P[row + j] = from_f32<T>(__expf(S[row + j] - mx) * inv);
+  if (n <= 64 * kHeld) {
+    float v[kHeld];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kHeld; ++e) {
+      const int j = lane + 64 * e;
+      v[e] = j < n ? S[row + j] : -INFINITY;
+      mx = fmaxf(mx, v[e]);
+    }
+    mx = wave_max(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < kHeld; ++e) {
+      v[e] = __expf(v[e] - mx);
+      sum += v[e];
+    }
+    sum = wave_sum(sum);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int e = 0; e < kHeld; ++e) {
+      const int j = lane + 64 * e;
+      if (j < n) P[row + j] = from_f32<T>(v[e] * inv);
+    }
+    return;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int j = lane; j < n; j += 64) {
+    const float x = S[row + j];
+    const float mn = fmaxf(m, x);
+    l = l * __expf(m - mn) + __expf(x - mn);
+    m = mn;
+  }
+  const float M = wave_max(m);
+  const float L = wave_sum(m == -INFINITY ? 0.f : l * __expf(m - M));
+  const float inv = 1.0f / L;
+  for (int j = lane; j < n; j += 64) P[row + j] = from_f32<T>(__expf(S[row + j] - M) * inv);
 }
 
 template <typename T>

@@ -1,0 +1,209 @@
+"""Measurement helpers around rocprofv3 output (kernel-trace stats and PMC
+counters) and a layer-bytes driver.
+
+HBM bytes come from the TCC counters FETCH_SIZE and WRITE_SIZE (KiB per
+dispatch).  On the MI355X they are calibrated with a plain copy kernel of
+known size: a 2 GiB copy reads FETCH_SIZE = 1,048,587 KiB (half of the 2 GiB
+read) and WRITE_SIZE = 2,097,152 KiB (exact), so FETCH_SIZE is scaled by 2
+and WRITE_SIZE by 1.
+
+Commands (run from the repository root; outputs go where --out says):
+  python -m transformer_decoder_layer_residual_amd.profiling stats \
+      --csv DIR/x_kernel_stats.csv --out profiles/NAME.md --cmd "COMMAND"
+  python -m transformer_decoder_layer_residual_amd.profiling traffic \
+      --fetch DIR_F --write DIR_W --out profiles/traffic.json
+  python -m transformer_decoder_layer_residual_amd.profiling layer-bytes \
+      --mode fused|unfused --calls 3            (run under rocprofv3 --pmc)
+  python -m transformer_decoder_layer_residual_amd.profiling bytes-summary \
+      --fused-fetch D --fused-write D --unfused-fetch D --unfused-write D \
+      --calls 3 --out profiles/NAME.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+FETCH_SCALE = 2.0
+WRITE_SCALE = 1.0
+
+# dominant kernels reported by bench.py: key -> (kernel-name regex, sources)
+KERNELS = {
+    "gemm_gateup_silu_prefill": (r"gemm_pp_kernel.*MapSwiglu", ("gemm.hip", "dl_common.hpp")),
+    "attn_decode_paged": (r"attn_decode_kernel", ("attn_decode.hip",)),
+}
+
+
+def source_sha(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(PKG, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        out.extend(csv.DictReader(open(f)))
+    return out
+
+
+def _per_kernel(d: str, counter: str):
+    """kernel name -> list of per-dispatch counter values (KiB)."""
+    res = {}
+    for r in _rows(d):
+        if r["Counter_Name"] != counter:
+            continue
+        res.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return res
+
+
+def traffic(fetch_dir: str, write_dir: str) -> dict:
+    f = _per_kernel(fetch_dir, "FETCH_SIZE")
+    w = _per_kernel(write_dir, "WRITE_SIZE")
+    out = {"fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE}
+    for key, (rx, srcs) in KERNELS.items():
+        names = [n for n in f if re.search(rx, n)]
+        if not names:
+            continue
+        fv = [v for n in names for v in f[n]]
+        wv = [v for n in names for v in w.get(n, [])]
+        fetch = sum(fv) / len(fv) * 1024 * FETCH_SCALE
+        write = (sum(wv) / len(wv) * 1024 * WRITE_SCALE) if wv else 0.0
+        out[key] = {"kernel": names[0][:160], "dispatches": len(fv),
+                    "fetch_bytes": round(fetch), "write_bytes": round(write),
+                    "bytes_per_launch": round(fetch + write),
+                    "source_sha": source_sha(*srcs)}
+    return out
+
+
+def layer_bytes(fetch_dir: str, write_dir: str, calls: int) -> dict:
+    """HBM bytes of the dl kernels of one layer call (the driver's setup
+    kernels and the RoPE table fill are excluded)."""
+    def total(d, counter, scale):
+        s = 0.0
+        per = {}
+        for r in _rows(d):
+            if r["Counter_Name"] != counter:
+                continue
+            n = r["Kernel_Name"]
+            if "dl" not in n or "rope_table" in n:
+                continue
+            v = float(r["Counter_Value"]) * 1024 * scale
+            s += v
+            short = re.sub(r"^_ZN2dl\d+", "", n)[:60]
+            per[short] = per.get(short, 0.0) + v
+        return s / calls, {k: v / calls for k, v in per.items()}
+    fb, fper = total(fetch_dir, "FETCH_SIZE", FETCH_SCALE)
+    wb, wper = total(write_dir, "WRITE_SIZE", WRITE_SCALE)
+    return {"fetch": fb, "write": wb, "total": fb + wb, "fetch_per_kernel": fper,
+            "write_per_kernel": wper}
+
+
+def stats_md(csv_path: str, out: str, cmd: str, title: str):
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = [f"# {title}", "", "Command (repository root on the MI355X box):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp", cmd, "```", "",
+             "| kernel | calls | avg us | % of GPU time |", "|---|---:|---:|---:|"]
+    for r in rows:
+        n = re.sub(r"^_ZN2dl\d+", "", r["Name"])[:110]
+        lines.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def run_layer(mode: str, calls: int):
+    """One 7B-shaped prefill layer (B1 x 2048), `calls` times, for counters."""
+    import torch
+
+    from . import binding as dl
+    from . import inputs as gen
+    from .harness import DeviceLayer, cache_dev, i32, to_dev
+    cfg = gen.CONFIGS[2]
+    pb = gen.prefill_batch(cfg)
+    layer = DeviceLayer.build(cfg, max_pos=pb.T, w_host=gen.weights(cfg))
+    x = to_dev(gen.hidden(cfg, pb.T), torch.float32)
+    bt = gen.block_table(cfg, pb.lens)
+    kb, vb = gen.empty_cache(cfg, bt.num_blocks)
+    kc, vc, btd = cache_dev(kb), cache_dev(vb), i32(bt.table)
+    m = dl.DL_FUSED if mode == "fused" else dl.DL_UNFUSED
+    n = dl.dl_layer_workspace_size(layer.dims, pb.T, pb.B, pb.max_seqlen, 0, m)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    pos, seq, cu = i32(pb.positions), i32(pb.seq_of_token), i32(pb.cu_seqlens)
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        dl.dl_layer_prefill(layer.dims, layer.w, layer.cs, x, y, pos, seq, cu, pb.max_seqlen, kc,
+                            vc, btd, mode=m, ws=ws)
+    torch.cuda.synchronize()
+    print(f"ran {calls} {mode} prefill layers", file=sys.stderr)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("--csv", required=True)
+    a.add_argument("--out", required=True)
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--title", default="Kernel trace")
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--out", required=True)
+    c = sub.add_parser("layer-bytes")
+    c.add_argument("--mode", choices=["fused", "unfused"], required=True)
+    c.add_argument("--calls", type=int, default=3)
+    d = sub.add_parser("bytes-summary")
+    for k in ("fused-fetch", "fused-write", "unfused-fetch", "unfused-write"):
+        d.add_argument("--" + k, required=True)
+    d.add_argument("--calls", type=int, default=3)
+    d.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    if args.cmd == "stats":
+        stats_md(args.csv, args.out, args.cmd, args.title)
+    elif args.cmd == "traffic":
+        t = traffic(args.fetch, args.write)
+        with open(args.out, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+    elif args.cmd == "layer-bytes":
+        run_layer(args.mode, args.calls)
+    else:
+        fu = layer_bytes(args.fused_fetch, args.fused_write, args.calls)
+        un = layer_bytes(args.unfused_fetch, args.unfused_write, args.calls)
+        lines = ["# HBM bytes per Llama-2-7B-shaped prefill layer (B1 x 2048), fused vs unfused", "",
+                 "FETCH_SIZE x 2 + WRITE_SIZE x 1 (copy-kernel calibration), summed over the "
+                 "layer's kernels, per layer call.", "",
+                 "| path | read GB | write GB | total GB |", "|---|---:|---:|---:|",
+                 f"| fused | {fu['fetch'] / 1e9:.3f} | {fu['write'] / 1e9:.3f} | {fu['total'] / 1e9:.3f} |",
+                 f"| unfused (kernel per op) | {un['fetch'] / 1e9:.3f} | {un['write'] / 1e9:.3f} | "
+                 f"{un['total'] / 1e9:.3f} |", "",
+                 f"fused / unfused = {fu['total'] / un['total']:.3f}", "", "## per kernel (GB, fused)", ""]
+        for k in sorted(fu["fetch_per_kernel"], key=lambda k: -fu["fetch_per_kernel"][k]):
+            lines.append(f"- `{k}`: read {fu['fetch_per_kernel'][k] / 1e9:.3f}, write "
+                         f"{fu['write_per_kernel'].get(k, 0) / 1e9:.3f}")
+        lines += ["", "## per kernel (GB, unfused)", ""]
+        for k in sorted(un["fetch_per_kernel"], key=lambda k: -un["fetch_per_kernel"][k]):
+            lines.append(f"- `{k}`: read {un['fetch_per_kernel'][k] / 1e9:.3f}, write "
+                         f"{un['write_per_kernel'].get(k, 0) / 1e9:.3f}")
+        with open(args.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines[:10]))
+
+
+if __name__ == "__main__":
+    main()
