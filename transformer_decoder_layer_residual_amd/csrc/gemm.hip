@@ -459,20 +459,38 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 // instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
 // so the 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int pp_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk swizzles (16-byte chunks within an LDS row); both keep the 32-row
+// fragment reads conflict-free for 32- and 64-bank LDS models.
+template <int BK>
+__device__ __forceinline__ int pp_swz(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);   // 8 chunks per row
+  else return ((r >> 1) ^ (r >> 3)) & 3;                      // 4 chunks per row
+}
 
-template <int BM, class Map, class Epi>
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BK, class Map, class Epi>
 __global__ void __launch_bounds__(512, 1)
 gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
                int tiles_n) {
-  constexpr int BN = 256, BK = 64;
-  constexpr int ROWB = BK * 2;                      // 128 bytes per LDS row
-  constexpr int STAGE = (BM + BN) * ROWB;           // 64 KB (BM 256) or 48 KB (BM 128)
+  constexpr int BN = 256;
+  constexpr int ROWB = BK * 2;                      // bytes per LDS row
+  constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                     // rows per wave load instruction (1 KB)
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
+  constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
+  constexpr int LA = NSTAGE - 1;                    // k-tiles loaded ahead
   constexpr int MS = BM / 128, NS = 4;              // 32x32 blocks per wave
+  constexpr int KS = BK / 16;                       // k16 steps per tile
   constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
-  constexpr int LI = RPW / 8;                       // load instructions per wave per stage
+  constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
   constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  static_assert(NSTAGE >= 2 && LA <= 3, "stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
 
   int bid = blockIdx.x;
   const int total = tiles_m * tiles_n;
@@ -490,12 +508,12 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
   const int fr = lane & 31, fh = lane >> 5;
 
   // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
-  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), 8 rows per instruction.
+  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), RPI rows per instruction.
   const unsigned char* src[LI];
 #pragma unroll
   for (int i = 0; i < LI; ++i) {
-    const int row = wave * RPW + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ pp_swz(row);         // logical chunk this lane fetches
+    const int row = wave * RPW + i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ pp_swz<BK>(row);   // logical chunk this lane fetches
     const bf16* base;
     if (row < BM) {
       base = X + (int64_t)min(tm * BM + row, M - 1) * K;   // rows >= M: valid, never stored
@@ -506,32 +524,39 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
     src[i] = reinterpret_cast<const unsigned char*>(base) + c * 16;
   }
   auto issue_loads = [&](int kt) {
-    unsigned char* dst = smem + (kt & 1) * STAGE + wave * RPW * ROWB;
+    unsigned char* dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
     const int64_t koff = (int64_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LI; ++i)
       __builtin_amdgcn_global_load_lds(
           (const void*)(src[i] + koff),
-          (__attribute__((address_space(3))) void*)(dst + i * 8 * ROWB), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(dst + i * RPI * ROWB), 16, 0, 0);
+  };
+  // wait until k-tile `need` has landed; tiles issued after it may stay in flight
+  auto wait_tile = [&](int need, int nkt) {
+    const int newer = min(LA - 1, nkt - 1 - need);
+    if (newer >= 2) wait_vmcnt<2 * LI>();
+    else if (newer == 1) wait_vmcnt<LI>();
+    else wait_vmcnt<0>();
   };
 
-  // ---- fragments (all 4 k16 steps of a k-tile)
-  bf16x8 fx[4][MS], fw[4][NS];
+  // ---- fragments (all k16 steps of a k-tile)
+  bf16x8 fx[KS][MS], fw[KS][NS];
   auto read_frags = [&](int kt) {
-    const unsigned char* st = smem + (kt & 1) * STAGE;
+    const unsigned char* st = smem + (kt % NSTAGE) * STAGE;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int c = ks * 2 + fh;                    // logical 16 B chunk
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
         const int r = grp * GR + wm * WR + i * 32 + fr;
-        fx[ks][i] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz(r)) << 4));
+        fx[ks][i] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int blk = (s < 2) ? 2 * wn + s : 4 + 2 * wn + (s - 2);  // first half, partners
         const int r = BM + blk * 32 + fr;
-        fw[ks][s] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz(r)) << 4));
+        fw[ks][s] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
       }
     }
   };
@@ -544,7 +569,7 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
       for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
   auto compute = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -556,32 +581,33 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
     __builtin_amdgcn_sched_barrier(0);                     \
   } while (0)
-#define DL_WAIT_LOADS() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
 
+  // Phases: group 0 does MEM(t) in phase 2t+1 and COMP(t) in 2t+2; group 1 is
+  // one phase later.  Tile t+LA goes into tile t-1's stage in phase 2t+1 (group
+  // 0 from its MEM(t), group 1 from its COMP(t-1)); tile t+1 must have landed
+  // by the end of phase 2t+2.
   const int nkt = K / BK;
-  issue_loads(0);
-  if (nkt > 1) issue_loads(1);
-  DL_WAIT_LOADS();
+  for (int i = 0; i <= LA && i < nkt; ++i) issue_loads(i);
+  wait_tile(0, nkt);
   DL_PHASE_END();                                   // phase 1 begins
   if (grp == 1) DL_PHASE_END();                     // group 1 starts one phase later
   for (int kt = 0; kt < nkt; ++kt) {
     // MEM(kt)
     read_frags(kt);
     if (grp == 0) {
-      if (kt >= 1 && kt + 1 < nkt) issue_loads(kt + 1);
+      if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
     } else {
-      DL_WAIT_LOADS();                              // tile kt+1 (issued in COMP(kt-1))
+      if (kt + 1 < nkt) wait_tile(kt + 1, nkt);
     }
     DL_PHASE_END();
     // COMP(kt)
-    if (grp == 1 && kt + 2 < nkt) issue_loads(kt + 2);
+    if (grp == 1 && kt + 1 + LA < nkt) issue_loads(kt + 1 + LA);
     compute();
-    if (grp == 0) DL_WAIT_LOADS();                  // tile kt+1 (issued in MEM(kt))
+    if (grp == 0 && kt + 1 < nkt) wait_tile(kt + 1, nkt);
     DL_PHASE_END();
   }
   if (grp == 0) DL_PHASE_END();                     // balance group 1's extra barrier
 #undef DL_PHASE_END
-#undef DL_WAIT_LOADS
 
   // epilogue: lane owns column m and rows n = 8 q + 4 (lane / 32) + j of each block
 #pragma unroll
@@ -699,21 +725,30 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
 
 template <class Map, class Epi>
 static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
-                             hipStream_t st, int bm = 256) {
+                             hipStream_t st, int bm = 256, int bk = 64) {
   const int tiles_n = (NL + 255) / 256;
   if (K % 64 == 0 && bm == 128) {
     const int tiles_m = (M + 127) / 128;
-    hipLaunchKernelGGL((gemm_pp_kernel<128, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
-                       x, M, K, map, epi, tiles_m, tiles_n);
+    if (bk == 32)
+      hipLaunchKernelGGL((gemm_pp_kernel<128, 32, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
+                         st, x, M, K, map, epi, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_pp_kernel<128, 64, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
+                         st, x, M, K, map, epi, tiles_m, tiles_n);
     return hipGetLastError();
   }
   const int tiles_m = (M + 255) / 256;
-  if (K % 64 == 0)
-    hipLaunchKernelGGL((gemm_pp_kernel<256, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st,
-                       x, M, K, map, epi, tiles_m, tiles_n);
-  else
+  if (K % 64 == 0) {
+    if (bk == 32)
+      hipLaunchKernelGGL((gemm_pp_kernel<256, 32, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
+                         st, x, M, K, map, epi, tiles_m, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_pp_kernel<256, 64, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
+                         st, x, M, K, map, epi, tiles_m, tiles_n);
+  } else {
     hipLaunchKernelGGL((gemm_big_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st, x,
                        M, K, map, epi, tiles_m, tiles_n);
+  }
   return hipGetLastError();
 }
 
