@@ -1,0 +1,235 @@
+"""Parity at the full sizes of the five workload configurations, in the launch
+configuration the benchmark times (one fused layer call per prefill or decode
+step, workspace from dl_layer_workspace_size):
+
+  * 7B prefill, B1 x 2048;
+  * 7B decode, B64, contexts U{128..4096}, synthetic prior K/V;
+  * 8B-GQA prefill of 8 ragged sequences U{256..1024}, then 128 decode steps
+    on the cache that prefill wrote;
+  * 70B decode, B4 x 4096 and B1 x 32768.
+
+The oracle cannot run these layers whole in seconds, so each step is checked
+on sampled rows (every row where B is small): a sampled row is recomputed by
+the oracle step from the GPU's own stored (bf16) inputs to that step, in the
+oracle's bf16-storage mode.  Properties that hold at any size are checked in
+full: the fused layer call equals the chain of exported step calls bit for
+bit, the KV cache after the write equals the oracle's reshape-and-cache of
+the GPU's k/v bit for bit (untouched slots keep their earlier bits), and
+decode attention is compared for every (sequence, head).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from transformer_decoder_layer_residual_amd import binding as dl
+from transformer_decoder_layer_residual_amd import inputs as gen
+from transformer_decoder_layer_residual_amd.harness import DeviceLayer, cache_dev, i32, to_dev
+
+from _util import assert_bf16_close, assert_f32_close, host, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[full-size]", *a, flush=True)
+
+
+def sample_rows(T, n, seed, must=()):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.asarray(must, np.int64), r.integers(0, T, n)]))
+
+
+def fused_ws(layer, T, B, max_seqlen, max_ctx):
+    n = dl.dl_layer_workspace_size(layer.dims, T, B, max_seqlen, max_ctx, dl.DL_FUSED)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device="cuda:0")
+
+
+def cache_bits_f32(bits):
+    return np.ascontiguousarray(gen.cache_to_f32(bits))
+
+
+def check_cache_write(got_dev, before_bits, k_gpu, v_gpu, seq, pos, table, which):
+    """got_dev: the (K, V) device caches after the write; before_bits: their
+    host bits before it.  The oracle writes the GPU's k/v into f32 copies."""
+    ok = cache_bits_f32(before_bits[0])
+    ov = cache_bits_f32(before_bits[1])
+    oracle.reshape_and_cache(k_gpu, v_gpu, seq, pos, table, ok, ov)
+    for got, want_f32 in ((got_dev[0], ok), (got_dev[1], ov)):
+        want = gen.bf16_bits(want_f32)   # untouched NaN sentinels keep their payload bits
+        g = host_bits(got)
+        bad = g != want
+        assert not bad.any(), f"{which}: {int(bad.sum())} cache elements differ from the oracle"
+    return ok, ov
+
+
+def check_tail(layer, s, x_host, rows, what):
+    """O projection, residual + RMSNorm, gate/up + SiLU*mul and down + residual
+    on the sampled rows, each from the GPU's own inputs to that step."""
+    w, c = layer.w_host, layer.cfg
+    T = x_host.shape[0]
+    attn = host(s["attn"]).reshape(T, -1)[rows]
+    o = host(s["o"])[rows]
+    assert_bf16_close(o, oracle.linear(attn, w["wo"], round_bf16=True), f"{what} o")
+    n2_ref, h_ref = oracle.rmsnorm(o, w["ln2"], c.rms_eps, resid=x_host[rows], mode=oracle.BF16)
+    assert_f32_close(host(s["h"])[rows], h_ref, f"{what} h", max_abs=1e-5, rel=1e-6)
+    n2 = host(s["n2"])[rows]
+    assert_bf16_close(n2, n2_ref, f"{what} n2")
+    a = host(s["a"])[rows]
+    assert_bf16_close(a, oracle.swiglu(n2, w["wg"], w["wu"], mode=oracle.BF16), f"{what} a")
+    y_ref = oracle.down_residual(a, w["wd"], host(s["h"])[rows])
+    assert_f32_close(host(s["y"])[rows], y_ref, f"{what} y")
+
+
+def check_head(layer, s, x_host, pos, rows, what):
+    """Input RMSNorm and the QKV + RoPE projection on the sampled rows."""
+    w, c = layer.w_host, layer.cfg
+    n1 = host(s["n1"])[rows]
+    assert_bf16_close(n1, oracle.rmsnorm(x_host[rows], w["ln1"], c.rms_eps, mode=oracle.BF16),
+                      f"{what} n1")
+    rq, rk, rv = oracle.qkv_rope(n1, w["wq"], w["wk"], w["wv"], pos[rows], c.rope_theta,
+                                 c.n_q_heads, c.n_kv_heads, c.head_dim, mode=oracle.BF16)
+    assert_bf16_close(host(s["q"])[rows], rq, f"{what} q")
+    assert_bf16_close(host(s["k"])[rows], rk, f"{what} k")
+    assert_bf16_close(host(s["v"])[rows], rv, f"{what} v")
+
+
+def check_prefill_attention(s, pb, rows, what):
+    """Causal attention of the sampled query rows over their own sequence's
+    keys 0..p, as single-query attention over a contiguous copy of those
+    keys (the same softmax over the same visible set)."""
+    q, k, v = host(s["q"]), host(s["k"]), host(s["v"])
+    Hkv, D = k.shape[1], k.shape[2]
+    ctx = (pb.positions[rows] + 1).astype(np.int32)
+    S = int(ctx.max())
+    kc = np.zeros((rows.size, Hkv, S, D), np.float32)
+    vc = np.zeros_like(kc)
+    for i, t in enumerate(rows):
+        start = int(pb.cu_seqlens[pb.seq_of_token[t]])
+        n = int(ctx[i])
+        kc[i, :, :n] = k[start:start + n].transpose(1, 0, 2)
+        vc[i, :, :n] = v[start:start + n].transpose(1, 0, 2)
+    ref = oracle.attn_decode_contig(q[rows], kc, vc, ctx, mode=oracle.BF16)
+    assert_bf16_close(host(s["attn"])[rows], ref, f"{what} attn")
+
+
+# ---------------------------------------------------------------------------
+# prefill: 7B B1 x 2048 and 8B-GQA ragged B8 (then its 128 decode steps)
+# ---------------------------------------------------------------------------
+
+def run_full_prefill(cfg, decode_capacity=0):
+    pb = gen.prefill_batch(cfg)
+    say(f"{cfg.name}: T={pb.T} B={pb.B} lens {pb.lens.min()}..{pb.lens.max()}")
+    layer = DeviceLayer.build(cfg, max_pos=int(pb.lens.max()) + decode_capacity + 1)
+    x = gen.hidden(cfg, pb.T)
+    bt = gen.block_table(cfg, pb.lens + decode_capacity)
+    kb, vb = gen.empty_cache(cfg, bt.num_blocks)
+    kc1, vc1, kc2, vc2 = cache_dev(kb), cache_dev(vb), cache_dev(kb), cache_dev(vb)
+    btd = i32(bt.table)
+    xd = to_dev(x, torch.float32)
+    ws = fused_ws(layer, pb.T, pb.B, pb.max_seqlen, 0)
+    y = layer.prefill(xd, pb, kc1, vc1, btd, ws=ws)
+    s = layer.steps_prefill(xd, pb, kc2, vc2, btd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, s["y"]), "fused prefill differs from the step-by-step chain"
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    starts = pb.cu_seqlens[:-1]
+    rows = sample_rows(pb.T, 10, cfg.config_id, must=[0, pb.T - 1, *starts[:2], *(starts[1:3] - 1)])
+    say(f"{cfg.name}: sampled rows {rows.tolist()}")
+    check_head(layer, s, x, pb.positions, rows, cfg.name)
+    check_cache_write((kc1, vc1), (kb, vb), host(s["k"]), host(s["v"]), pb.seq_of_token,
+                      pb.positions, bt.table, f"{cfg.name} cache")
+    check_prefill_attention(s, pb, rows, cfg.name)
+    check_tail(layer, s, x, rows, cfg.name)
+    return layer, pb, bt, (kc1, vc1), btd, xd, y
+
+
+def test_llama2_7b_prefill_full_size():
+    cfg = gen.CONFIGS[2]
+    layer, pb, bt, caches, btd, xd, y = run_full_prefill(cfg)
+    # the unfused kernel-per-op chain at the same size stays within tolerance
+    kb, vb = gen.empty_cache(cfg, bt.num_blocks)
+    yu = layer.prefill(xd, pb, cache_dev(kb), cache_dev(vb), btd, mode=dl.DL_UNFUSED)
+    torch.cuda.synchronize()
+    assert_f32_close(host(yu), host(y), "fused vs unfused (7B prefill)")
+
+
+def decode_step_checked(layer, x_host, ctx, caches, bt, btd, what, rows=None):
+    """One fused decode step on `caches` (updated in place) and the same step
+    through the exported calls on a copy; both compared, then sampled rows
+    and every attention output against the oracle."""
+    c = layer.cfg
+    B = x_host.shape[0]
+    kb, vb = host_bits(caches[0]), host_bits(caches[1])
+    kc2, vc2 = caches[0].clone(), caches[1].clone()
+    xd = to_dev(x_host, torch.float32)
+    ws = fused_ws(layer, B, B, 0, int(ctx.max()))
+    y = layer.decode(xd, ctx, caches[0], caches[1], btd, ws=ws)
+    s = layer.steps_decode(xd, ctx, kc2, vc2, btd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, s["y"]), f"{what}: fused decode differs from the step-by-step chain"
+    assert torch.equal(caches[0].view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(caches[1].view(torch.int16), vc2.view(torch.int16))
+    del kc2, vc2
+    pos = (ctx - 1).astype(np.int32)
+    rows = np.arange(B) if rows is None else rows
+    check_head(layer, s, x_host, pos, rows, what)
+    ok, ov = check_cache_write(caches, (kb, vb), host(s["k"]), host(s["v"]),
+                               np.arange(B, dtype=np.int32), pos, bt.table, f"{what} cache")
+    del kb, vb
+    ref = oracle.attn_decode_paged(host(s["q"]), ok, ov, bt.table, ctx, mode=oracle.BF16)
+    del ok, ov
+    assert_bf16_close(host(s["attn"]), ref, f"{what} attn")
+    check_tail(layer, s, x_host, rows, what)
+    return y
+
+
+def test_llama3_8b_gqa_prefill_then_128_decode_steps():
+    cfg = gen.CONFIGS[4]
+    layer, pb, bt, caches, btd, _, _ = run_full_prefill(cfg, decode_capacity=cfg.decode_steps)
+    checked = {0, cfg.decode_steps // 2, cfg.decode_steps - 1}
+    for step in range(cfg.decode_steps):
+        ctx = (pb.lens + step + 1).astype(np.int32)
+        x = gen.hidden(cfg, pb.B, step=1 + step)
+        if step in checked:
+            say(f"{cfg.name}: decode step {step}, ctx {ctx.min()}..{ctx.max()}")
+            decode_step_checked(layer, x, ctx, caches, bt, btd, f"{cfg.name} decode {step}")
+        else:
+            layer.decode(to_dev(x, torch.float32), ctx, caches[0], caches[1], btd)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# decode without a prefill of its own: 7B B64, 70B B4 x 4096 and B1 x 32768
+# ---------------------------------------------------------------------------
+
+def run_full_decode(layer, ctx, case, rows=None):
+    cfg = layer.cfg
+    bt = gen.block_table(cfg, ctx)
+    kb, vb = gen.synthetic_cache(cfg, bt, ctx, case=case)
+    caches = (cache_dev(kb), cache_dev(vb))
+    del kb, vb
+    x = gen.hidden(cfg, ctx.size, step=1 + case)
+    say(f"{cfg.name}: B={ctx.size} ctx {ctx.min()}..{ctx.max()} ({bt.num_blocks} blocks)")
+    decode_step_checked(layer, x, ctx, caches, bt, i32(bt.table), f"{cfg.name} case {case}",
+                        rows=rows)
+
+
+def test_llama2_7b_decode_full_size():
+    cfg = gen.CONFIGS[3]
+    ctx = gen.decode_context_lens(cfg)
+    layer = DeviceLayer.build(cfg, max_pos=int(ctx.max()) + 1)
+    run_full_decode(layer, ctx, 0, rows=sample_rows(ctx.size, 12, 3, must=[0, ctx.size - 1]))
+
+
+@pytest.fixture(scope="module")
+def layer_70b():
+    cfg = gen.CONFIGS[5]
+    say(f"{cfg.name}: building weights")
+    return DeviceLayer.build(cfg, max_pos=max(c for _, c in cfg.extra["cases"]) + 1)
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_llama_70b_decode_full_size(layer_70b, case):
+    run_full_decode(layer_70b, gen.decode_context_lens(layer_70b.cfg, case), case)

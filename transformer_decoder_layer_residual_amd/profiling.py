@@ -112,6 +112,32 @@ def layer_bytes(fetch_dir: str, write_dir: str, calls: int) -> dict:
             "write_per_kernel": wper}
 
 
+def traffic_md(t: dict, out: str):
+    lines = ["# HBM traffic of the benchmark's dominant kernels (rocprofv3 PMC)", "",
+             "Per-launch bytes = mean over dispatches of FETCH_SIZE x 2 + WRITE_SIZE x 1 (KiB x "
+             "1024; scales from a plain 2 GiB copy kernel, which reads FETCH_SIZE = 1,048,587 KiB "
+             "and WRITE_SIZE = 2,097,152 KiB).  `source_sha` hashes the kernel's source files; "
+             "bench.py reports the figure only while it matches the current source.", "",
+             "Commands (repository root on the MI355X box):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp",
+             "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_f -o bench -- python -u "
+             "bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_w -o bench -- python -u "
+             "bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "python -m transformer_decoder_layer_residual_amd.profiling traffic --fetch "
+             "gpurun_out/pmc_f --write gpurun_out/pmc_w --out profiles/traffic.json", "```", "",
+             "| key | kernel | dispatches | fetch MB | write MB | bytes/launch MB | source_sha |",
+             "|---|---|---:|---:|---:|---:|---|"]
+    for k, r in t.items():
+        if not isinstance(r, dict):
+            continue
+        lines.append(f"| {k} | `{r['kernel'][:70]}` | {r['dispatches']} | "
+                     f"{r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} | "
+                     f"{r['bytes_per_launch'] / 1e6:.1f} | {r['source_sha']} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def stats_md(csv_path: str, out: str, cmd: str, title: str):
     rows = list(csv.DictReader(open(csv_path)))
     lines = [f"# {title}", "", "Command (repository root on the MI355X box):", "", "```",
@@ -154,7 +180,7 @@ def run_layer(mode: str, calls: int):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub = ap.add_subparsers(dest="sub", required=True)
     a = sub.add_parser("stats")
     a.add_argument("--csv", required=True)
     a.add_argument("--out", required=True)
@@ -173,14 +199,15 @@ def main(argv=None):
     d.add_argument("--calls", type=int, default=3)
     d.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    if args.cmd == "stats":
+    if args.sub == "stats":
         stats_md(args.csv, args.out, args.cmd, args.title)
-    elif args.cmd == "traffic":
+    elif args.sub == "traffic":
         t = traffic(args.fetch, args.write)
         with open(args.out, "w") as f:
             json.dump(t, f, indent=1)
+        traffic_md(t, os.path.splitext(args.out)[0] + ".md")
         print(json.dumps(t, indent=1))
-    elif args.cmd == "layer-bytes":
+    elif args.sub == "layer-bytes":
         run_layer(args.mode, args.calls)
     else:
         fu = layer_bytes(args.fused_fetch, args.fused_write, args.calls)
@@ -188,6 +215,15 @@ def main(argv=None):
         lines = ["# HBM bytes per Llama-2-7B-shaped prefill layer (B1 x 2048), fused vs unfused", "",
                  "FETCH_SIZE x 2 + WRITE_SIZE x 1 (copy-kernel calibration), summed over the "
                  "layer's kernels, per layer call.", "",
+                 "Commands (repository root on the MI355X box; one counter per run, MODE = fused "
+                 "or unfused, COUNTER = FETCH_SIZE or WRITE_SIZE):", "", "```",
+                 "cd /tmp && export TMPDIR=/tmp && export PYTHONPATH=$REPO",
+                 "rocprofv3 --pmc COUNTER -f csv -d gpurun_out/lb_MODE_COUNTER -o lb -- python -u -m "
+                 "transformer_decoder_layer_residual_amd.profiling layer-bytes --mode MODE --calls 3",
+                 "python -m transformer_decoder_layer_residual_amd.profiling bytes-summary "
+                 "--fused-fetch gpurun_out/lb_fused_FETCH_SIZE --fused-write gpurun_out/lb_fused_WRITE_SIZE "
+                 "--unfused-fetch gpurun_out/lb_unfused_FETCH_SIZE --unfused-write "
+                 "gpurun_out/lb_unfused_WRITE_SIZE --calls 3 --out profiles/NAME.md", "```", "",
                  "| path | read GB | write GB | total GB |", "|---|---:|---:|---:|",
                  f"| fused | {fu['fetch'] / 1e9:.3f} | {fu['write'] / 1e9:.3f} | {fu['total'] / 1e9:.3f} |",
                  f"| unfused (kernel per op) | {un['fetch'] / 1e9:.3f} | {un['write'] / 1e9:.3f} | "
