@@ -77,6 +77,8 @@ GEMM_SHAPES = [
     (1, 256, 64), (5, 512, 200), (16, 1024, 256), (33, 768, 520), (64, 4096, 512),
     (200, 1024, 4096), (600, 2048, 256), (2048, 16384, 320), (100, 96, 688),
     (700, 22000, 200),   # 256x256 prefill tile: M tail, ragged N, K tail
+    (40, 1008, 264),     # decode weight-streaming kernel: ragged last tile, K tail
+    (64, 4096, 11008),   # decode down-projection shape: 16 K slices
 ]
 
 
@@ -162,7 +164,7 @@ def test_rope_position_zero_and_table():
 # FFN
 # ---------------------------------------------------------------------------
 
-FFN_CASES = [(1, 256, 688), (29, 512, 1376), (64, 1024, 2048), (520, 512, 1024)]
+FFN_CASES = [(1, 256, 688), (29, 512, 1376), (64, 1024, 2048), (520, 512, 1024), (8, 512, 1408)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

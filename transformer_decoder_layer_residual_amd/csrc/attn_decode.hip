@@ -13,12 +13,16 @@
 //   * one workgroup per (sequence, kv head, split); a split is a fixed range
 //     of LOGICAL blocks, so the arithmetic does not depend on which physical
 //     blocks hold the data (a permuted block_table gives bit-identical
-//     results);
+//     results); the splits of all sequences are numbered densely, so with
+//     ragged contexts no idle workgroups sit between working ones (measured:
+//     idle ones in between cost about a fifth of the bandwidth);
 //   * the whole query group (Hq/Hkv heads sharing the kv head) is handled by
 //     the workgroup, so each K/V byte serves all of them;
 //   * each KV block is read straight into registers with 16-byte loads (a
-//     block of one head is one contiguous BS x D run), and the next block's
-//     loads are in flight while the current one is processed;
+//     block of one head is one contiguous BS x D run); for query groups of
+//     up to two heads two blocks are in flight, and the physical ids of the
+//     split's blocks are fetched once, up front, so no load waits on a
+//     block-table read;
 //   * scores: each thread holds a 16-byte slice of a token row; partial dots
 //     of all group heads are reduced over the token's lanes with shuffles;
 //   * online softmax in the log2 domain, kept per wave over the tokens the
@@ -31,6 +35,7 @@ namespace dl {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecMaxBS = 128;
+constexpr int kDecMaxSplitBlocks = 8;  // KV blocks per split, at most
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int BS) {
   DecodePlan pl{};
@@ -39,7 +44,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int B
   // aim for >= 2048 workgroups at the longest context, at most 8 blocks each
   int want = (2048 + items - 1) / items;
   int cb = (nblk + want - 1) / want;
-  if (cb > 8) cb = 8;
+  if (cb > kDecMaxSplitBlocks) cb = kDecMaxSplitBlocks;
   if (cb < 2 && nblk >= 16) cb = 2;
   if (cb < 1) cb = 1;
   pl.chunk_blocks = cb;
@@ -52,8 +57,8 @@ template <typename T, int D, int G>
 __global__ void __launch_bounds__(kDecThreads)
 attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                    const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ ctx,
-                   int Hq, int Hkv, int BS, float scale_log2, int chunk_blocks, int max_splits,
-                   float* __restrict__ ws, int num_blocks) {
+                   int B, int Hq, int Hkv, int BS, float scale_log2, int chunk_blocks,
+                   int max_splits, float* __restrict__ ws, int num_blocks) {
   // Register-resident streaming: thread t owns 16-byte chunk c = t % LPT of
   // tokens tok = t / LPT + TPI * i (i = 0 .. NI-1) of every KV block, for K
   // and V alike.  Scores are reduced over the LPT lanes of a token with lane
@@ -65,19 +70,45 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   constexpr int TPI = NT / LPT;               // tokens per load step (whole workgroup)
   constexpr int NI = (kDecMaxBS + TPI - 1) / TPI;
   constexpr int NWV = NT / kWave;
-  constexpr bool PREFETCH = G <= 2;           // register budget: double-buffer small groups
   __shared__ float red_m[NWV][G], red_l[NWV][G];
   __shared__ __attribute__((aligned(16))) float red_o[NWV][G][D];
 
-  const int b = blockIdx.z, g = blockIdx.y, split = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // lengths beyond the table or the host-declared maximum are clamped, so a
   // violated precondition cannot index outside block_table or the workspace
-  const int nblk = min(min((ctx[b] + BS - 1) / BS, max_blocks), max_splits * chunk_blocks);
+  auto blocks_of = [&](int len) {
+    return min(min((len + BS - 1) / BS, max_blocks), max_splits * chunk_blocks);
+  };
+  // Workgroup -> (kv head, work item); work items are the sequences' splits
+  // numbered in order, found by a wave prefix sum over the split counts.
+  // The grid is sized for the longest context, so the unused workgroups all
+  // sit at its end instead of leaving holes between working ones.
+  const int g = blockIdx.x % Hkv, item = blockIdx.x / Hkv;
+  int b = -1, split = 0;
+  for (int b0 = 0, base = 0; b0 < B; b0 += kWave) {
+    const int nb_l = b0 + lane < B ? blocks_of(ctx[b0 + lane]) : 0;
+    const int ns = (nb_l + chunk_blocks - 1) / chunk_blocks;
+    int inc = ns;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += y;
+    }
+    const int total = __shfl(inc, kWave - 1, kWave);
+    if (item < base + total) {
+      const bool mine = item >= base + inc - ns && item < base + inc;
+      const int L = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      b = b0 + L;
+      split = item - base - __shfl(inc - ns, L, kWave);
+      break;
+    }
+    base += total;
+  }
+  if (b < 0) return;
+  const int nblk = blocks_of(ctx[b]);
   const int n = min(ctx[b], nblk * BS);
   const int blk_begin = split * chunk_blocks;
-  if (blk_begin >= nblk) return;
   const int blk_end = min(nblk, blk_begin + chunk_blocks);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = tid % LPT, tok0 = tid / LPT;
 
   // this thread's slice of the (pre-scaled) query of every head in the group
@@ -98,33 +129,31 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
     for (int e = 0; e < VE; ++e) o[h][e] = 0.f;
   }
 
-  u32x4 kr[NI], vr[NI];
-  auto gload = [&](int blk) {
-    int phys = bt[(int64_t)b * max_blocks + blk];
-    phys = (phys < 0 || phys >= num_blocks) ? 0 : phys;  // invalid entry: no fault
+  // physical ids of this split's blocks, one per lane (a split has at most
+  // 64 blocks); invalid entries read block 0 instead of faulting
+  const int nb = blk_end - blk_begin;
+  int my_phys = 0;
+  if (lane < nb) {
+    const int p = bt[(int64_t)b * max_blocks + blk_begin + lane];
+    my_phys = (p < 0 || p >= num_blocks) ? 0 : p;
+  }
+  // Loads are unconditional and two blocks deep: token slots past BS are
+  // clamped into the block (their scores are masked), and past the split's
+  // last block the loads repeat that block (cache hits, never used), so the
+  // compiler's in-order load counting never has to drain the queue.
+  auto gload = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], int j) {
+    const bool past = j >= nb;  // look-ahead past the split: one cached row
+    const int phys = __builtin_amdgcn_readlane(my_phys, min(j, nb - 1));
     const int64_t base = (((int64_t)phys * Hkv + g) * BS) * D + c * VE;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int tok = tok0 + i * TPI;
-      if (tok < BS) {
-        kr[i] = ld16(kc + base + (int64_t)tok * D);
-        vr[i] = ld16(vc + base + (int64_t)tok * D);
-      }
+      const int tok = past ? 0 : min(tok0 + i * TPI, BS - 1);
+      kr[i] = ld16(kc + base + (int64_t)tok * D);
+      vr[i] = ld16(vc + base + (int64_t)tok * D);
     }
   };
-
-  if (PREFETCH) gload(blk_begin);
-  for (int blk = blk_begin; blk < blk_end; ++blk) {
-    if (!PREFETCH) gload(blk);
-    u32x4 kcur[NI], vcur[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kcur[i] = kr[i];
-      vcur[i] = vr[i];
-    }
-    if (PREFETCH && blk + 1 < blk_end) gload(blk + 1);   // next block in flight during the math
+  auto process = [&](const u32x4 (&kcur)[NI], const u32x4 (&vcur)[NI], int blk) {
     const int ntok = min(BS, n - blk * BS);
-
     float sc[NI][G];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -181,6 +210,30 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
 #pragma unroll
           for (int e = 0; e < VE; ++e) o[h][e] += sc[i][h] * vv[e];
       }
+    }
+  };
+
+  if constexpr (G <= 2) {
+    // unrolled over the largest split; leaving early is a branch out, so no
+    // join point ever mixes different numbers of loads in flight
+    u32x4 ka[NI], va[NI], kb[NI], vb[NI];
+    gload(ka, va, 0);
+    gload(kb, vb, 1);
+#pragma unroll
+    for (int j = 0; j < kDecMaxSplitBlocks; j += 2) {
+      process(ka, va, blk_begin + j);
+      if (j + 1 >= nb) break;
+      gload(ka, va, j + 2);
+      process(kb, vb, blk_begin + j + 1);
+      if (j + 2 >= nb) break;
+      gload(kb, vb, j + 3);
+    }
+  } else {
+    // larger query groups keep G x D of state per thread: one block in flight
+    for (int j = 0; j < nb; ++j) {
+      u32x4 ka[NI], va[NI];
+      gload(ka, va, j);
+      process(ka, va, blk_begin + j);
     }
   }
 
@@ -256,10 +309,10 @@ static hipError_t launch_dec(const T* q, const T* kc, const T* vc, const int32_t
                              int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int BS,
                              float sl2, const DecodePlan& pl, float* ws, int num_blocks,
                              hipStream_t st) {
-  dim3 grid(pl.max_splits, Hkv, B);
+  const dim3 grid(pl.max_splits * Hkv * B);
   hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kDecThreads), 0, st, q, kc, vc,
-                     bt, max_blocks, ctx, Hq, Hkv, BS, sl2, pl.chunk_blocks, pl.max_splits, ws,
-                     num_blocks);
+                     bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl.chunk_blocks, pl.max_splits,
+                     ws, num_blocks);
   return hipGetLastError();
 }
 

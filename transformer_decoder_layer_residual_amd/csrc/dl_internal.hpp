@@ -26,7 +26,8 @@ enum GemmCfg : int {
   kCfg16 = 3,    // BM 16,  BN 128, 4 waves (1x4), wave tile 16x32
   kCfg32s = 4,   // BM 32,  BN 32,  2 waves (2x1), wave tile 16x32 (small/odd shapes)
   kCfgPP128 = 5, // BM 128, BN 256, 8 waves: ping-pong kernel (K % 64 == 0), bf16
-  kCfgCount = 6
+  kCfgSkinny = 6,// M <= 64, BN 128, 4 waves: weight-streaming decode kernel, bf16
+  kCfgCount = 7
 };
 
 struct GemmPlan {

@@ -27,6 +27,9 @@
 // over the 8 XCDs, so the id is remapped to give every XCD a contiguous run of
 // tiles, walked M-first in groups so neighbours share weight and activation
 // tiles in that XCD's L2.
+#include <algorithm>
+#include <utility>
+
 #include "dl_internal.hpp"
 
 namespace dl {
@@ -627,6 +630,154 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming GEMM for decode-sized M (at most 64 activation rows).
+//
+// Here the weights are read exactly once and dominate the bytes (the
+// activation block is at most 64 x K), so the kernel is built to keep HBM
+// busy rather than to reuse tiles:
+//   * a workgroup owns 128 weight rows (the 64 pair-columns of a tile and
+//     their partners) and one K slice of at most KCMAX values;
+//   * the activation rows of that slice are copied once into LDS by direct
+//     global->LDS loads, issued together with the first two weight stages,
+//     so the copy overlaps the weights' first HBM round trip; the
+//     slice is stored per 256-wide stage as rows of 32 16-byte chunks, chunk
+//     c of row m at c ^ (m % 16), so the 16 rows of a fragment read hit
+//     distinct banks;
+//   * each wave streams its 2 x 16 weight rows straight from HBM into
+//     registers in the 16x16x32 MFMA operand layout (lane l holds row l % 16
+//     at k = 8 * (l / 16) of each 32-wide k group); two 256-wide stages are
+//     in flight, and each k group's registers are reloaded for two stages
+//     ahead as soon as its MFMAs are issued;
+//   * MFMA 16x16x32 bf16 with the weight block as first operand: lane l ends
+//     with four consecutive output columns of activation row l % 16.
+// Splits over K write fp32 partials that splitk_reduce sums in fixed order.
+// ---------------------------------------------------------------------------
+constexpr int kSkBN = 128, kSkP = 64, kSkNT = 256, kSkKS = 256;
+constexpr int kSkMaxStages = 4;  // K slice of at most 1024
+
+// MB: activation rows held (16, 32 or 64); NST: 256-wide stages per K slice.
+// Every workgroup runs all NST stages; where its slice is shorter (the last
+// slice), the extra stages multiply zero activations.
+template <int MB, int NST, class Map, class Epi>
+__global__ void __launch_bounds__(kSkNT, 1)
+gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi,
+                   float* __restrict__ partial, int NP) {
+  constexpr int NI = MB / 16, G = kSkKS / 32, STAGE_B = MB * kSkKS * 2;
+  constexpr int kc = NST * kSkKS;
+  __shared__ __attribute__((aligned(1024))) unsigned char xs[NST * STAGE_B];
+
+  const int tn = blockIdx.x, split = blockIdx.y;
+  const int k0 = split * kc;
+  const int klen = min(K - k0, kc);  // > 0, multiple of 8
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int kl = 8 * (lane >> 4);    // this lane's k offset inside a 32-wide group
+
+  // ---- activation slice -> LDS (direct loads; 1 KB = 2 rows of one stage per
+  // wave instruction).  Rows past M read row M-1 (never stored); k past the
+  // slice reads valid memory and is overwritten with zeros below.
+  {
+    constexpr int n_ins = MB * NST / 2;  // multiple of 4
+    const int sub = lane >> 5, pc = lane & 31;
+#pragma unroll
+    for (int ins = wave; ins < n_ins; ins += kSkNT / 64) {
+      const int st = ins / (MB / 2), m = 2 * (ins % (MB / 2)) + sub;
+      const int c = pc ^ (m & 15);
+      const int k = min(st * kSkKS + c * 8, klen - 8);
+      const bf16* src = X + (int64_t)min(m, M - 1) * K + k0 + k;
+      unsigned char* dst = xs + st * STAGE_B + (ins % (MB / 2)) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  }
+
+  // ---- weight rows of this lane: block 0 = pair-column row, block 1 = partner
+  const int r = wave * 16 + (lane & 15);
+  const bf16* wr0 = map.row(tn, r);
+  const bf16* wr1 = map.row(tn, r + kSkP);
+  if (!wr0) wr0 = X;  // rows past a ragged N: valid memory, results never stored
+  if (!wr1) wr1 = X;
+
+  // Weight loads are unconditional and unmasked: past the slice they re-read
+  // the slice's last 16 bytes of the row (already cached), which meet zero
+  // activations in LDS; missing rows read the activation block and are never
+  // stored.  With no select on loaded data and no data-dependent branches,
+  // the compiler's in-order load counting keeps two stages in flight.
+  u32x4 wa[2][G], wb[2][G];
+  auto load_group = [&](u32x4 (&w)[2][G], int g, int ks) {
+    const int e = k0 + min(ks + 32 * g + kl, klen - 8);
+    w[0][g] = ld16(wr0 + e);
+    w[1][g] = ld16(wr1 + e);
+  };
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_group(wa, g, 0);
+  if constexpr (NST > 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) load_group(wb, g, kSkKS);
+  }
+  // The activation copy and the first two weight stages were issued together,
+  // so waiting for all of them costs about one HBM round trip.  Then every
+  // chunk past the slice is zeroed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  {
+    const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = t; i < MB * NST * 32; i += kSkNT) {
+      const int st = i / (MB * 32), m = (i >> 5) % MB, c = i & 31;
+      if (st * kSkKS + 8 * c >= klen)
+        st16(xs + st * STAGE_B + m * 512 + ((c ^ (m & 15)) << 4), zero);
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[2][NI];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = lane & 15;  // chunk swizzle of this lane's fragment rows
+  auto step = [&](u32x4 (&w)[2][G], auto stc) {
+    constexpr int st = decltype(stc)::value;
+    const unsigned char* xst = xs + st * STAGE_B + (lane & 15) * 512;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int off = ((4 * g + (lane >> 4)) ^ sw) * 16;
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, w[0][g]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, w[1][g]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xst + i * 16 * 512 + off);
+        acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xf, acc[0][i], 0, 0, 0);
+        acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xf, acc[1][i], 0, 0, 0);
+      }
+      if constexpr (st + 2 < NST) load_group(w, g, (st + 2) * kSkKS);
+      // keep the reload here: the scheduler would otherwise sink it to its
+      // use two stages later and serialise the stream
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  static_assert(NST >= 1 && NST <= kSkMaxStages, "stage count");
+  step(wa, std::integral_constant<int, 0>{});
+  if constexpr (NST > 1) step(wb, std::integral_constant<int, 1>{});
+  if constexpr (NST > 2) step(wa, std::integral_constant<int, 2>{});
+  if constexpr (NST > 3) step(wb, std::integral_constant<int, 3>{});
+
+  // lane holds C[n = 4 * (lane / 16) + e][m = 16 * i + lane % 16] of each block
+  const int j = wave * 16 + 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int m = 16 * i + (lane & 15);
+    if (m >= M) continue;
+    if (partial) {
+      float* p = partial + ((int64_t)split * M + m) * NP + (int64_t)tn * kSkBN + j;
+      store4(p, acc[0][i][0], acc[0][i][1], acc[0][i][2], acc[0][i][3]);
+      store4(p + kSkP, acc[1][i][0], acc[1][i][1], acc[1][i][2], acc[1][i][3]);
+    } else {
+      epi(m, tn, j, acc[0][i], acc[1][i]);
+    }
+  }
+}
+
 // Deterministic split-K reduction (fixed split order) followed by the
 // epilogue.  One thread per (row, tile, group of 4 first-half columns).
 // Partials are [split][M][NP] with NP = tiles * BN (padded to whole tiles).
@@ -654,8 +805,9 @@ splitk_reduce(const float* __restrict__ partial, int splits, int M, int NP, int 
 // ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
-static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32, 128};
-static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32, 256};
+static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32, 128, 64};
+static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32, 256, kSkBN};
+
 
 GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   GemmPlan pl{};
@@ -666,6 +818,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   int cfg;
   if (is_f32) {
     cfg = kCfg32s;
+  } else if (M <= 64 && fits(kCfgSkinny)) {
+    cfg = kCfgSkinny;  // decode: weight streaming
   } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
     // ping-pong kernel; 256-row tiles when they fill the chip, else 128
     cfg = tiles(kCfg256) >= 256 ? kCfg256 : kCfgPP128;
@@ -681,6 +835,25 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   pl.BN = kCfgBN[cfg];
   const int nt = tiles(cfg);
   const int ktiles = (K + bk - 1) / bk;
+  if (cfg == kCfgSkinny) {
+    // K slice of 1024, 512 or 256: the longest one that still gives 1.5
+    // workgroups per CU, while the fp32 partial sums (written and re-read)
+    // stay within a quarter of the weight bytes; never longer than K needs.
+    const int cap = std::max(1, K / (8 * M));
+    int kc = kSkMaxStages * kSkKS;
+    while (kc > kSkKS) {
+      if (((K + kc - 1) / kc) * nt >= 384) break;
+      const int s2 = (K + kc / 2 - 1) / (kc / 2);
+      if (s2 > 1 && s2 > cap) break;
+      kc /= 2;
+    }
+    while (kc > kSkKS && kc / 2 >= K) kc /= 2;
+    pl.splits = (K + kc - 1) / kc;
+    pl.k_per_split = kc;
+    pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)tiles_n(cfg) * kSkBN *
+                                      sizeof(float) : 0;
+    return pl;
+  }
   int splits = 1;
   const bool single_pass = (cfg == kCfg256 || cfg == kCfgPP128);  // no split-K variant
   if (single_pass) {
@@ -752,6 +925,40 @@ static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const 
   return hipGetLastError();
 }
 
+template <int MB, class Map, class Epi>
+static void launch_skinny_mb(const bf16* x, int M, int K, const Map& map, const Epi& epi,
+                             int kc, dim3 grid, float* partial, int NP, hipStream_t st) {
+  if (kc == kSkKS)
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 1, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
+                       map, epi, partial, NP);
+  else if (kc == 2 * kSkKS)
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 2, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
+                       map, epi, partial, NP);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 4, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
+                       map, epi, partial, NP);
+}
+
+template <class Map, class Epi>
+static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, const Epi& epi,
+                                int NL, const GemmPlan& pl, void* ws, hipStream_t st) {
+  const int kc = pl.k_per_split;
+  if (M > 64 || (kc != kSkKS && kc != 2 * kSkKS && kc != 4 * kSkKS)) return hipErrorInvalidValue;
+  const int tiles_n = (NL + kSkBN - 1) / kSkBN;
+  const int NP = tiles_n * kSkBN;
+  float* partial = pl.splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  const dim3 grid(tiles_n, pl.splits);
+  if (M <= 16) launch_skinny_mb<16>(x, M, K, map, epi, kc, grid, partial, NP, st);
+  else if (M <= 32) launch_skinny_mb<32>(x, M, K, map, epi, kc, grid, partial, NP, st);
+  else launch_skinny_mb<64>(x, M, K, map, epi, kc, grid, partial, NP, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.splits == 1) return e;
+  const int64_t work = (int64_t)M * tiles_n * (kSkBN / 8);
+  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3((int)((work + 255) / 256)), dim3(256), 0, st,
+                     partial, pl.splits, M, NP, kSkBN, epi);
+  return hipGetLastError();
+}
+
 typedef Tile<128, 128, 2, 2> T128;
 typedef Tile<64, 128, 1, 4> T64;
 typedef Tile<16, 128, 1, 4> T16;
@@ -773,6 +980,8 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
       case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg16: return launch_cfg<T, T16>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg32s: return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
+      case kCfgSkinny:
+        return launch_skinny(x, M, K, mk_map(kSkBN, kSkP), mk_epi(kSkBN, kSkP), NL, pl, ws, st);
     }
     return hipErrorInvalidValue;
   }
