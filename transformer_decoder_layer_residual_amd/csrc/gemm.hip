@@ -28,6 +28,7 @@
 // tiles, walked M-first in groups so neighbours share weight and activation
 // tiles in that XCD's L2.
 #include <algorithm>
+#include <cmath>
 #include <utility>
 
 #include "dl_internal.hpp"
@@ -636,109 +637,123 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
 // Here the weights are read exactly once and dominate the bytes (the
 // activation block is at most 64 x K), so the kernel is built to keep HBM
 // busy rather than to reuse tiles:
-//   * a workgroup owns 128 weight rows (the 64 pair-columns of a tile and
-//     their partners) and one K slice of at most KCMAX values;
-//   * the activation rows of that slice are copied once into LDS by direct
-//     global->LDS loads, issued together with the first two weight stages,
-//     so the copy overlaps the weights' first HBM round trip; the
-//     slice is stored per 256-wide stage as rows of 32 16-byte chunks, chunk
-//     c of row m at c ^ (m % 16), so the 16 rows of a fragment read hit
-//     distinct banks;
+//   * work items are (128 weight rows, K slice) pairs: the 64 pair-columns of
+//     a tile and their partners, over NST stages of 256 k;
+//   * the grid is persistent (one workgroup per CU), each workgroup walks a
+//     contiguous run of items as one unbroken stream of stages: the loads for
+//     the next item start while the current one finishes, so no workgroup
+//     start or drain idles the memory pipe;
 //   * each wave streams its 2 x 16 weight rows straight from HBM into
 //     registers in the 16x16x32 MFMA operand layout (lane l holds row l % 16
-//     at k = 8 * (l / 16) of each 32-wide k group); two 256-wide stages are
-//     in flight, and each k group's registers are reloaded for two stages
-//     ahead as soon as its MFMAs are issued;
+//     at k = 8 * (l / 16) of each 32-wide k group); two stages are in flight,
+//     and each k group's registers are reloaded for two stages ahead as soon
+//     as its MFMAs are issued;
+//   * the activation rows of a stage are loaded into registers one stage
+//     ahead and written to a double-buffered LDS tile (2 x MB x 256 bf16, at
+//     most 64 KB); chunk c of row m sits at c ^ (m % 16), so a fragment's 16
+//     rows hit distinct banks; one barrier per stage;
+//   * one workgroup per CU (all 512 registers per lane), so that the weight
+//     stream, not occupancy, hides the memory latency;
+//   * every load is issued unconditionally (clamped into valid memory; the
+//     activation chunks past a slice are written as zeros, which cancels the
+//     clamped weights), so the compiler's in-order load counting stays exact;
 //   * MFMA 16x16x32 bf16 with the weight block as first operand: lane l ends
 //     with four consecutive output columns of activation row l % 16.
 // Splits over K write fp32 partials that splitk_reduce sums in fixed order.
 // ---------------------------------------------------------------------------
 constexpr int kSkBN = 128, kSkP = 64, kSkNT = 256, kSkKS = 256;
-constexpr int kSkMaxStages = 4;  // K slice of at most 1024
+constexpr int kSkGrid = 256;  // persistent workgroups: one per CU of the MI355X
 
-// MB: activation rows held (16, 32 or 64); NST: 256-wide stages per K slice.
-// Every workgroup runs all NST stages; where its slice is shorter (the last
-// slice), the extra stages multiply zero activations.
 template <int MB, int NST, class Map, class Epi>
 __global__ void __launch_bounds__(kSkNT, 1)
-gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi,
-                   float* __restrict__ partial, int NP) {
+gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_n,
+                   int n_items, float* __restrict__ partial, int NP) {
+  static_assert(NST % 2 == 0 && NST >= 2, "stage pairs");
   constexpr int NI = MB / 16, G = kSkKS / 32, STAGE_B = MB * kSkKS * 2;
+  constexpr int XI = MB / 8;  // activation vectors (16 B) per thread per stage
   constexpr int kc = NST * kSkKS;
-  __shared__ __attribute__((aligned(1024))) unsigned char xs[NST * STAGE_B];
+  __shared__ __attribute__((aligned(1024))) unsigned char xs[2][STAGE_B];
 
-  const int tn = blockIdx.x, split = blockIdx.y;
-  const int k0 = split * kc;
-  const int klen = min(K - k0, kc);  // > 0, multiple of 8
+  // contiguous run of items for this workgroup; item = split * tiles_n + tile
+  const int i0 = (int)(((int64_t)blockIdx.x * n_items) / gridDim.x);
+  const int i1 = (int)(((int64_t)(blockIdx.x + 1) * n_items) / gridDim.x);
+  if (i0 >= i1) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int kl = 8 * (lane >> 4);    // this lane's k offset inside a 32-wide group
-
-  // ---- activation slice -> LDS (direct loads; 1 KB = 2 rows of one stage per
-  // wave instruction).  Rows past M read row M-1 (never stored); k past the
-  // slice reads valid memory and is overwritten with zeros below.
-  {
-    constexpr int n_ins = MB * NST / 2;  // multiple of 4
-    const int sub = lane >> 5, pc = lane & 31;
-#pragma unroll
-    for (int ins = wave; ins < n_ins; ins += kSkNT / 64) {
-      const int st = ins / (MB / 2), m = 2 * (ins % (MB / 2)) + sub;
-      const int c = pc ^ (m & 15);
-      const int k = min(st * kSkKS + c * 8, klen - 8);
-      const bf16* src = X + (int64_t)min(m, M - 1) * K + k0 + k;
-      unsigned char* dst = xs + st * STAGE_B + (ins % (MB / 2)) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-  }
-
-  // ---- weight rows of this lane: block 0 = pair-column row, block 1 = partner
+  const int kl = 8 * (lane >> 4);  // this lane's k offset inside a 32-wide group
   const int r = wave * 16 + (lane & 15);
-  const bf16* wr0 = map.row(tn, r);
-  const bf16* wr1 = map.row(tn, r + kSkP);
-  if (!wr0) wr0 = X;  // rows past a ragged N: valid memory, results never stored
-  if (!wr1) wr1 = X;
 
-  // Weight loads are unconditional and unmasked: past the slice they re-read
-  // the slice's last 16 bytes of the row (already cached), which meet zero
-  // activations in LDS; missing rows read the activation block and are never
-  // stored.  With no select on loaded data and no data-dependent branches,
-  // the compiler's in-order load counting keeps two stages in flight.
-  u32x4 wa[2][G], wb[2][G];
-  auto load_group = [&](u32x4 (&w)[2][G], int g, int ks) {
-    const int e = k0 + min(ks + 32 * g + kl, klen - 8);
-    w[0][g] = ld16(wr0 + e);
-    w[1][g] = ld16(wr1 + e);
+  struct Item {
+    const bf16 *w0, *w1;  // this lane's weight rows (block 0 and partner)
+    int tn, split, k0, klen;
   };
+  auto make = [&](int it) {
+    Item x;
+    x.tn = it % tiles_n;
+    x.split = it / tiles_n;
+    x.k0 = x.split * kc;
+    x.klen = min(K - x.k0, kc);
+    x.w0 = map.row(x.tn, r);
+    x.w1 = map.row(x.tn, r + kSkP);
+    if (!x.w0) x.w0 = X;  // rows past a ragged N: valid memory, results never stored
+    if (!x.w1) x.w1 = X;
+    return x;
+  };
+
+  // ---- activations of stage st of item x: thread t loads 16-byte vectors
+  // v = t + 256 u (row v / 32, chunk v % 32: a row's 512 B by 32 consecutive
+  // threads) at the start of the stage before and writes them at its end, so
+  // waiting for them leaves that stage's weight reloads in flight; chunk c of
+  // row m goes to LDS position c ^ (m % 16).  Rows past M read row M-1 (never
+  // stored); k past the slice is written as zero.
+  u32x4 xr[XI];
+  auto load_x = [&](const Item& x, int st) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) load_group(wa, g, 0);
-  if constexpr (NST > 1) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) load_group(wb, g, kSkKS);
-  }
-  // The activation copy and the first two weight stages were issued together,
-  // so waiting for all of them costs about one HBM round trip.  Then every
-  // chunk past the slice is zeroed.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  {
+    for (int u = 0; u < XI; ++u) {
+      const int v = t + kSkNT * u, m = v >> 5, c = v & 31;
+      const int k = min(st * kSkKS + 8 * c, x.klen - 8);
+      xr[u] = ld16(X + (int64_t)min(m, M - 1) * K + x.k0 + k);
+    }
+  };
+  auto store_x = [&](const Item& x, int st, int buf) {
     const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
-    for (int i = t; i < MB * NST * 32; i += kSkNT) {
-      const int st = i / (MB * 32), m = (i >> 5) % MB, c = i & 31;
-      if (st * kSkKS + 8 * c >= klen)
-        st16(xs + st * STAGE_B + m * 512 + ((c ^ (m & 15)) << 4), zero);
+    for (int u = 0; u < XI; ++u) {
+      const int v = t + kSkNT * u, m = v >> 5, c = v & 31;
+      st16(&xs[buf][m * 512 + ((c ^ (m & 15)) << 4)],
+           st * kSkKS + 8 * c < x.klen ? xr[u] : zero);
     }
-  }
-  __syncthreads();
+  };
+  u32x4 wa[2][G], wb[2][G];
+  auto load_group = [&](u32x4 (&w)[2][G], const Item& x, int g, int st) {
+    const int e = x.k0 + min(st * kSkKS + 32 * g + kl, x.klen - 8);
+    w[0][g] = ld16(x.w0 + e);
+    w[1][g] = ld16(x.w1 + e);
+  };
 
   f32x4 acc[2][NI];
+  auto zero_acc = [&] {
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NI; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
   const int sw = lane & 15;  // chunk swizzle of this lane's fragment rows
-  auto step = [&](u32x4 (&w)[2][G], auto stc) {
+
+  // One stage st of item cur: next activations' first half load, barrier
+  // (this stage's activations visible; the other buffer free), MFMAs with
+  // the weight reloads for two stages ahead (which may fall in item nxt),
+  // the next activations into the other buffer.  Past the last item, loads
+  // repeat the current item's last stage (cached) and feed nothing.
+  auto stage = [&](u32x4 (&w)[2][G], auto stc, const Item& cur, const Item& nxt, bool last) {
     constexpr int st = decltype(stc)::value;
-    const unsigned char* xst = xs + st * STAGE_B + (lane & 15) * 512;
+    const Item& xa = st + 1 < NST ? cur : (last ? cur : nxt);
+    const int sx = st + 1 < NST ? st + 1 : (last ? NST - 1 : 0);
+    const Item& wi = st + 2 < NST ? cur : (last ? cur : nxt);
+    const int swt = st + 2 < NST ? st + 2 : (last ? NST - 1 : st + 2 - NST);
+    load_x(xa, sx);
+    // bare barrier: __syncthreads() would also drain the weight loads in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const unsigned char* xst = &xs[st & 1][(lane & 15) * 512];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int off = ((4 * g + (lane >> 4)) ^ sw) * 16;
@@ -750,32 +765,58 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi,
         acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xf, acc[0][i], 0, 0, 0);
         acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xf, acc[1][i], 0, 0, 0);
       }
-      if constexpr (st + 2 < NST) load_group(w, g, (st + 2) * kSkKS);
+      load_group(w, wi, g, swt);
       // keep the reload here: the scheduler would otherwise sink it to its
       // use two stages later and serialise the stream
       __builtin_amdgcn_sched_barrier(0);
     }
+    store_x(xa, sx, (st + 1) & 1);
   };
-  static_assert(NST >= 1 && NST <= kSkMaxStages, "stage count");
-  step(wa, std::integral_constant<int, 0>{});
-  if constexpr (NST > 1) step(wb, std::integral_constant<int, 1>{});
-  if constexpr (NST > 2) step(wa, std::integral_constant<int, 2>{});
-  if constexpr (NST > 3) step(wb, std::integral_constant<int, 3>{});
 
-  // lane holds C[n = 4 * (lane / 16) + e][m = 16 * i + lane % 16] of each block
-  const int j = wave * 16 + 4 * (lane >> 4);
+  Item cur = make(i0);
+  Item nxt = make(min(i0 + 1, i1 - 1));
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int m = 16 * i + (lane & 15);
-    if (m >= M) continue;
-    if (partial) {
-      float* p = partial + ((int64_t)split * M + m) * NP + (int64_t)tn * kSkBN + j;
-      store4(p, acc[0][i][0], acc[0][i][1], acc[0][i][2], acc[0][i][3]);
-      store4(p + kSkP, acc[1][i][0], acc[1][i][1], acc[1][i][2], acc[1][i][3]);
-    } else {
-      epi(m, tn, j, acc[0][i], acc[1][i]);
+  for (int g = 0; g < G; ++g) load_group(wa, cur, g, 0);
+#pragma unroll
+  for (int g = 0; g < G; ++g) load_group(wb, cur, g, 1);
+  load_x(cur, 0);
+  store_x(cur, 0, 0);
+
+  const int j = wave * 16 + 4 * (lane >> 4);
+  for (int it = i0; it < i1; ++it) {
+    const bool last = it + 1 >= i1;
+    zero_acc();
+    using std::integral_constant;
+    stage(wa, integral_constant<int, 0>{}, cur, nxt, last);
+    stage(wb, integral_constant<int, 1>{}, cur, nxt, last);
+    if constexpr (NST > 2) {
+      stage(wa, integral_constant<int, 2>{}, cur, nxt, last);
+      stage(wb, integral_constant<int, 3>{}, cur, nxt, last);
     }
+    if constexpr (NST > 4) {
+      stage(wa, integral_constant<int, 4>{}, cur, nxt, last);
+      stage(wb, integral_constant<int, 5>{}, cur, nxt, last);
+      stage(wa, integral_constant<int, 6>{}, cur, nxt, last);
+      stage(wb, integral_constant<int, 7>{}, cur, nxt, last);
+    }
+    static_assert(NST == 2 || NST == 4 || NST == 8, "stage sequence above");
+    // lane holds C[n = 4 * (lane / 16) + e][m = 16 * i + lane % 16] of each block
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int m = 16 * i + (lane & 15);
+      if (m >= M) continue;
+      if (partial) {
+        float* p = partial + ((int64_t)cur.split * M + m) * NP + (int64_t)cur.tn * kSkBN + j;
+        store4(p, acc[0][i][0], acc[0][i][1], acc[0][i][2], acc[0][i][3]);
+        store4(p + kSkP, acc[1][i][0], acc[1][i][1], acc[1][i][2], acc[1][i][3]);
+      } else {
+        epi(m, cur.tn, j, acc[0][i], acc[1][i]);
+      }
+    }
+    cur = nxt;
+    nxt = make(min(it + 2, i1 - 1));
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // look-ahead loads past the last item
 }
 
 // Deterministic split-K reduction (fixed split order) followed by the
@@ -836,20 +877,28 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   const int nt = tiles(cfg);
   const int ktiles = (K + bk - 1) / bk;
   if (cfg == kCfgSkinny) {
-    // K slice of 1024, 512 or 256: the longest one that still gives 1.5
-    // workgroups per CU, while the fp32 partial sums (written and re-read)
-    // stay within a quarter of the weight bytes; never longer than K needs.
-    const int cap = std::max(1, K / (8 * M));
-    int kc = kSkMaxStages * kSkKS;
-    while (kc > kSkKS) {
-      if (((K + kc - 1) / kc) * nt >= 384) break;
-      const int s2 = (K + kc / 2 - 1) / (kc / 2);
-      if (s2 > 1 && s2 > cap) break;
-      kc /= 2;
+    // K slice of 2048, 1024 or 512 (whole stage pairs) with the least modelled
+    // time: the persistent workgroups take items in rounds; a round streams one
+    // item per busy workgroup at min(40 GB/s, 5.6 TB/s / busy workgroups)
+    // (measured per-workgroup and whole-chip streaming rates), plus the fp32
+    // partial sums written and re-read at 5.6 TB/s
+    int best_kc = 8 * kSkKS;
+    double best = 1e300;
+    for (int kc = 8 * kSkKS; kc >= 2 * kSkKS; kc /= 2) {
+      if (kc >= 2 * K && kc > 2 * kSkKS) continue;  // mostly empty stages
+      const int s = (K + kc - 1) / kc;
+      const int items = s * nt, full = items / kSkGrid, rest = items % kSkGrid;
+      const double item_bytes = (double)kSkBN * std::min(kc, K) * 2;
+      auto round = [&](int busy) { return item_bytes / std::min(40e9, 5.6e12 / busy); };
+      double t = full * round(kSkGrid) + (rest ? round(rest) : 0.0);
+      if (s > 1) t += 2.0 * s * M * nt * kSkBN * 4 / 5.6e12;
+      if (t < best * 0.98) {
+        best = t;
+        best_kc = kc;
+      }
     }
-    while (kc > kSkKS && kc / 2 >= K) kc /= 2;
-    pl.splits = (K + kc - 1) / kc;
-    pl.k_per_split = kc;
+    pl.splits = (K + best_kc - 1) / best_kc;
+    pl.k_per_split = best_kc;
     pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)tiles_n(cfg) * kSkBN *
                                       sizeof(float) : 0;
     return pl;
@@ -926,31 +975,32 @@ static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const 
 }
 
 template <int MB, class Map, class Epi>
-static void launch_skinny_mb(const bf16* x, int M, int K, const Map& map, const Epi& epi,
-                             int kc, dim3 grid, float* partial, int NP, hipStream_t st) {
-  if (kc == kSkKS)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 1, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, partial, NP);
-  else if (kc == 2 * kSkKS)
+static void launch_skinny_mb(const bf16* x, int M, int K, const Map& map, const Epi& epi, int kc,
+                             int tiles_n, int n_items, float* partial, int NP, hipStream_t st) {
+  const dim3 grid(std::min(n_items, kSkGrid));
+  if (kc == 2 * kSkKS)
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, 2, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, partial, NP);
-  else
+                       map, epi, tiles_n, n_items, partial, NP);
+  else if (kc == 4 * kSkKS)
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, 4, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, partial, NP);
+                       map, epi, tiles_n, n_items, partial, NP);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 8, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
+                       map, epi, tiles_n, n_items, partial, NP);
 }
 
 template <class Map, class Epi>
 static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, const Epi& epi,
                                 int NL, const GemmPlan& pl, void* ws, hipStream_t st) {
   const int kc = pl.k_per_split;
-  if (M > 64 || (kc != kSkKS && kc != 2 * kSkKS && kc != 4 * kSkKS)) return hipErrorInvalidValue;
+  if (M > 64 || (kc != 2 * kSkKS && kc != 4 * kSkKS && kc != 8 * kSkKS)) return hipErrorInvalidValue;
   const int tiles_n = (NL + kSkBN - 1) / kSkBN;
   const int NP = tiles_n * kSkBN;
+  const int n_items = tiles_n * pl.splits;
   float* partial = pl.splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  const dim3 grid(tiles_n, pl.splits);
-  if (M <= 16) launch_skinny_mb<16>(x, M, K, map, epi, kc, grid, partial, NP, st);
-  else if (M <= 32) launch_skinny_mb<32>(x, M, K, map, epi, kc, grid, partial, NP, st);
-  else launch_skinny_mb<64>(x, M, K, map, epi, kc, grid, partial, NP, st);
+  if (M <= 16) launch_skinny_mb<16>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
+  else if (M <= 32) launch_skinny_mb<32>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
+  else launch_skinny_mb<64>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t work = (int64_t)M * tiles_n * (kSkBN / 8);
