@@ -1,0 +1,182 @@
+// gemm_epi.hpp -- weight-row maps, fused epilogues and the split-K reduction
+// shared by every projection GEMM kernel.
+//
+// Every projection of the layer is C = X W^T: X [M][K] activations, W [N][K]
+// weights in [out_features][in_features] layout (the FFN weight shapes given on
+// the ascend-transformer-boost fusion page, section "fusion operator matrix").
+// Both operands are K-contiguous, so 16-byte global loads land directly in the
+// MFMA operand layout.  The weight tile is the MFMA's first operand and the
+// activation tile its second; each lane therefore ends up owning four
+// consecutive output columns of one row, which gives vector stores.
+//
+// Output columns are organised in pairs (see dl_internal.hpp): a BN-wide tile
+// holds P = BN/2 pair-columns; column j (j < P) and column j + P are owned by
+// the same lane.  That lets the epilogues need no data exchange:
+//   * QKV + RoPE: pair = (i, i + D/2) of one head -- the rotary pairs of the
+//     merged Q/K/V projection with the rotary embedding applied on its output
+//     (ops-transformer Llama2-7B page, "single-layer operator call chain");
+//   * gate/up + SiLU*mul: pair = (gate row j, up row j) -- MergedMatMul(GateUp)
+//     then SiLU and the gate x up product (same paragraph);
+//   * down + residual: y = h + acc in fp32 (residual add fused into the last
+//     dense layer, ATB fusion-strategy page, "MLP fusion");
+//   * plain: O-projection and the unfused chain (N may end in a partial
+//     tile; its missing weight rows read as zero and its stores are dropped).
+#pragma once
+
+#include "dl_internal.hpp"
+
+namespace dl {
+
+// ---------------------------------------------------------------------------
+// weight-row maps: logical column r of tile tn -> pointer to the weight row
+// ---------------------------------------------------------------------------
+template <typename T>
+struct MapPlain {
+  const T* W;
+  int K, BN, N;
+  __device__ const T* row(int tn, int r) const {
+    const int n = tn * BN + r;
+    return n < N ? W + (int64_t)n * K : nullptr;  // ragged last tile: zero rows
+  }
+};
+
+template <typename T>
+struct MapSwiglu {
+  const T *Wg, *Wu;
+  int K, P;
+  __device__ const T* row(int tn, int r) const {
+    return r < P ? Wg + ((int64_t)tn * P + r) * K : Wu + ((int64_t)tn * P + (r - P)) * K;
+  }
+};
+
+template <typename T>
+struct MapQKV {
+  const T *Wq, *Wk, *Wv;
+  int K, Hq, Hkv, D, P;
+  __device__ const T* row(int tn, int r) const {
+    const int half = D / 2;
+    const int second = r >= P;
+    const int pc = tn * P + (second ? r - P : r);
+    const int head = pc / half, c = pc - head * half;
+    const int in_head = second * half + c;
+    if (head < Hq) return Wq + ((int64_t)head * D + in_head) * K;
+    if (head < Hq + Hkv) return Wk + ((int64_t)(head - Hq) * D + in_head) * K;
+    return Wv + ((int64_t)(head - Hq - Hkv) * D + in_head) * K;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// epilogues: (row m, tile tn, first-half column j (multiple of 4), 4 values of
+// columns j..j+3 and 4 values of their partners j+P..j+P+3)
+// ---------------------------------------------------------------------------
+// Plain store; columns at or beyond N (the ragged last tile) are dropped.
+// N is a multiple of 16, so a group of 4 columns is either all in or all out.
+template <typename To>
+struct EpiPlain {
+  To* out;
+  int ldo, BN, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int n = tn * BN + j;
+    To* p = out + (int64_t)m * ldo + n;
+    if (n < ldo) store4(p, a[0], a[1], a[2], a[3]);
+    if (n + P < ldo) store4(p + P, b[0], b[1], b[2], b[3]);
+  }
+};
+
+struct EpiResid {
+  float* out;
+  const float* resid;
+  int ldo, BN, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int n = tn * BN + j;
+    const int64_t o = (int64_t)m * ldo + n;
+    if (n < ldo) {
+      const f32x4 r0 = *reinterpret_cast<const f32x4*>(resid + o);
+      store4(out + o, r0[0] + a[0], r0[1] + a[1], r0[2] + a[2], r0[3] + a[3]);
+    }
+    if (n + P < ldo) {
+      const f32x4 r1 = *reinterpret_cast<const f32x4*>(resid + o + P);
+      store4(out + o + P, r1[0] + b[0], r1[1] + b[1], r1[2] + b[2], r1[3] + b[3]);
+    }
+  }
+};
+
+template <typename To>
+struct EpiSwiglu {
+  To* out;
+  int I, P;
+  __device__ void operator()(int m, int tn, int j, f32x4 g, f32x4 u) const {
+    To* p = out + (int64_t)m * I + (int64_t)tn * P + j;
+    store4(p, silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2], silu(g[3]) * u[3]);
+  }
+};
+
+// Rotate-half RoPE on q and k heads; v passes through.  cos_sin is
+// [max_pos][D/2][2] fp32 (cos, sin) built from fp64 angles.
+template <typename To>
+struct EpiRope {
+  To *q, *k, *v;
+  const int32_t* pos;
+  const float* cs;
+  int Hq, Hkv, D, P, max_pos;
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    const int half = D / 2;
+    const int pc = tn * P + j;
+    const int head = pc / half, c = pc - head * half;
+    To* dst;
+    bool rot = true;
+    if (head < Hq) {
+      dst = q + ((int64_t)m * Hq + head) * D;
+    } else if (head < Hq + Hkv) {
+      dst = k + ((int64_t)m * Hkv + (head - Hq)) * D;
+    } else {
+      dst = v + ((int64_t)m * Hkv + (head - Hq - Hkv)) * D;
+      rot = false;
+    }
+    if (rot) {
+      const int p = min(max(pos[m], 0), max_pos - 1);  // out-of-table positions clamp
+      const float* cp = cs + ((int64_t)p * half + c) * 2;
+      f32x4 c0 = *reinterpret_cast<const f32x4*>(cp);      // cos c, sin c, cos c+1, sin c+1
+      f32x4 c1 = *reinterpret_cast<const f32x4*>(cp + 4);  // cos c+2, sin c+2, cos c+3, sin c+3
+      float co[4] = {c0[0], c0[2], c1[0], c1[2]};
+      float si[4] = {c0[1], c0[3], c1[1], c1[3]};
+      float o1[4], o2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o1[e] = a[e] * co[e] - b[e] * si[e];
+        o2[e] = b[e] * co[e] + a[e] * si[e];
+      }
+      store4(dst + c, o1[0], o1[1], o1[2], o1[3]);
+      store4(dst + half + c, o2[0], o2[1], o2[2], o2[3]);
+    } else {
+      store4(dst + c, a[0], a[1], a[2], a[3]);
+      store4(dst + half + c, b[0], b[1], b[2], b[3]);
+    }
+  }
+};
+
+// Deterministic split-K reduction (fixed split order) followed by the
+// epilogue.  One thread per (row, tile, group of 4 first-half columns).
+// Partials are [split][M][NP] with NP = tiles * BN (padded to whole tiles).
+template <class Epi>
+__global__ void __launch_bounds__(256)
+splitk_reduce(const float* __restrict__ partial, int splits, int M, int NP, int BN, Epi epi) {
+  const int P = BN / 2, gpt = P / 4, tiles = NP / BN;
+  const int NL = NP;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)M * tiles * gpt;
+  if (idx >= total) return;
+  const int g = (int)(idx % gpt);
+  const int64_t rest = idx / gpt;
+  const int tn = (int)(rest % tiles);
+  const int m = (int)(rest / tiles);
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
+  for (int s = 0; s < splits; ++s) {
+    const float* p = partial + ((int64_t)s * M + m) * NL + (int64_t)tn * BN + 4 * g;
+    a += *reinterpret_cast<const f32x4*>(p);
+    b += *reinterpret_cast<const f32x4*>(p + P);
+  }
+  epi(m, tn, 4 * g, a, b);
+}
+
+}  // namespace dl

@@ -1,0 +1,327 @@
+// gemm_prefill.hpp -- large-tile bf16 MFMA GEMMs for prefill-sized M: the
+// ping-pong kernel (K % 64 == 0) and the double-buffered 256x256 kernel.
+#pragma once
+
+#include "gemm_epi.hpp"
+
+namespace dl {
+
+// ---------------------------------------------------------------------------
+// Large prefill tile: 256 x 256 x 64, 8 waves (2 x 4), wave tile 128 x 64 made
+// of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16 (the bf16 MFMA shape that
+// sustains close to the chip's peak; 16x16x32 issues at well under half of it).
+// Loads are branch-free (rows past M or N are clamped to valid memory; their
+// results are never stored) and only the last K tile, when K is not a
+// multiple of 64, takes the zero-filling path.  MFMA fragments of the next
+// 16-wide k step are read from LDS while the current step's MFMAs run.
+// ---------------------------------------------------------------------------
+template <class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
+                int tiles_n) {
+  constexpr int BM = 256, BN = 256, BK = 64, WN = 4, NT = 512;
+  constexpr int MS = BM / (32 * 2), NS = BN / (32 * WN);  // 4 x 2 blocks of 32x32
+  constexpr int LS = BK + 8;
+  constexpr int RSTEP = NT / 8;
+  constexpr int A_IT = BM / RSTEP, W_IT = BN / RSTEP;
+  static_assert(NS == 2, "one first-half and one partner block per wave");
+  __shared__ __attribute__((aligned(16))) bf16 smem[2][(BM + BN) * LS];
+
+  int bid = blockIdx.x;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int gsz = GM * tiles_n;
+  const int first_m = (bid / gsz) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % gsz) % gm;
+  const int tn = (bid % gsz) / gm;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int chunk = t & 7, r0 = t >> 3;
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+
+  const bf16* xp[A_IT];
+  const bf16* wp[W_IT];
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int m = min(tm * BM + r0 + i * RSTEP, M - 1);  // clamped: rows >= M never stored
+    xp[i] = X + (int64_t)m * K + chunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < W_IT; ++i) {
+    const bf16* b = map.row(tn, r0 + i * RSTEP);
+    wp[i] = (b ? b : X) + chunk * 8;  // missing rows read valid memory; never stored
+  }
+  const int nkt = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
+  u32x4 ra[A_IT], rw[W_IT];
+  const u32x4 zero = {0, 0, 0, 0};
+  auto gload = [&](int k0, bool masked) {
+    if (!masked) {
+#pragma unroll
+      for (int i = 0; i < A_IT; ++i) ra[i] = ld16(xp[i] + k0);
+#pragma unroll
+      for (int i = 0; i < W_IT; ++i) rw[i] = ld16(wp[i] + k0);
+    } else {
+      const bool kin = k0 + chunk * 8 < K;
+#pragma unroll
+      for (int i = 0; i < A_IT; ++i) ra[i] = kin ? ld16(xp[i] + k0) : zero;
+#pragma unroll
+      for (int i = 0; i < W_IT; ++i) rw[i] = kin ? ld16(wp[i] + k0) : zero;
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16* As = smem[buf];
+    bf16* Ws = As + BM * LS;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) st16(As + (r0 + i * RSTEP) * LS + chunk * 8, ra[i]);
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) st16(Ws + (r0 + i * RSTEP) * LS + chunk * 8, rw[i]);
+  };
+  bf16x8 fx[2][MS], fw[2][NS];
+  auto lds_frags = [&](int buf, int ks, int set) {
+    const bf16* As = smem[buf];
+    const bf16* Ws = As + BM * LS;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int nsub = (s == 0) ? wn : BN / 64 + wn;  // 32-col blocks: first half, partner half
+      fw[set][s] = *reinterpret_cast<const bf16x8*>(Ws + (nsub * 32 + fr) * LS + ks * 16 + fk);
+    }
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+      fx[set][i] = *reinterpret_cast<const bf16x8*>(As + ((wm * MS + i) * 32 + fr) * LS + ks * 16 + fk);
+  };
+  f32x16 acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc[i][s] = mfma_32x32x16(fw[set][s], fx[set][i], acc[i][s]);
+  };
+
+  gload(0, nkt == 1 && ktail);
+  sstore(0);
+  __syncthreads();
+  lds_frags(0, 0, 0);
+  for (int it = 0; it < nkt; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nkt) gload((it + 1) * BK, (it + 2 == nkt) && ktail);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      if (ks + 1 < BK / 16) lds_frags(cur, ks + 1, (ks + 1) & 1);
+      mfmas(ks & 1);
+    }
+    if (it + 1 < nkt) sstore(cur ^ 1);
+    __syncthreads();
+    if (it + 1 < nkt) lds_frags(cur ^ 1, 0, 0);
+  }
+  // epilogue: lane owns column m = ... + (lane & 31) and rows n = 8*i + 4*(lane/32) + j
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int m = tm * BM + (wm * MS + i) * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = wn * 32 + 8 * g + 4 * (lane >> 5);
+      const f32x4 a = {acc[i][0][4 * g], acc[i][0][4 * g + 1], acc[i][0][4 * g + 2], acc[i][0][4 * g + 3]};
+      const f32x4 b = {acc[i][1][4 * g], acc[i][1][4 * g + 1], acc[i][1][4 * g + 2], acc[i][1][4 * g + 3]};
+      epi(m, tn, j, a, b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong prefill tile: BM x 256 x 64, 8 waves in two groups of 4.
+//
+// Group g computes output rows [128 g, 128 g + 128) of the tile; each wave a
+// 64 x 128 block (2 x 4 blocks of 32 x 32, v_mfma_f32_32x32x16_bf16).  The
+// groups run one barrier phase apart: while one group issues its 32 MFMAs for
+// k-tile t, the other reads all its MFMA fragments of the next k-tile from
+// LDS and issues global->LDS loads, so each SIMD (one wave of each group)
+// always has a wave feeding the matrix pipe.
+//   group 0: MEM(t) in phase 2t+1, COMP(t) in phase 2t+2
+//   group 1: MEM(t) in phase 2t+2, COMP(t) in phase 2t+3
+// K-tiles live in two LDS stages; tile t+2 is loaded into tile t's stage in
+// phase 2t+3 (after both groups read tile t) and waited for at the end of
+// phase 2t+4, before either group reads it.
+// Global->LDS loads go straight to LDS (global_load_lds_dwordx4, 1 KB per wave
+// instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
+// so the 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
+// ---------------------------------------------------------------------------
+// Chunk swizzles (16-byte chunks within an LDS row); both keep the 32-row
+// fragment reads conflict-free for 32- and 64-bank LDS models.
+template <int BK>
+__device__ __forceinline__ int pp_swz(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);   // 8 chunks per row
+  else return ((r >> 1) ^ (r >> 3)) & 3;                      // 4 chunks per row
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BK, class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
+               int tiles_n) {
+  constexpr int BN = 256;
+  constexpr int ROWB = BK * 2;                      // bytes per LDS row
+  constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                     // rows per wave load instruction (1 KB)
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
+  constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
+  constexpr int LA = NSTAGE - 1;                    // k-tiles loaded ahead
+  constexpr int MS = BM / 128, NS = 4;              // 32x32 blocks per wave
+  constexpr int KS = BK / 16;                       // k16 steps per tile
+  constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
+  constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
+  constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
+  static_assert(NSTAGE >= 2 && LA <= 3, "stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
+
+  int bid = blockIdx.x;
+  const int total = tiles_m * tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int gsz = GM * tiles_n;
+  const int first_m = (bid / gsz) * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int tm = first_m + (bid % gsz) % gm;
+  const int tn = (bid % gsz) / gm;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int grp = wave >> 2, wig = wave & 3;        // group, wave in group
+  const int wm = wig >> 1, wn = wig & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
+  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), RPI rows per instruction.
+  const unsigned char* src[LI];
+#pragma unroll
+  for (int i = 0; i < LI; ++i) {
+    const int row = wave * RPW + i * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ pp_swz<BK>(row);   // logical chunk this lane fetches
+    const bf16* base;
+    if (row < BM) {
+      base = X + (int64_t)min(tm * BM + row, M - 1) * K;   // rows >= M: valid, never stored
+    } else {
+      const bf16* b = map.row(tn, row - BM);
+      base = b ? b : X;                                     // missing rows: valid, never stored
+    }
+    src[i] = reinterpret_cast<const unsigned char*>(base) + c * 16;
+  }
+  auto issue_loads = [&](int kt) {
+    unsigned char* dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
+    const int64_t koff = (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < LI; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[i] + koff),
+          (__attribute__((address_space(3))) void*)(dst + i * RPI * ROWB), 16, 0, 0);
+  };
+  // wait until k-tile `need` has landed; tiles issued after it may stay in flight
+  auto wait_tile = [&](int need, int nkt) {
+    const int newer = min(LA - 1, nkt - 1 - need);
+    if (newer >= 2) wait_vmcnt<2 * LI>();
+    else if (newer == 1) wait_vmcnt<LI>();
+    else wait_vmcnt<0>();
+  };
+
+  // ---- fragments (all k16 steps of a k-tile)
+  bf16x8 fx[KS][MS], fw[KS][NS];
+  auto read_frags = [&](int kt) {
+    const unsigned char* st = smem + (kt % NSTAGE) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c = ks * 2 + fh;                    // logical 16 B chunk
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        const int r = grp * GR + wm * WR + i * 32 + fr;
+        fx[ks][i] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int blk = (s < 2) ? 2 * wn + s : 4 + 2 * wn + (s - 2);  // first half, partners
+        const int r = BM + blk * 32 + fr;
+        fw[ks][s] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
+      }
+    }
+  };
+  f32x16 acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
+  auto compute = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[i][s] = mfma_32x32x16(fw[ks][s], fx[ks][i], acc[i][s]);
+  };
+#define DL_PHASE_END()                                     \
+  do {                                                     \
+    __builtin_amdgcn_sched_barrier(0);                     \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    __builtin_amdgcn_sched_barrier(0);                     \
+  } while (0)
+
+  // Phases: group 0 does MEM(t) in phase 2t+1 and COMP(t) in 2t+2; group 1 is
+  // one phase later.  Tile t+LA goes into tile t-1's stage in phase 2t+1 (group
+  // 0 from its MEM(t), group 1 from its COMP(t-1)); tile t+1 must have landed
+  // by the end of phase 2t+2.
+  const int nkt = K / BK;
+  for (int i = 0; i <= LA && i < nkt; ++i) issue_loads(i);
+  wait_tile(0, nkt);
+  DL_PHASE_END();                                   // phase 1 begins
+  if (grp == 1) DL_PHASE_END();                     // group 1 starts one phase later
+  for (int kt = 0; kt < nkt; ++kt) {
+    // MEM(kt)
+    read_frags(kt);
+    if (grp == 0) {
+      if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
+    } else {
+      if (kt + 1 < nkt) wait_tile(kt + 1, nkt);
+    }
+    DL_PHASE_END();
+    // COMP(kt)
+    if (grp == 1 && kt + 1 + LA < nkt) issue_loads(kt + 1 + LA);
+    compute();
+    if (grp == 0 && kt + 1 < nkt) wait_tile(kt + 1, nkt);
+    DL_PHASE_END();
+  }
+  if (grp == 0) DL_PHASE_END();                     // balance group 1's extra barrier
+#undef DL_PHASE_END
+
+  // epilogue: lane owns column m and rows n = 8 q + 4 (lane / 32) + j of each block
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const int m = tm * BM + grp * GR + wm * WR + i * 32 + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = (2 * wn + b) * 32 + 8 * q + 4 * fh;
+        const f32x4 lo = {acc[i][b][4 * q], acc[i][b][4 * q + 1], acc[i][b][4 * q + 2], acc[i][b][4 * q + 3]};
+        const f32x4 hi = {acc[i][b + 2][4 * q], acc[i][b + 2][4 * q + 1], acc[i][b + 2][4 * q + 2],
+                          acc[i][b + 2][4 * q + 3]};
+        epi(m, tn, j, lo, hi);
+      }
+  }
+}
+
+}  // namespace dl

@@ -71,7 +71,7 @@ class DeviceLayer:
         return y
 
     # -- step by step (exported step entry points) ---------------------------
-    def steps_prefill(self, x, pb, kc, vc, bt_dev):
+    def steps_prefill(self, x, pb, kc, vc, bt_dev, gu_events=None):
         c, dt = self.cfg, torch_dtype(self.cfg)
         T, H, Hq, Hkv, D, I = pb.T, c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate
         s = {}
@@ -86,7 +86,7 @@ class DeviceLayer:
         dl.dl_reshape_and_cache(s["k"], s["v"], i32(pb.seq_of_token), pos, bt_dev, kc, vc)
         s["attn"] = torch.empty(T, Hq, D, dtype=dt, device=DEV)
         dl.dl_attn_prefill(s["q"], s["k"], s["v"], i32(pb.cu_seqlens), pb.max_seqlen, s["attn"])
-        return self._tail(x, s, T, H, I, dt)
+        return self._tail(x, s, T, H, I, dt, gu_events)
 
     def steps_decode(self, x, ctx, kc, vc, bt_dev):
         c, dt = self.cfg, torch_dtype(self.cfg)
@@ -107,7 +107,7 @@ class DeviceLayer:
         dl.dl_attn_decode_paged(s["q"], kc, vc, bt_dev, i32(ctx), int(ctx.max()), s["attn"])
         return self._tail(x, s, B, H, I, dt)
 
-    def _tail(self, x, s, T, H, I, dt):
+    def _tail(self, x, s, T, H, I, dt, gu_events=None):
         c = self.cfg
         s["o"] = torch.empty(T, H, dtype=dt, device=DEV)
         dl.dl_linear(s["attn"].view(T, -1), self.w["wo"], s["o"])
@@ -116,7 +116,14 @@ class DeviceLayer:
         dl.dl_rmsnorm_residual(s["o"], self.w["ln2"], s["n2"], c.rms_eps, residual_in=x,
                                residual_out=s["h"])
         s["a"] = torch.empty(T, I, dtype=dt, device=DEV)
-        dl.dl_gate_up_silu(s["n2"], self.w["wg"], self.w["wu"], s["a"])
+        ws = None
+        if gu_events is not None:   # time the gate/up launch alone, inside the chain
+            n = dl.lib().dl_gate_up_silu_workspace_size(T, H, I, dl.dtype_code(dt))
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+            gu_events[0].record()
+        dl.dl_gate_up_silu(s["n2"], self.w["wg"], self.w["wu"], s["a"], ws=ws)
+        if gu_events is not None:
+            gu_events[1].record()
         s["y"] = torch.empty(T, H, device=DEV)
         dl.dl_down_residual(s["a"], self.w["wd"], s["y"], residual=s["h"])
         return s

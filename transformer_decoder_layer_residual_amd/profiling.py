@@ -37,8 +37,9 @@ WRITE_SCALE = 1.0
 
 # dominant kernels reported by bench.py: key -> (kernel-name regex, sources)
 KERNELS = {
-    "gemm_gateup_silu_prefill": (r"gemm_pp_kernel.*MapSwiglu", ("gemm.hip", "dl_common.hpp")),
-    "attn_decode_paged": (r"attn_decode_kernel", ("attn_decode.hip",)),
+    "gemm_gateup_silu_prefill": (r"gemm_pp_kernel.*MapSwiglu",
+                                 ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
+    "attn_decode_paged": (r"attn_decode_kernel", ("attn_decode.hip", "dl_common.hpp")),
 }
 
 
