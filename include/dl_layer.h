@@ -143,6 +143,26 @@ dl_status dl_qkv_rope(const void* x, const void* w_q, const void* w_k, const voi
                       dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * QKV + RoPE with the reshape-and-cache write fused into the epilogue (the KV
+ * update folded into the attention block: ascend-transformer-boost fusion
+ * page, section "KVCache management"; ATB KV-cache page, "KV cache memory
+ * bottleneck").  Computes what dl_qkv_rope computes and also writes the
+ * rotated k and v of token t to the caches exactly as dl_reshape_and_cache
+ * would (same bits): sequence seq_of_token[t] (t itself when NULL), block
+ * block_table[seq][positions[t] / BS], slot positions[t] % BS.  k and v may
+ * both be NULL (then they go to the cache only) or both be given.  Table
+ * entries outside [0, num_blocks) and positions outside the table are
+ * skipped.  Workspace as dl_qkv_rope_workspace_size.
+ */
+dl_status dl_qkv_rope_cache(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                            const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                            void* q, void* k, void* v, const int32_t* seq_of_token,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const dl_kv_cache* cache, int32_t T, int32_t H, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t BS, dl_dtype dt, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * Reshape-and-cache (ATB KV-cache page, "KV cache memory bottleneck":
  * ReshapeAndCache writes step K/V into the paged blocks through block_table).
  * Token t of sequence seq_of_token[t] at position positions[t] is copied to

@@ -221,6 +221,66 @@ def test_reshape_and_cache_bit_exact(cfg_id):
     assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
 
 
+@pytest.mark.parametrize("cfg_id,decode", [(1, False), (4, False), (4, True)])
+def test_qkv_rope_cache_equals_separate_calls(cfg_id, decode):
+    """The fused projection + cache write gives the same q/k/v and the same
+    cache bits (sentinels included) as dl_qkv_rope then dl_reshape_and_cache,
+    also when a block-table entry is invalid, and with k/v going to the cache
+    only."""
+    cfg = gen.CONFIGS[cfg_id]
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    Hq, Hkv, D, BS = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    H = 512 if cfg_id == 4 else cfg.hidden
+    if decode:
+        ctx = np.array([1, BS, BS + 1, 3 * BS + 5], np.int32)
+        bt = gen.block_table(cfg, ctx)
+        pos, seq = (ctx - 1).astype(np.int32), None
+        T = ctx.size
+    else:
+        pb = gen.packed([1, BS - 1, BS, BS + 1, 3 * BS + 5])
+        bt = gen.block_table(cfg, pb.lens)
+        pos, seq, T = pb.positions, pb.seq_of_token, pb.T
+    bt.table[-1, pos[-1] // BS] = -1           # one invalid entry: skipped by both paths
+    kbits, vbits = gen.empty_cache(cfg, bt.num_blocks)
+    x = rnd(T, H, dtype=dtype)
+    wq, wk, wv = (rnd(h * D, H, scale=0.05, dtype=dtype) for h in (Hq, Hkv, Hkv))
+    cs = torch.empty(4096, D, device=DEV)
+    dl.dl_rope_table_fill(cs, 4096, D, cfg.rope_theta)
+    xd, wqd, wkd, wvd = (dev_as(a, dtype) for a in (x, wq, wk, wv))
+    posd, btd = dev_i32(pos), dev_i32(bt.table)
+    seqd = dev_i32(seq) if seq is not None else None
+    outs = []
+    for variant in ("separate", "fused", "cache-only"):
+        q = torch.empty(T, Hq, D, dtype=dtype, device=DEV)
+        k = torch.empty(T, Hkv, D, dtype=dtype, device=DEV)
+        v = torch.empty(T, Hkv, D, dtype=dtype, device=DEV)
+        kc, vc = dev_cache(kbits), dev_cache(vbits)
+        if variant == "separate":
+            dl.dl_qkv_rope(xd, wqd, wkd, wvd, posd, cs, q, k, v)
+            dl.dl_reshape_and_cache(k, v, seqd, posd, btd, kc, vc)
+        elif variant == "fused":
+            dl.dl_qkv_rope_cache(xd, wqd, wkd, wvd, posd, cs, q, k, v, seqd, btd, kc, vc)
+        else:
+            dl.dl_qkv_rope_cache(xd, wqd, wkd, wvd, posd, cs, q, None, None, seqd, btd, kc, vc,
+                                 Hkv=Hkv)
+        torch.cuda.synchronize()
+        outs.append((host_bits(q), host_bits(k), host_bits(v), host_bits(kc), host_bits(vc)))
+    ref = outs[0]
+    for name, got in zip(("fused", "cache-only"), outs[1:]):
+        assert np.array_equal(got[0], ref[0]), f"{name}: q differs"
+        assert np.array_equal(got[3], ref[3]) and np.array_equal(got[4], ref[4]), f"{name}: cache"
+    assert np.array_equal(outs[1][1], ref[1]) and np.array_equal(outs[1][2], ref[2])
+    # and the separate path's cache is the oracle's reshape of its k/v
+    okc, ovc = gen.cache_to_f32(kbits).copy(), gen.cache_to_f32(vbits).copy()
+    kf = ref[1].view(np.float32) if dtype == torch.float32 else gen.bits_to_f32(ref[1])
+    vf = ref[2].view(np.float32) if dtype == torch.float32 else gen.bits_to_f32(ref[2])
+    sq = seq if seq is not None else np.arange(T, dtype=np.int32)
+    keep = bt.table[sq, pos // BS] >= 0         # the tokens whose block entry is valid
+    oracle.reshape_and_cache(kf[keep], vf[keep], sq[keep], pos[keep], bt.table, okc, ovc)
+    want_k = gen.bf16_bits(okc) if dtype == torch.bfloat16 else okc.view(np.uint32)
+    assert np.array_equal(ref[3], want_k)
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------

@@ -61,6 +61,10 @@ _SIGS = [
     ("dl_qkv_rope_workspace_size", _sz, [_c_int] * 5 + [ctypes.c_int]),
     ("dl_qkv_rope", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, ctypes.c_int, _vp, _sz, _vp]),
+    ("dl_qkv_rope_cache", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                         _vp, _c_int, ctypes.POINTER(KVCache), _c_int, _c_int,
+                                         _c_int, _c_int, _c_int, _c_int, ctypes.c_int, _vp, _sz,
+                                         _vp]),
     ("dl_reshape_and_cache", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_int,
                                             ctypes.POINTER(KVCache), _c_int, _c_int, _c_int,
                                             _c_int, ctypes.c_int, _vp]),
@@ -186,6 +190,23 @@ def dl_qkv_rope(x, w_q, w_k, w_v, positions, cos_sin, q, k, v, ws=None):
     _check(L.dl_qkv_rope(_p(x), _p(w_q), _p(w_k), _p(w_v), _p(positions), _p(cos_sin),
                          cos_sin.shape[0], _p(q), _p(k), _p(v), T, H, Hq, Hkv, D, dt, _p(ws), nb,
                          _stream()))
+
+
+def dl_qkv_rope_cache(x, w_q, w_k, w_v, positions, cos_sin, q, k, v, seq_of_token, block_table,
+                      k_cache, v_cache, Hkv=None, ws=None):
+    """k, v: [T, Hkv, D] tensors, or both None (K/V then go to the cache only;
+    pass Hkv)."""
+    T, H = x.shape
+    _, Hq, D = q.shape
+    Hkv = k.shape[1] if k is not None else Hkv
+    dt = dtype_code(x.dtype)
+    L = lib()
+    ws, nb = _ws(L.dl_qkv_rope_workspace_size(T, H, Hq, Hkv, D, dt), ws, x.device)
+    c = _cache(k_cache, v_cache)
+    _check(L.dl_qkv_rope_cache(_p(x), _p(w_q), _p(w_k), _p(w_v), _p(positions), _p(cos_sin),
+                               cos_sin.shape[0], _p(q), _p(k), _p(v), _p(seq_of_token),
+                               _p(block_table), block_table.shape[1], ctypes.byref(c), T, H, Hq,
+                               Hkv, D, k_cache.shape[2], dt, _p(ws), nb, _stream()))
 
 
 def dl_reshape_and_cache(k, v, seq_of_token, positions, block_table, k_cache, v_cache):

@@ -249,18 +249,38 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
   T* vc = static_cast<T*>(cache->v_cache);
 
   DL_HIP((rmsnorm_residual<float, T>(x, nullptr, nullptr, g1, n1, Tn, H, d->rms_eps, st)), "norm1");
-  if (m == DL_FUSED) {
+  if (m == DL_FUSED && is_decode) {
+    // decode: the projection's epilogue writes rotated k and v straight into
+    // the paged cache (attention reads them only from there)
+    KVSink kv;
+    kv.k_cache = kc;
+    kv.v_cache = vc;
+    kv.seq_of_token = seq;
+    kv.block_table = bt;
+    kv.max_blocks = maxblk;
+    kv.block_size = BS;
+    kv.num_blocks = cache->num_blocks;
+    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, nullptr, nullptr, Tn, H, Hq,
+                            Hkv, D, plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st, kv),
+           "qkv_rope_cache");
+  } else if (m == DL_FUSED) {
+    // prefill: attention reads k/v from the projection's output, and a
+    // separate copy kernel fills the cache (writing the cache from the GEMM
+    // epilogue as well measured 2.5x more write traffic for the projection,
+    // from partial-line stores, than the 67 MB the copy kernel moves)
     DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, k, v, Tn, H, Hq, Hkv, D,
                             plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st), "qkv_rope");
+    DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
+                                cache->num_blocks, st), "reshape_and_cache");
   } else {
     DL_HIP((gemm_linear<T, T>(n1, wq, q, Tn, Hq * D, H, plan_lin(Tn, Hq * D, H, dt), part, st)), "q");
     DL_HIP((gemm_linear<T, T>(n1, wk, k, Tn, Hkv * D, H, plan_lin(Tn, Hkv * D, H, dt), part, st)), "k");
     DL_HIP((gemm_linear<T, T>(n1, wv, v, Tn, Hkv * D, H, plan_lin(Tn, Hkv * D, H, dt), part, st)), "v");
     DL_HIP(unf_rope<T>(q, pos, cs, max_pos, Tn, Hq, D, st), "rope q");
     DL_HIP(unf_rope<T>(k, pos, cs, max_pos, Tn, Hkv, D, st), "rope k");
+    DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
+                                cache->num_blocks, st), "reshape_and_cache");
   }
-  DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
-                              cache->num_blocks, st), "reshape_and_cache");
   if (!is_decode) {
     if (m == DL_FUSED) {
       DL_HIP(attn_prefill<T>(q, k, v, cu, B, S_or_ctx, Hq, Hkv, D, scale, attn, st), "attn_prefill");
@@ -400,6 +420,56 @@ dl_status dl_qkv_rope(const void* x, const void* w_q, const void* w_k, const voi
       ? gemm_qkv_rope<bf16>((const bf16*)x, (const bf16*)w_q, (const bf16*)w_k, (const bf16*)w_v, positions, cos_sin, max_pos, (bf16*)q, (bf16*)k, (bf16*)v, T, H, Hq, Hkv, D, pl, ws, st)
       : gemm_qkv_rope<float>((const float*)x, (const float*)w_q, (const float*)w_k, (const float*)w_v, positions, cos_sin, max_pos, (float*)q, (float*)k, (float*)v, T, H, Hq, Hkv, D, pl, ws, st);
   DL_HIP(e, "qkv_rope");
+  return ok();
+}
+
+dl_status dl_qkv_rope_cache(const void* x, const void* w_q, const void* w_k, const void* w_v,
+                            const int32_t* positions, const float* cos_sin, int32_t max_pos,
+                            void* q, void* k, void* v, const int32_t* seq_of_token,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const dl_kv_cache* cache, int32_t T, int32_t H, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t BS, dl_dtype dt, void* ws,
+                            size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  if (T < 0) return fail(DL_ERR_INVALID_ARG, "T must be >= 0");
+  TRY(check_heads(Hq, Hkv, D));
+  TRY(check_bs(BS));
+  if (H <= 0 || H % 8) return fail(DL_ERR_UNSUPPORTED, "H must be a positive multiple of 8");
+  if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
+  if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  TRY(check_cache(cache));
+  if (T == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w_q);
+  CHECK_PTR(w_k);
+  CHECK_PTR(w_v);
+  CHECK_IDX(positions);
+  CHECK_PTR(cos_sin);
+  CHECK_PTR(q);
+  if ((k == nullptr) != (v == nullptr)) return fail(DL_ERR_INVALID_ARG, "k and v must both be given or both be NULL");
+  if (k) {
+    CHECK_PTR(k);
+    CHECK_PTR(v);
+  }
+  if (seq_of_token) CHECK_IDX(seq_of_token);
+  CHECK_IDX(block_table);
+  const GemmPlan pl = plan_qkv(T, H, Hq, Hkv, D, dt);
+  if (pl.ws_bytes > ws_bytes || (pl.ws_bytes && !ws))
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR_OPT(ws);
+  KVSink kv;
+  kv.k_cache = cache->k_cache;
+  kv.v_cache = cache->v_cache;
+  kv.seq_of_token = seq_of_token;
+  kv.block_table = block_table;
+  kv.max_blocks = max_blocks_per_seq;
+  kv.block_size = BS;
+  kv.num_blocks = cache->num_blocks;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? gemm_qkv_rope<bf16>((const bf16*)x, (const bf16*)w_q, (const bf16*)w_k, (const bf16*)w_v, positions, cos_sin, max_pos, (bf16*)q, (bf16*)k, (bf16*)v, T, H, Hq, Hkv, D, pl, ws, st, kv)
+      : gemm_qkv_rope<float>((const float*)x, (const float*)w_q, (const float*)w_k, (const float*)w_v, positions, cos_sin, max_pos, (float*)q, (float*)k, (float*)v, T, H, Hq, Hkv, D, pl, ws, st, kv);
+  DL_HIP(e, "qkv_rope_cache");
   return ok();
 }
 

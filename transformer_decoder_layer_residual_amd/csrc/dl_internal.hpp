@@ -42,11 +42,23 @@ struct GemmPlan {
 // P = BN/2 must divide N/2; plain GEMMs accept a ragged last tile (N % 16 == 0).
 GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired);
 
-// Workspace-free variants share kernels; these return hipError_t.
+// Where the QKV epilogue also writes k and v: the paged cache through the
+// block table (k_cache == nullptr: no cache write).
+struct KVSink {
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  const int32_t* seq_of_token = nullptr;  // nullptr: token t belongs to sequence t
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, block_size = 0, num_blocks = 0;
+};
+
+// Workspace-free variants share kernels; these return hipError_t.  k and v may
+// be nullptr when a sink takes them.
 template <typename T>
 hipError_t gemm_qkv_rope(const T* x, const T* wq, const T* wk, const T* wv, const int32_t* pos,
                          const float* cos_sin, int max_pos, T* q, T* k, T* v, int M, int H,
-                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st);
+                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st,
+                         const KVSink& kv = KVSink{});
 template <typename T, typename To>
 hipError_t gemm_linear(const T* x, const T* w, To* out, int M, int N, int K, const GemmPlan& pl,
                        void* ws, hipStream_t st);

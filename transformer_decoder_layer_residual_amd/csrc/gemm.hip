@@ -31,6 +31,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
     cfg = kCfgSkinny;  // decode: weight streaming
   } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
     // ping-pong kernel; 256-row tiles when they fill the chip, else 128
+    // (a round-count model favoured 128-row tiles for 1.5 rounds of 256-row
+    // ones, but measured no faster and with more panel traffic)
     cfg = tiles(kCfg256) >= 256 ? kCfg256 : kCfgPP128;
   } else if (M >= 512) {
     cfg = (fits(kCfg256) && tiles(kCfg256) >= 256) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
@@ -208,12 +210,21 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
 template <typename T>
 hipError_t gemm_qkv_rope(const T* x, const T* wq, const T* wk, const T* wv, const int32_t* pos,
                          const float* cos_sin, int max_pos, T* q, T* k, T* v, int M, int H,
-                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st) {
+                         int Hq, int Hkv, int D, const GemmPlan& pl, void* ws, hipStream_t st,
+                         const KVSink& kv) {
   const int NL = (Hq + 2 * Hkv) * D;
+  CacheSink<T> sink;
+  sink.kc = static_cast<T*>(kv.k_cache);
+  sink.vc = static_cast<T*>(kv.v_cache);
+  sink.seq = kv.seq_of_token;
+  sink.bt = kv.block_table;
+  sink.max_blocks = kv.max_blocks;
+  sink.BS = kv.block_size;
+  sink.num_blocks = kv.num_blocks;
   return dispatch<T>(
       x, M, H, NL, pl, ws, st,
       [&](int, int P) { return MapQKV<T>{wq, wk, wv, H, Hq, Hkv, D, P}; },
-      [&](int, int P) { return EpiRope<T>{q, k, v, pos, cos_sin, Hq, Hkv, D, P, max_pos}; });
+      [&](int, int P) { return EpiRope<T>{q, k, v, pos, cos_sin, Hq, Hkv, D, P, max_pos, sink}; });
 }
 
 template <typename T, typename To>
@@ -243,7 +254,7 @@ hipError_t gemm_swiglu(const T* x, const T* wg, const T* wu, T* a, int M, int H,
 #define DL_INST(T)                                                                              \
   template hipError_t gemm_qkv_rope<T>(const T*, const T*, const T*, const T*, const int32_t*, \
                                        const float*, int, T*, T*, T*, int, int, int, int, int, \
-                                       const GemmPlan&, void*, hipStream_t);                   \
+                                       const GemmPlan&, void*, hipStream_t, const KVSink&);    \
   template hipError_t gemm_linear<T, T>(const T*, const T*, T*, int, int, int, const GemmPlan&, \
                                         void*, hipStream_t);                                    \
   template hipError_t gemm_linear_resid<T>(const T*, const T*, const float*, float*, int, int,  \

@@ -111,26 +111,54 @@ struct EpiSwiglu {
   }
 };
 
+// Optional destination of the rotated k and of v in the paged KV cache
+// ([num_blocks][Hkv][BS][D]): token m of sequence seq[m] (m itself when seq is
+// null) at position pos[m] goes to block bt[seq][pos / BS], slot pos % BS --
+// the reshape-and-cache write done in the projection's epilogue (the KV update
+// the ascend-transformer-boost fusion page, section "KVCache management", folds
+// into the attention block).  Ids outside the table or the pool are skipped.
+template <typename To>
+struct CacheSink {
+  To *kc = nullptr, *vc = nullptr;  // kc == nullptr: no cache write
+  const int32_t* seq = nullptr;
+  const int32_t* bt = nullptr;
+  int max_blocks = 0, BS = 0, num_blocks = 0;
+  __device__ To* slot(To* cache, int m, int g, int Hkv, int D, int p) const {
+    if (p < 0 || p / BS >= max_blocks) return nullptr;
+    const int s = seq ? seq[m] : m;
+    const int blk = bt[(int64_t)s * max_blocks + p / BS];
+    if (blk < 0 || blk >= num_blocks) return nullptr;
+    return cache + (((int64_t)blk * Hkv + g) * BS + p % BS) * D;
+  }
+};
+
 // Rotate-half RoPE on q and k heads; v passes through.  cos_sin is
-// [max_pos][D/2][2] fp32 (cos, sin) built from fp64 angles.
+// [max_pos][D/2][2] fp32 (cos, sin) built from fp64 angles.  k and v may be
+// null when they only go to the cache.
 template <typename To>
 struct EpiRope {
   To *q, *k, *v;
   const int32_t* pos;
   const float* cs;
   int Hq, Hkv, D, P, max_pos;
+  CacheSink<To> sink;
   __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
     const int half = D / 2;
     const int pc = tn * P + j;
     const int head = pc / half, c = pc - head * half;
     To* dst;
+    To* cdst = nullptr;
     bool rot = true;
     if (head < Hq) {
       dst = q + ((int64_t)m * Hq + head) * D;
     } else if (head < Hq + Hkv) {
-      dst = k + ((int64_t)m * Hkv + (head - Hq)) * D;
+      const int g = head - Hq;
+      dst = k ? k + ((int64_t)m * Hkv + g) * D : nullptr;
+      if (sink.kc) cdst = sink.slot(sink.kc, m, g, Hkv, D, pos[m]);
     } else {
-      dst = v + ((int64_t)m * Hkv + (head - Hq - Hkv)) * D;
+      const int g = head - Hq - Hkv;
+      dst = v ? v + ((int64_t)m * Hkv + g) * D : nullptr;
+      if (sink.kc) cdst = sink.slot(sink.vc, m, g, Hkv, D, pos[m]);
       rot = false;
     }
     if (rot) {
@@ -146,11 +174,23 @@ struct EpiRope {
         o1[e] = a[e] * co[e] - b[e] * si[e];
         o2[e] = b[e] * co[e] + a[e] * si[e];
       }
-      store4(dst + c, o1[0], o1[1], o1[2], o1[3]);
-      store4(dst + half + c, o2[0], o2[1], o2[2], o2[3]);
+      if (dst) {
+        store4(dst + c, o1[0], o1[1], o1[2], o1[3]);
+        store4(dst + half + c, o2[0], o2[1], o2[2], o2[3]);
+      }
+      if (cdst) {  // the same rounding as the buffer store: identical bits
+        store4(cdst + c, o1[0], o1[1], o1[2], o1[3]);
+        store4(cdst + half + c, o2[0], o2[1], o2[2], o2[3]);
+      }
     } else {
-      store4(dst + c, a[0], a[1], a[2], a[3]);
-      store4(dst + half + c, b[0], b[1], b[2], b[3]);
+      if (dst) {
+        store4(dst + c, a[0], a[1], a[2], a[3]);
+        store4(dst + half + c, b[0], b[1], b[2], b[3]);
+      }
+      if (cdst) {
+        store4(cdst + c, a[0], a[1], a[2], a[3]);
+        store4(cdst + half + c, b[0], b[1], b[2], b[3]);
+      }
     }
   }
 };
