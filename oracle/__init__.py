@@ -54,6 +54,7 @@ def lib():
 
 _f32p = ctypes.POINTER(ctypes.c_float)
 _i32p = ctypes.POINTER(ctypes.c_int32)
+_i8p = ctypes.POINTER(ctypes.c_int8)
 _i = ctypes.c_int
 _d = ctypes.c_double
 
@@ -95,6 +96,18 @@ def _declare(L):
     L.orc_layer_decode.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
                                    _f32p, _f32p, _f32p, _i32p, _i, _f32p, _f32p,
                                    _i32p, _i, _i]
+    L.orc_kv_quant_rows.argtypes = [_f32p, ctypes.c_int64, _i, _i8p, _f32p]
+    L.orc_reshape_and_cache_q8.argtypes = [_f32p, _f32p, _i32p, _i32p, _i32p, _i,
+                                           _i8p, _i8p, _f32p, _f32p, _i, _i, _i, _i]
+    L.orc_attn_decode_paged_q8.argtypes = [_f32p, _i8p, _i8p, _f32p, _f32p, _i32p,
+                                           _i, _i32p, _i, _i, _i, _i, _i, _d, _f32p,
+                                           _i]
+    L.orc_layer_prefill_q8.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                       _f32p, _f32p, _f32p, _i32p, _i32p, _i32p, _i,
+                                       _i, _i8p, _i8p, _f32p, _f32p, _i32p, _i, _i]
+    L.orc_layer_decode_q8.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                      _f32p, _f32p, _f32p, _i32p, _i, _i8p, _i8p,
+                                      _f32p, _f32p, _i32p, _i, _i]
     L.orc_kv_cache_bytes.argtypes = [_i, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, _i]
     L.orc_kv_cache_bytes.restype = _d
@@ -115,6 +128,8 @@ def _p(a):
         return a.ctypes.data_as(_f32p)
     if a.dtype == np.int32:
         return a.ctypes.data_as(_i32p)
+    if a.dtype == np.int8:
+        return a.ctypes.data_as(_i8p)
     raise TypeError(a.dtype)
 
 
@@ -190,6 +205,38 @@ def reshape_and_cache(k, v, seq_of_token, pos, block_table, k_cache, v_cache):
                                 T, Hkv, D, BS)
 
 
+def _cache_out(a, dtype, name):
+    assert a.dtype == dtype and a.flags.c_contiguous, name
+
+
+def kv_quant_rows(x):
+    """INT8 per-row quantisation of x [..., D] -> (codes int8 [..., D], scales [...])."""
+    x = _f(x)
+    D = x.shape[-1]
+    R = x.size // D
+    codes = np.empty(x.shape, np.int8)
+    scales = np.empty(x.shape[:-1], np.float32)
+    lib().orc_kv_quant_rows(_p(x), R, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def reshape_and_cache_q8(k, v, seq_of_token, pos, block_table, k_codes, v_codes,
+                         k_scale, v_scale):
+    """Quantising cache write, in place: codes int8 [nb, Hkv, BS, D], scales
+    float32 [nb, Hkv, BS]."""
+    k, v = _f(k), _f(v)
+    T, Hkv, D = k.shape
+    bt = _ii(block_table)
+    for a, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _cache_out(a, np.int8, n)
+    for a, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _cache_out(a, np.float32, n)
+    BS = k_codes.shape[2]
+    lib().orc_reshape_and_cache_q8(_p(k), _p(v), _p(_ii(seq_of_token)), _p(_ii(pos)),
+                                   _p(bt), bt.shape[1], _p(k_codes), _p(v_codes),
+                                   _p(k_scale), _p(v_scale), T, Hkv, D, BS)
+
+
 def attn_prefill(q, k, v, cu_seqlens, scale=None, mode=EXACT):
     q, k, v = _f(q), _f(k), _f(v)
     T, Hq, D = q.shape
@@ -215,6 +262,23 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, scale=None
     lib().orc_attn_decode_paged(_p(q), _p(kc), _p(vc), _p(bt), bt.shape[1],
                                 _p(_ii(context_lens)), B, Hq, Hkv, D, BS, scale,
                                 _p(out), mode)
+    return out
+
+
+def attn_decode_paged_q8(q, k_codes, v_codes, k_scale, v_scale, block_table,
+                         context_lens, scale=None, mode=EXACT):
+    q = _f(q)
+    B, Hq, D = q.shape
+    kq = np.ascontiguousarray(k_codes, dtype=np.int8)
+    vq = np.ascontiguousarray(v_codes, dtype=np.int8)
+    ks, vs = _f(k_scale), _f(v_scale)
+    Hkv, BS = kq.shape[1], kq.shape[2]
+    bt = _ii(block_table)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    out = np.empty_like(q)
+    lib().orc_attn_decode_paged_q8(_p(q), _p(kq), _p(vq), _p(ks), _p(vs), _p(bt),
+                                   bt.shape[1], _p(_ii(context_lens)), B, Hq, Hkv, D,
+                                   BS, scale, _p(out), mode)
     return out
 
 
@@ -307,6 +371,48 @@ def layer_decode(dims, weights, x, context_lens, k_cache, v_cache, block_table,
     lib().orc_layer_decode(ctypes.byref(d), ctypes.byref(w), _p(x), _p(y), _p(h),
                            _p(_ii(context_lens)), B, _p(k_cache), _p(v_cache), _p(bt),
                            bt.shape[1], mode)
+    del keep
+    return y, h
+
+
+def layer_prefill_q8(dims, weights, x, pos, seq_of_token, cu_seqlens, k_codes,
+                     v_codes, k_scale, v_scale, block_table, mode=EXACT):
+    """layer_prefill with an INT8 cache (updated in place).  Returns (y, h)."""
+    d, w, keep = _pack(dims, weights)
+    x = _f(x)
+    T, H = x.shape
+    y = np.empty_like(x)
+    h = np.empty_like(x)
+    cu = _ii(cu_seqlens)
+    bt = _ii(block_table)
+    for a, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _cache_out(a, np.int8, n)
+    for a, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _cache_out(a, np.float32, n)
+    lib().orc_layer_prefill_q8(ctypes.byref(d), ctypes.byref(w), _p(x), _p(y), _p(h),
+                               _p(_ii(pos)), _p(_ii(seq_of_token)), _p(cu), cu.size - 1,
+                               T, _p(k_codes), _p(v_codes), _p(k_scale), _p(v_scale),
+                               _p(bt), bt.shape[1], mode)
+    del keep
+    return y, h
+
+
+def layer_decode_q8(dims, weights, x, context_lens, k_codes, v_codes, k_scale,
+                    v_scale, block_table, mode=EXACT):
+    """layer_decode with an INT8 cache (updated in place).  Returns (y, h)."""
+    d, w, keep = _pack(dims, weights)
+    x = _f(x)
+    B, H = x.shape
+    y = np.empty_like(x)
+    h = np.empty_like(x)
+    bt = _ii(block_table)
+    for a, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _cache_out(a, np.int8, n)
+    for a, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _cache_out(a, np.float32, n)
+    lib().orc_layer_decode_q8(ctypes.byref(d), ctypes.byref(w), _p(x), _p(y), _p(h),
+                              _p(_ii(context_lens)), B, _p(k_codes), _p(v_codes),
+                              _p(k_scale), _p(v_scale), _p(bt), bt.shape[1], mode)
     del keep
     return y, h
 

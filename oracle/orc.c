@@ -51,6 +51,12 @@
  *   [mlp]    ATB fusion-strategy page (gitcode.csdn.net), section "MLP
  *            fusion": residual add fused into the last dense layer; section
  *            "configuration": LLaMA uses SiLU.
+ *   [kvquant] ATB KV-cache page (hwcomputing.csdn.net), section "KV cache
+ *            quantisation (INT8/INT4 precision-latency trade-off)": at
+ *            per-token granularity each token's K and its V carry their own
+ *            fp32 scale; online quantisation computes the scale as the token
+ *            is written; PagedAttention dequantises while it loads cache
+ *            blocks; the scales sit in HBM beside the blocks.
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   RMSNorm in the Llama form (eps inside the root, gamma after normalising);
@@ -58,7 +64,12 @@
  *   fp64 (the pages give no rotary formula); attention scale 1/sqrt(D);
  *   GQA kv head = q head div (Hq/Hkv); SwiGLU a = silu(gate) * up;
  *   decode writes the new token to the cache before attending, and
- *   context_lens counts that token.
+ *   context_lens counts that token;
+ *   INT8 KV rows: symmetric (no offset), one scale per (token, kv head) row
+ *   of K and of V, scale = max|x| / 127, code = x / scale rounded to the
+ *   nearest integer (ties to even) and clamped to [-127, 127], both in fp32
+ *   (the precision the page gives the scale); an all-zero row has scale 0
+ *   and codes 0; a dequantised element is code x scale.
  *
  * Parity pins: every function here is pinned by CPU tests against closed
  * forms, invariants, exact integer cases and brute force (tests/test_oracle_*).
@@ -228,15 +239,20 @@ void orc_reshape_and_cache(const float* k, const float* v,
  * keys[j], vals[j] point at D-vectors; n keys.  o = sum_j P_j v_j with
  * P = softmax(s), s_j = scale * q.k_j, max subtracted.  In the unfused mode
  * the scores are stored in fp32 and P in bf16 before the PV product.
- * scratch holds n doubles.
+ * kmul / vmul (NULL = all ones) multiply every element of key j / value j:
+ * an INT8 row is passed as its codes with its scale as the multiplier, so
+ * the element used is the dequantised code x scale (an exact product in
+ * fp64).  scratch holds n doubles.
  */
 static void attend(const float* q, const float* const* keys,
-                   const float* const* vals, int n, int D, double scale,
-                   float* out, int mode, double* s) {
+                   const float* const* vals, const double* kmul,
+                   const double* vmul, int n, int D, double scale, float* out,
+                   int mode, double* s) {
   double mx = -INFINITY;
   for (int j = 0; j < n; ++j) {
+    const double km = kmul ? kmul[j] : 1.0;
     double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += (double)q[d] * (double)keys[j][d];
+    for (int d = 0; d < D; ++d) acc += (double)q[d] * ((double)keys[j][d] * km);
     s[j] = acc * scale;
     if (mode == ORC_BF16_UNFUSED) s[j] = (double)(float)s[j];
     if (s[j] > mx) mx = s[j];
@@ -252,7 +268,8 @@ static void attend(const float* q, const float* const* keys,
   }
   for (int d = 0; d < D; ++d) {
     double acc = 0.0;
-    for (int j = 0; j < n; ++j) acc += s[j] * (double)vals[j][d];
+    for (int j = 0; j < n; ++j)
+      acc += s[j] * ((double)vals[j][d] * (vmul ? vmul[j] : 1.0));
     out[d] = store(acc, mode != ORC_EXACT);
   }
 }
@@ -280,7 +297,7 @@ void orc_attn_prefill(const float* q, const float* k, const float* v,
           keys[j] = k + ((int64_t)(t0 + j) * Hkv + g) * D;
           vals[j] = v + ((int64_t)(t0 + j) * Hkv + g) * D;
         }
-        attend(q + ((int64_t)(t0 + i) * Hq + h) * D, keys, vals, i + 1, D, scale,
+        attend(q + ((int64_t)(t0 + i) * Hq + h) * D, keys, vals, NULL, NULL, i + 1, D, scale,
                out + ((int64_t)(t0 + i) * Hq + h) * D, mode, sc);
         free(keys);
         free(vals);
@@ -314,7 +331,7 @@ void orc_attn_decode_paged(const float* q, const float* k_cache,
         keys[j] = k_cache + off;
         vals[j] = v_cache + off;
       }
-      attend(q + ((int64_t)b * Hq + h) * D, keys, vals, n, D, scale,
+      attend(q + ((int64_t)b * Hq + h) * D, keys, vals, NULL, NULL, n, D, scale,
              out + ((int64_t)b * Hq + h) * D, mode, sc);
       free(keys);
       free(vals);
@@ -343,7 +360,7 @@ void orc_attn_decode_contig(const float* q, const float* k_cache,
         keys[j] = k_cache + off;
         vals[j] = v_cache + off;
       }
-      attend(q + ((int64_t)b * Hq + h) * D, keys, vals, n, D, scale,
+      attend(q + ((int64_t)b * Hq + h) * D, keys, vals, NULL, NULL, n, D, scale,
              out + ((int64_t)b * Hq + h) * D, mode, sc);
       free(keys);
       free(vals);
@@ -394,6 +411,115 @@ void orc_ffn(const float* x, const float* wg, const float* wu, const float* wd,
 }
 
 /* ------------------------------------------------------------------------ */
+/* INT8 KV cache with per-token scales, quantised on write      [kvquant]   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One cached row (one token, one kv head, K or V; D values):
+ *   scale = max_d |x_d| / 127            (fp32 division)
+ *   code_d = nearest integer to x_d / scale, ties to even, in [-127, 127]
+ * An all-zero row gets scale 0 and all-zero codes.
+ */
+void orc_kv_quant_row(const float* x, int D, int8_t* code, float* scale) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float a = fabsf(x[d]);
+    if (a > amax) amax = a;
+  }
+  const float s = amax / 127.0f;
+  *scale = s;
+  for (int d = 0; d < D; ++d) {
+    if (s == 0.0f) {
+      code[d] = 0;
+      continue;
+    }
+    float r = rintf(x[d] / s); /* default rounding mode: nearest, ties to even */
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    code[d] = (int8_t)r;
+  }
+}
+
+/* R consecutive rows of D values (x [R][D] -> codes [R][D], scales [R]). */
+void orc_kv_quant_rows(const float* x, int64_t R, int D, int8_t* codes,
+                       float* scales) {
+  for (int64_t r = 0; r < R; ++r)
+    orc_kv_quant_row(x + r * D, D, codes + r * D, scales + r);
+}
+
+/*
+ * Reshape-and-cache into an INT8 cache: the placement of
+ * orc_reshape_and_cache, with each (token, kv head) row of k and of v
+ * quantised on the way in.  Codes [num_blocks][Hkv][BS][D] int8; scales
+ * [num_blocks][Hkv][BS] fp32, indexed like the rows they belong to.
+ */
+void orc_reshape_and_cache_q8(const float* k, const float* v,
+                              const int32_t* seq_of_token, const int32_t* pos,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              int8_t* k_codes, int8_t* v_codes, float* k_scale,
+                              float* v_scale, int T, int Hkv, int D, int BS) {
+  for (int t = 0; t < T; ++t) {
+    int s = seq_of_token[t], p = pos[t];
+    int blk = block_table[(int64_t)s * max_blocks_per_seq + p / BS];
+    int slot = p % BS;
+    for (int g = 0; g < Hkv; ++g) {
+      int64_t row = ((int64_t)blk * Hkv + g) * BS + slot;
+      int64_t src = ((int64_t)t * Hkv + g) * D;
+      orc_kv_quant_row(k + src, D, k_codes + row * D, k_scale + row);
+      orc_kv_quant_row(v + src, D, v_codes + row * D, v_scale + row);
+    }
+  }
+}
+
+/*
+ * Paged decode attention over an INT8 cache              [kvquant], [kvpage]
+ * The computation of orc_attn_decode_paged on the dequantised cache: key j
+ * is k_codes row x k_scale of that row, value j likewise (the dequantisation
+ * done while the blocks are loaded).
+ */
+void orc_attn_decode_paged_q8(const float* q, const int8_t* k_codes,
+                              const int8_t* v_codes, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table,
+                              int max_blocks_per_seq, const int32_t* context_lens,
+                              int B, int Hq, int Hkv, int D, int BS, double scale,
+                              float* out, int mode) {
+  const int grp = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < Hq; ++h) {
+      const int g = h / grp, n = context_lens[b];
+      float* kf = (float*)malloc(sizeof(float) * (size_t)n * D);
+      float* vf = (float*)malloc(sizeof(float) * (size_t)n * D);
+      const float** keys = (const float**)malloc(sizeof(float*) * (size_t)n);
+      const float** vals = (const float**)malloc(sizeof(float*) * (size_t)n);
+      double* km = (double*)malloc(sizeof(double) * (size_t)n);
+      double* vm = (double*)malloc(sizeof(double) * (size_t)n);
+      double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+      for (int j = 0; j < n; ++j) {
+        int blk = block_table[(int64_t)b * max_blocks_per_seq + j / BS];
+        int64_t row = ((int64_t)blk * Hkv + g) * BS + j % BS;
+        for (int d = 0; d < D; ++d) {  /* codes are integers: exact in fp32 */
+          kf[(int64_t)j * D + d] = (float)k_codes[row * D + d];
+          vf[(int64_t)j * D + d] = (float)v_codes[row * D + d];
+        }
+        keys[j] = kf + (int64_t)j * D;
+        vals[j] = vf + (int64_t)j * D;
+        km[j] = (double)k_scale[row];
+        vm[j] = (double)v_scale[row];
+      }
+      attend(q + ((int64_t)b * Hq + h) * D, keys, vals, km, vm, n, D, scale,
+             out + ((int64_t)b * Hq + h) * D, mode, sc);
+      free(kf);
+      free(vf);
+      free(keys);
+      free(vals);
+      free(km);
+      free(vm);
+      free(sc);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Whole decoder layer                            [graph], [chain], [kvupd] */
 /* ------------------------------------------------------------------------ */
 
@@ -427,16 +553,38 @@ static void layer_tail(const orc_dims* d, const orc_weights* w, const float* x,
 }
 
 /*
+ * Where a layer keeps its K/V: float caches (k, v), or an INT8 cache (codes
+ * kq, vq and row scales ks, vs).  Members of the other kind are NULL.
+ */
+typedef struct {
+  float *k, *v;
+  int8_t *kq, *vq;
+  float *ks, *vs;
+} orc_kv;
+
+static void cache_write(const orc_kv* c, const float* k, const float* v,
+                        const int32_t* seq, const int32_t* pos,
+                        const int32_t* block_table, int max_blocks_per_seq, int T,
+                        int Hkv, int D, int BS) {
+  if (c->kq)
+    orc_reshape_and_cache_q8(k, v, seq, pos, block_table, max_blocks_per_seq,
+                             c->kq, c->vq, c->ks, c->vs, T, Hkv, D, BS);
+  else if (c->k)
+    orc_reshape_and_cache(k, v, seq, pos, block_table, max_blocks_per_seq,
+                          c->k, c->v, T, Hkv, D, BS);
+}
+
+/*
  * Prefill over packed sequences.  x, y [T][H]; positions restart at 0 in
  * every sequence.  K/V of every token are written to the cache; attention
  * reads k/v straight from the projection output.
  */
-void orc_layer_prefill(const orc_dims* d, const orc_weights* w, const float* x,
-                       float* y, float* h_out, const int32_t* pos,
-                       const int32_t* seq_of_token, const int32_t* cu_seqlens,
-                       int B, int T, float* k_cache, float* v_cache,
-                       const int32_t* block_table, int max_blocks_per_seq,
-                       int mode) {
+static void layer_prefill(const orc_dims* d, const orc_weights* w, const float* x,
+                          float* y, float* h_out, const int32_t* pos,
+                          const int32_t* seq_of_token, const int32_t* cu_seqlens,
+                          int B, int T, const orc_kv* c,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          int mode) {
   const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
   float* n1 = (float*)malloc(sizeof(float) * (size_t)T * H);
   float* q = (float*)malloc(sizeof(float) * (size_t)T * Hq * D);
@@ -446,10 +594,8 @@ void orc_layer_prefill(const orc_dims* d, const orc_weights* w, const float* x,
   orc_rmsnorm(x, NULL, NULL, w->ln1, n1, T, H, d->rms_eps, mode);
   orc_qkv_rope(n1, w->wq, w->wk, w->wv, pos, d->rope_theta, q, k, v, T, H, Hq,
                Hkv, D, mode);
-  if (k_cache)
-    orc_reshape_and_cache(k, v, seq_of_token, pos, block_table,
-                          max_blocks_per_seq, k_cache, v_cache, T, Hkv, D,
-                          d->block_size);
+  cache_write(c, k, v, seq_of_token, pos, block_table, max_blocks_per_seq, T,
+              Hkv, D, d->block_size);
   orc_attn_prefill(q, k, v, cu_seqlens, B, Hq, Hkv, D, 1.0 / sqrt((double)D),
                    attn, mode);
   layer_tail(d, w, x, attn, y, h_out, T, mode);
@@ -465,10 +611,10 @@ void orc_layer_prefill(const orc_dims* d, const orc_weights* w, const float* x,
  * Its K/V are written into the cache first, then attention runs over the
  * whole cached context (which includes the new token).
  */
-void orc_layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
-                      float* y, float* h_out, const int32_t* context_lens, int B,
-                      float* k_cache, float* v_cache, const int32_t* block_table,
-                      int max_blocks_per_seq, int mode) {
+static void layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
+                         float* y, float* h_out, const int32_t* context_lens,
+                         int B, const orc_kv* c, const int32_t* block_table,
+                         int max_blocks_per_seq, int mode) {
   const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
   int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
   int32_t* seq = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
@@ -481,14 +627,20 @@ void orc_layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
   float* k = (float*)malloc(sizeof(float) * (size_t)B * Hkv * D);
   float* v = (float*)malloc(sizeof(float) * (size_t)B * Hkv * D);
   float* attn = (float*)malloc(sizeof(float) * (size_t)B * Hq * D);
+  const double scale = 1.0 / sqrt((double)D);
   orc_rmsnorm(x, NULL, NULL, w->ln1, n1, B, H, d->rms_eps, mode);
   orc_qkv_rope(n1, w->wq, w->wk, w->wv, pos, d->rope_theta, q, k, v, B, H, Hq,
                Hkv, D, mode);
-  orc_reshape_and_cache(k, v, seq, pos, block_table, max_blocks_per_seq,
-                        k_cache, v_cache, B, Hkv, D, d->block_size);
-  orc_attn_decode_paged(q, k_cache, v_cache, block_table, max_blocks_per_seq,
-                        context_lens, B, Hq, Hkv, D, d->block_size,
-                        1.0 / sqrt((double)D), attn, mode);
+  cache_write(c, k, v, seq, pos, block_table, max_blocks_per_seq, B, Hkv, D,
+              d->block_size);
+  if (c->kq)
+    orc_attn_decode_paged_q8(q, c->kq, c->vq, c->ks, c->vs, block_table,
+                             max_blocks_per_seq, context_lens, B, Hq, Hkv, D,
+                             d->block_size, scale, attn, mode);
+  else
+    orc_attn_decode_paged(q, c->k, c->v, block_table, max_blocks_per_seq,
+                          context_lens, B, Hq, Hkv, D, d->block_size, scale,
+                          attn, mode);
   layer_tail(d, w, x, attn, y, h_out, B, mode);
   free(pos);
   free(seq);
@@ -497,6 +649,50 @@ void orc_layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
   free(k);
   free(v);
   free(attn);
+}
+
+/* Float caches [num_blocks][Hkv][BS][D] (k_cache NULL: no cache write). */
+void orc_layer_prefill(const orc_dims* d, const orc_weights* w, const float* x,
+                       float* y, float* h_out, const int32_t* pos,
+                       const int32_t* seq_of_token, const int32_t* cu_seqlens,
+                       int B, int T, float* k_cache, float* v_cache,
+                       const int32_t* block_table, int max_blocks_per_seq,
+                       int mode) {
+  const orc_kv c = {k_cache, v_cache, NULL, NULL, NULL, NULL};
+  layer_prefill(d, w, x, y, h_out, pos, seq_of_token, cu_seqlens, B, T, &c,
+                block_table, max_blocks_per_seq, mode);
+}
+
+void orc_layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
+                      float* y, float* h_out, const int32_t* context_lens, int B,
+                      float* k_cache, float* v_cache, const int32_t* block_table,
+                      int max_blocks_per_seq, int mode) {
+  const orc_kv c = {k_cache, v_cache, NULL, NULL, NULL, NULL};
+  layer_decode(d, w, x, y, h_out, context_lens, B, &c, block_table,
+               max_blocks_per_seq, mode);
+}
+
+/* INT8 cache: codes [num_blocks][Hkv][BS][D], scales [num_blocks][Hkv][BS]. */
+void orc_layer_prefill_q8(const orc_dims* d, const orc_weights* w, const float* x,
+                          float* y, float* h_out, const int32_t* pos,
+                          const int32_t* seq_of_token, const int32_t* cu_seqlens,
+                          int B, int T, int8_t* k_codes, int8_t* v_codes,
+                          float* k_scale, float* v_scale,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          int mode) {
+  const orc_kv c = {NULL, NULL, k_codes, v_codes, k_scale, v_scale};
+  layer_prefill(d, w, x, y, h_out, pos, seq_of_token, cu_seqlens, B, T, &c,
+                block_table, max_blocks_per_seq, mode);
+}
+
+void orc_layer_decode_q8(const orc_dims* d, const orc_weights* w, const float* x,
+                         float* y, float* h_out, const int32_t* context_lens,
+                         int B, int8_t* k_codes, int8_t* v_codes, float* k_scale,
+                         float* v_scale, const int32_t* block_table,
+                         int max_blocks_per_seq, int mode) {
+  const orc_kv c = {NULL, NULL, k_codes, v_codes, k_scale, v_scale};
+  layer_decode(d, w, x, y, h_out, context_lens, B, &c, block_table,
+               max_blocks_per_seq, mode);
 }
 
 /* ------------------------------------------------------------------------ */

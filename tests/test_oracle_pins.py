@@ -337,6 +337,147 @@ def test_paged_decode_equals_contiguous_under_permutation():
 
 
 # ---------------------------------------------------------------------------
+# INT8 KV cache: per-row quantisation on write, dequantisation in attention
+# ---------------------------------------------------------------------------
+
+def test_kv_quant_hand_values_ties_to_even():
+    # amax 127 gives scale exactly 1, so each code is x rounded half to even
+    x = np.array([[127.0, 2.5, -2.5, 3.5, -0.5, 0.5, 1.5, -127.0, 126.49, -3.51]], np.float32)
+    codes, s = oracle.kv_quant_rows(x)
+    assert s[0] == 1.0
+    assert codes[0].tolist() == [127, 2, -2, 4, 0, 0, 2, -127, 126, -4]
+    # amax 254: scale 2, codes x / 2 rounded half to even
+    codes, s = oracle.kv_quant_rows(np.array([[254.0, 5.0, -3.0, 7.0, 1.0]], np.float32))
+    assert s[0] == 2.0 and codes[0].tolist() == [127, 2, -2, 4, 0]
+
+
+def test_kv_quant_zero_and_one_hot_rows():
+    codes, s = oracle.kv_quant_rows(np.zeros((3, 64), np.float32))
+    assert (codes == 0).all() and (s == 0).all()
+    x = np.zeros((2, 128), np.float32)
+    x[0, 17] = -0.03
+    x[1, 100] = 5e3
+    codes, s = oracle.kv_quant_rows(x)
+    assert codes[0, 17] == -127 and codes[1, 100] == 127
+    assert np.count_nonzero(codes) == 2
+    assert s[0] == np.float32(0.03) / np.float32(127) and s[1] == np.float32(5e3) / np.float32(127)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_quant_error_bound_symmetry_and_scaling(D):
+    x = (R.standard_normal((200, D)) * R.uniform(0.01, 20, (200, 1))).astype(np.float32)
+    codes, s = oracle.kv_quant_rows(x)
+    assert codes.dtype == np.int8 and (np.abs(codes.astype(int)) <= 127).all()
+    # the largest magnitude of every row maps to +-127
+    i = np.abs(x).argmax(1)
+    r = np.arange(x.shape[0])
+    assert (np.abs(codes[r, i].astype(int)) == 127).all()
+    assert (np.sign(codes[r, i]) == np.sign(x[r, i])).all()
+    # rounding error at most half a step (plus fp32 slack)
+    err = np.abs(codes.astype(np.float64) * s[:, None] - x)
+    assert (err <= 0.5 * s[:, None].astype(np.float64) * (1 + 1e-5)).all()
+    # each code is the integer nearest x / scale (fp64), away from exact ties
+    t = x.astype(np.float64) / s[:, None]
+    far = np.abs(np.abs(t - np.floor(t)) - 0.5) > 1e-4
+    assert np.array_equal(codes[far], np.round(t)[far].astype(np.int8))
+    # sign symmetry and exact power-of-two scaling
+    cn, sn = oracle.kv_quant_rows(-x)
+    assert np.array_equal(cn, -codes) and np.array_equal(sn, s)
+    c8, s8 = oracle.kv_quant_rows(x * np.float32(8))
+    assert np.array_equal(c8, codes) and np.array_equal(s8, s * np.float32(8))
+
+
+def test_reshape_and_cache_q8_placement_and_sentinels():
+    T, Hkv, D, BS = 37, 2, 64, 16
+    lens = [20, 17]
+    seq = np.repeat([0, 1], lens).astype(np.int32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    k = (R.standard_normal((T, Hkv, D)) * 3).astype(np.float32)
+    v = R.standard_normal((T, Hkv, D)).astype(np.float32)
+    nb = 7
+    bt = np.array([[5, 2], [0, 6]], np.int32)
+    kq = np.full((nb, Hkv, BS, D), -128, np.int8)
+    vq = kq.copy()
+    ks = np.full((nb, Hkv, BS), np.nan, np.float32)
+    vs = ks.copy()
+    oracle.reshape_and_cache_q8(k, v, seq, pos, bt, kq, vq, ks, vs)
+    kc_ref, ks_ref = oracle.kv_quant_rows(k)
+    vc_ref, vs_ref = oracle.kv_quant_rows(v)
+    written = np.zeros((nb, BS), bool)
+    for t in range(T):
+        blk, slot = bt[seq[t], pos[t] // BS], pos[t] % BS
+        assert np.array_equal(kq[blk, :, slot], kc_ref[t]) and np.array_equal(ks[blk, :, slot], ks_ref[t])
+        assert np.array_equal(vq[blk, :, slot], vc_ref[t]) and np.array_equal(vs[blk, :, slot], vs_ref[t])
+        written[blk, slot] = True
+    free = ~written
+    assert (kq.transpose(0, 2, 1, 3)[free] == -128).all() and (vq.transpose(0, 2, 1, 3)[free] == -128).all()
+    assert np.isnan(ks.transpose(0, 2, 1)[free]).all() and np.isnan(vs.transpose(0, 2, 1)[free]).all()
+    # dequantised cache is the float cache to within half a step per row
+    kc = np.full((nb, Hkv, BS, D), np.nan, np.float32)
+    vc = kc.copy()
+    oracle.reshape_and_cache(k, v, seq, pos, bt, kc, vc)
+    wmask = np.broadcast_to(written[:, None, :], ks.shape)
+    deq = kq.astype(np.float64) * ks[..., None]
+    assert (np.abs(deq - kc)[wmask] <= 0.5 * np.broadcast_to(ks[..., None], deq.shape)[wmask] * 1.00001).all()
+
+
+def _paged_q8_case(ctx, Hq, Hkv, D, BS, seed):
+    rs = np.random.default_rng(seed)
+    B = len(ctx)
+    nblk = [(c + BS - 1) // BS for c in ctx]
+    pool = sum(nblk) + 3
+    perm = rs.permutation(pool)
+    bt = np.full((B, max(nblk)), -1, np.int32)
+    j = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[j:j + nblk[b]]
+        j += nblk[b]
+    kq = rs.integers(-127, 128, (pool, Hkv, BS, D)).astype(np.int8)
+    vq = rs.integers(-127, 128, (pool, Hkv, BS, D)).astype(np.int8)
+    q = rs.standard_normal((B, Hq, D)).astype(np.float32) * 0.1
+    return q, kq, vq, bt, np.array(ctx, np.int32), rs
+
+
+def test_attn_decode_q8_unit_scales_equal_float_path():
+    q, kq, vq, bt, ctx, _ = _paged_q8_case([5, 40, 33], 4, 2, 64, 16, 11)
+    ones = np.ones(kq.shape[:3], np.float32)
+    got = oracle.attn_decode_paged_q8(q, kq, vq, ones, ones, bt, ctx)
+    want = oracle.attn_decode_paged(q, kq.astype(np.float32), vq.astype(np.float32), bt, ctx)
+    assert np.array_equal(got, want)
+
+
+def test_attn_decode_q8_row_scales_equal_dequantised_float_cache():
+    # power-of-two scales make code x scale exact in fp32, so the float path on
+    # the dequantised cache must agree bit for bit; K and V scales differ, so a
+    # swapped or mis-indexed scale changes the result
+    q, kq, vq, bt, ctx, rs = _paged_q8_case([17, 64, 3, 50], 8, 2, 128, 16, 12)
+    ks = (2.0 ** rs.integers(-9, -4, kq.shape[:3])).astype(np.float32)
+    vs = (2.0 ** rs.integers(-6, 0, kq.shape[:3])).astype(np.float32)
+    got = oracle.attn_decode_paged_q8(q, kq, vq, ks, vs, bt, ctx)
+    want = oracle.attn_decode_paged(q, kq * ks[..., None], vq * vs[..., None], bt, ctx)
+    assert np.array_equal(got, want)
+    swapped = oracle.attn_decode_paged_q8(q, kq, vq, vs, ks, bt, ctx)
+    assert not np.allclose(swapped, got)
+
+
+def test_attn_decode_q8_closed_forms():
+    q, kq, vq, bt, ctx, rs = _paged_q8_case([1, 9], 2, 1, 64, 16, 13)
+    ks = rs.uniform(0.01, 0.05, kq.shape[:3]).astype(np.float32)
+    vs = rs.uniform(0.01, 0.05, kq.shape[:3]).astype(np.float32)
+    # identical dequantised keys in sequence 1: output = mean of its dequantised values
+    blk = bt[1, 0]
+    kq[blk, 0, :9] = kq[blk, 0, 0]
+    ks[blk, 0, :9] = ks[blk, 0, 0]
+    out = oracle.attn_decode_paged_q8(q, kq, vq, ks, vs, bt, ctx)
+    want = (vq[blk, 0, :9].astype(np.float64) * vs[blk, 0, :9, None]).mean(0)
+    np.testing.assert_allclose(out[1, 0], want, rtol=1e-6, atol=1e-7)
+    # a one-token context returns that token's dequantised value
+    b0 = bt[0, 0]
+    np.testing.assert_allclose(out[0, 1], vq[b0, 0, 0].astype(np.float64) * vs[b0, 0, 0],
+                               rtol=1e-7, atol=0)
+
+
+# ---------------------------------------------------------------------------
 # SwiGLU feed-forward
 # ---------------------------------------------------------------------------
 
@@ -438,6 +579,66 @@ def test_decode_after_prefill_equals_prefill_row():
     full = gen.packed([n + 1])
     yp, _ = oracle.layer_prefill(d, w, x, full.positions, full.seq_of_token, full.cu_seqlens)
     np.testing.assert_allclose(yd[0], yp[n], rtol=1e-6, atol=1e-6)
+
+
+def _q8_cache(nb, Hkv=4, BS=16, D=64):
+    return (np.full((nb, Hkv, BS, D), -128, np.int8), np.full((nb, Hkv, BS, D), -128, np.int8),
+            np.full((nb, Hkv, BS), np.nan, np.float32), np.full((nb, Hkv, BS), np.nan, np.float32))
+
+
+def test_layer_q8_prefill_output_unchanged_and_cache_quantised():
+    cfg, gen, w = _tiny()
+    d = cfg.dims()
+    pb = gen.packed([13, 6])
+    x = gen.hidden(cfg, pb.T)
+    bt = gen.block_table(cfg, pb.lens)
+    kq, vq, ks, vs = _q8_cache(bt.num_blocks)
+    y8, h8 = oracle.layer_prefill_q8(d, w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens,
+                                     kq, vq, ks, vs, bt.table, mode=oracle.BF16)
+    y, h = oracle.layer_prefill(d, w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens,
+                                mode=oracle.BF16)
+    assert np.array_equal(y8, y) and np.array_equal(h8, h)   # prefill never reads the cache
+    n1 = oracle.rmsnorm(x, w["ln1"], d["rms_eps"], mode=oracle.BF16)
+    _, k, v = oracle.qkv_rope(n1, w["wq"], w["wk"], w["wv"], pb.positions, d["rope_theta"], 4,
+                              4, 64, mode=oracle.BF16)
+    kq2, vq2, ks2, vs2 = _q8_cache(bt.num_blocks)
+    oracle.reshape_and_cache_q8(k, v, pb.seq_of_token, pb.positions, bt.table, kq2, vq2, ks2, vs2)
+    assert np.array_equal(kq, kq2) and np.array_equal(vq, vq2)
+    assert np.array_equal(ks, ks2, equal_nan=True) and np.array_equal(vs, vs2, equal_nan=True)
+
+
+def test_layer_q8_decode_equals_steps_and_tracks_float_cache():
+    cfg, gen, w = _tiny()
+    d = cfg.dims()
+    n = 21
+    x = gen.hidden(cfg, n + 1)
+    bt = gen.block_table(cfg, [n + 1])
+    pb = gen.packed([n])
+    kq, vq, ks, vs = _q8_cache(bt.num_blocks)
+    oracle.layer_prefill_q8(d, w, x[:n], pb.positions, pb.seq_of_token, pb.cu_seqlens,
+                            kq, vq, ks, vs, bt.table)
+    ctx = np.array([n + 1], np.int32)
+    before = (kq.copy(), vq.copy(), ks.copy(), vs.copy())
+    yd, hd = oracle.layer_decode_q8(d, w, x[n:], ctx, kq, vq, ks, vs, bt.table)
+    # the same step by step
+    kq2, vq2, ks2, vs2 = before
+    n1 = oracle.rmsnorm(x[n:], w["ln1"], d["rms_eps"])
+    q, k, v = oracle.qkv_rope(n1, w["wq"], w["wk"], w["wv"], ctx - 1, d["rope_theta"], 4, 4, 64)
+    oracle.reshape_and_cache_q8(k, v, [0], ctx - 1, bt.table, kq2, vq2, ks2, vs2)
+    at = oracle.attn_decode_paged_q8(q, kq2, vq2, ks2, vs2, bt.table, ctx).reshape(1, -1)
+    o = oracle.linear(at, w["wo"])
+    n2, hh = oracle.rmsnorm(o, w["ln2"], d["rms_eps"], resid=x[n:])
+    yy = oracle.ffn(n2, w["wg"], w["wu"], w["wd"], hh)
+    assert np.array_equal(yd, yy) and np.array_equal(hd, hh) and np.array_equal(kq, kq2)
+    # and it stays close to the float-cache layer (INT8 error only)
+    kc = np.full((bt.num_blocks, 4, 16, 64), np.nan, np.float32)
+    vc = kc.copy()
+    oracle.layer_prefill(d, w, x[:n], pb.positions, pb.seq_of_token, pb.cu_seqlens, kc, vc,
+                         bt.table)
+    yf, _ = oracle.layer_decode(d, w, x[n:], ctx, kc, vc, bt.table)
+    dy, df = yd - x[n:], yf - x[n:]
+    rel = np.linalg.norm(dy - df) / np.linalg.norm(df)
+    assert 0 < rel < 2e-2, rel
 
 
 def test_layer_bf16_modes_close_to_exact():
