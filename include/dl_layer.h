@@ -26,8 +26,9 @@
  *     cache, attention output and FFN intermediate are bf16 (round to nearest
  *     even), every product accumulates in fp32, and the residual stream
  *     (hidden_in, h, hidden_out) is fp32.  DL_F32: everything is fp32.
- *   - KV cache: separate K and V tensors, each [num_blocks][Hkv][BS][D] in the
- *     layer dtype.  Position p of sequence s lives in physical block
+ *   - KV cache: separate K and V tensors, each [num_blocks][Hkv][BS][D], in
+ *     the layer dtype or as INT8 codes with row scales (dl_kv_cache below).
+ *     Position p of sequence s lives in physical block
  *     block_table[s][p / BS] at slot p % BS.  block_table is
  *     [B][max_blocks_per_seq] int32; unused entries may hold any value.
  *   - Return value: DL_OK, or an error code, in which case NOTHING was
@@ -89,10 +90,36 @@ typedef struct {
   const void *ln1_gamma, *w_q, *w_k, *w_v, *w_o, *ln2_gamma, *w_gate, *w_up, *w_down;
 } dl_layer_weights;
 
+/*
+ * Element format of a KV cache.
+ *   DL_KV_LAYER: K and V values in the layer dtype.
+ *   DL_KV_INT8:  per-token INT8 quantisation with online scales (ATB KV-cache
+ *     page, hwcomputing.csdn.net, section "KV cache quantisation": one fp32
+ *     scale for each token's K and one for its V, computed as the token is
+ *     written; the paged attention dequantises the blocks as it loads them).
+ *     A row is one (token, kv head) D-vector of K or of V; writing it stores
+ *       scale = max|x| / 127 and code = x / scale rounded to the nearest
+ *       integer (ties to even), clamped to [-127, 127], both in fp32
+ *     (an all-zero row stores scale 0 and zero codes); reading it uses
+ *     code x scale.  Symmetric: there is no offset.
+ */
+typedef enum { DL_KV_LAYER = 0, DL_KV_INT8 = 1 } dl_kv_format;
+
+/*
+ * A paged KV cache.  A zero-initialised tail (format 0, NULL scales) is the
+ * layer-dtype cache.
+ *   k_cache, v_cache: [num_blocks][Hkv][BS][D] values (DL_KV_LAYER) or int8
+ *     codes (DL_KV_INT8), 16-byte aligned;
+ *   k_scale, v_scale: DL_KV_INT8 only, [num_blocks][Hkv][BS] fp32, 4-byte
+ *     aligned: the scale of the row at the same (block, head, slot).
+ */
 typedef struct {
-  void* k_cache;       /* [num_blocks][Hkv][BS][D] */
-  void* v_cache;       /* [num_blocks][Hkv][BS][D] */
+  void* k_cache;
+  void* v_cache;
   int32_t num_blocks;
+  dl_kv_format format;
+  float* k_scale;
+  float* v_scale;
 } dl_kv_cache;
 
 /* Human-readable name of a status code (static string). */
@@ -152,7 +179,9 @@ dl_status dl_qkv_rope(const void* x, const void* w_q, const void* w_k, const voi
  * block_table[seq][positions[t] / BS], slot positions[t] % BS.  k and v may
  * both be NULL (then they go to the cache only) or both be given.  Table
  * entries outside [0, num_blocks) and positions outside the table are
- * skipped.  Workspace as dl_qkv_rope_workspace_size.
+ * skipped.  Workspace as dl_qkv_rope_workspace_size.  DL_KV_LAYER caches
+ * only (an INT8 cache returns DL_ERR_UNSUPPORTED; write it with dl_qkv_rope
+ * followed by dl_reshape_and_cache).
  */
 dl_status dl_qkv_rope_cache(const void* x, const void* w_q, const void* w_k, const void* w_v,
                             const int32_t* positions, const float* cos_sin, int32_t max_pos,
@@ -167,8 +196,12 @@ dl_status dl_qkv_rope_cache(const void* x, const void* w_q, const void* w_k, con
  * ReshapeAndCache writes step K/V into the paged blocks through block_table).
  * Token t of sequence seq_of_token[t] at position positions[t] is copied to
  * block block_table[seq][pos / BS], slot pos % BS, of both caches.  A bit
- * copy.  k, v [T][Hkv][D]; seq_of_token [T] int32, or NULL meaning
- * seq_of_token[t] = t (one token per sequence, the decode case).
+ * copy for a DL_KV_LAYER cache; a DL_KV_INT8 cache gets each (token, kv
+ * head) row of k and of v quantised as dl_kv_format describes, its scale
+ * going to the same (block, head, slot) of k_scale / v_scale.  k, v
+ * [T][Hkv][D] of dtype dt; seq_of_token [T] int32, or NULL meaning
+ * seq_of_token[t] = t (one token per sequence, the decode case).  Table
+ * entries outside [0, num_blocks) drop the token's write.
  */
 dl_status dl_reshape_and_cache(const void* k, const void* v, const int32_t* seq_of_token,
                                const int32_t* positions, const int32_t* block_table,
@@ -196,7 +229,8 @@ dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
  * ATB KV-cache page: PagedAttention over block_table and contextLens).
  * Sequence b attends over cached positions 0 .. context_lens[b]-1 (the new
  * token must already be in the cache).  q, out [B][Hq][D].  The result does
- * not depend on which physical blocks hold the data.
+ * not depend on which physical blocks hold the data.  A DL_KV_INT8 cache is
+ * dequantised (code x row scale) as its blocks are read.
  */
 size_t dl_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                      int32_t max_context_len, int32_t BS);
@@ -253,7 +287,9 @@ size_t dl_layer_workspace_size(const dl_layer_dims* d, int32_t max_tokens, int32
  *   hidden_in [T][H] fp32 -> hidden_out [T][H] fp32 (must not alias).
  *   positions [T] (restart at 0 in every sequence), seq_of_token [T],
  *   cu_seqlens [B+1]; every token's K/V is also written to the cache.
- * Attention reads K/V straight from the projection output.
+ * Attention reads K/V straight from the projection output.  DL_KV_INT8
+ * caches need m == DL_FUSED (the kernel-per-op chain is the baseline of the
+ * layer-dtype cache; it returns DL_ERR_UNSUPPORTED for them).
  */
 dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
                            const float* cos_sin, int32_t max_pos, const float* hidden_in,
@@ -269,7 +305,8 @@ dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
  *   positions [B] = context_lens - 1; context_lens [B] counts the new token.
  * The new K/V are written to the cache first, then attention runs over the
  * whole cached context (ascend-transformer-boost page, "KVCache management":
- * update the cache in place, then attend over the full cache).
+ * update the cache in place, then attend over the full cache).  DL_KV_INT8
+ * caches need m == DL_FUSED, as for dl_layer_prefill.
  */
 dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
                           const float* cos_sin, int32_t max_pos, const float* hidden_in,

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings_and_version(L):
     assert L.dl_status_string(0) == b"DL_OK"
     assert L.dl_status_string(4) == b"DL_ERR_WORKSPACE"
-    assert L.dl_abi_version() == 1
+    assert L.dl_abi_version() == 2
 
 
 def test_null_and_unsupported_arguments_fail_on_host(L):
@@ -58,6 +58,31 @@ def test_null_and_unsupported_arguments_fail_on_host(L):
     # empty work is fine and touches nothing
     assert L.dl_rmsnorm_residual(None, dl.DL_F32, None, None, None, None, 0, 256, 1e-5,
                                  dl.DL_F32, None) == 0
+
+
+def test_int8_cache_descriptor_checks(L):
+    # (fake, aligned device addresses: every call below fails before any launch)
+    no_scales = dl.KVCache(16, 32, 4, dl.DL_KV_INT8, None, None)
+    s = L.dl_reshape_and_cache(16, 32, None, 48, 64, 2, ctypes.byref(no_scales), 4, 2, 128, 16,
+                               dl.DL_BF16, None)
+    assert s == 1 and b"k_scale must not be NULL" in L.dl_last_error()
+    odd = dl.KVCache(16, 32, 4, 7, None, None)
+    s = L.dl_reshape_and_cache(16, 32, None, 48, 64, 2, ctypes.byref(odd), 4, 2, 128, 16,
+                               dl.DL_BF16, None)
+    assert s == 1 and b"unknown cache format" in L.dl_last_error()
+    misaligned = dl.KVCache(16, 32, 4, dl.DL_KV_INT8, 18, 64)
+    s = L.dl_reshape_and_cache(16, 32, None, 48, 64, 2, ctypes.byref(misaligned), 4, 2, 128, 16,
+                               dl.DL_BF16, None)
+    assert s == 3 and b"k_scale" in L.dl_last_error()
+    q8 = dl.KVCache(16, 32, 4, dl.DL_KV_INT8, 48, 64)
+    s = L.dl_qkv_rope_cache(16, 32, 48, 64, 80, 96, 8, 112, 128, 144, None, 160, 2,
+                            ctypes.byref(q8), 4, 256, 4, 4, 64, 16, dl.DL_BF16, None, 0, None)
+    assert s == 2 and b"INT8" in L.dl_last_error()
+    d = dl.LayerDims(256, 4, 4, 64, 688, 16, 1e-5, dl.DL_BF16)
+    w = dl.LayerWeights(*[256 * (i + 1) for i in range(9)])
+    s = L.dl_layer_decode(ctypes.byref(d), ctypes.byref(w), 4096, 64, 8192, 8448, 8704, 8960, 32,
+                          1, ctypes.byref(q8), 9216, 2, dl.DL_UNFUSED, 9472, 1 << 20, None)
+    assert s == 2 and b"DL_FUSED" in L.dl_last_error()
 
 
 def test_layer_workspace_queries(L):

@@ -6,7 +6,8 @@ step, workspace from dl_layer_workspace_size):
   * 7B decode, B64, contexts U{128..4096}, synthetic prior K/V;
   * 8B-GQA prefill of 8 ragged sequences U{256..1024}, then 128 decode steps
     on the cache that prefill wrote;
-  * 70B decode, B4 x 4096 and B1 x 32768.
+  * 70B decode, B4 x 4096 and B1 x 32768;
+  * 7B decode B64 and 70B decode B1 x 32768 again with an INT8 KV cache.
 
 The oracle cannot run these layers whole in seconds, so each step is checked
 on sampled rows (every row where B is small): a sampled row is recomputed by
@@ -238,3 +239,69 @@ def layer_70b():
 @pytest.mark.parametrize("case", [0, 1])
 def test_llama_70b_decode_full_size(layer_70b, case):
     run_full_decode(layer_70b, gen.decode_context_lens(layer_70b.cfg, case), case)
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache at full size
+# ---------------------------------------------------------------------------
+
+def q8_equal(a, b):
+    if a.dtype == torch.float32:
+        return torch.equal(a.view(torch.int32), b.view(torch.int32))
+    return torch.equal(a, b)
+
+
+def decode_step_checked_q8(layer, x_host, ctx, caches, bt, btd, what, rows=None):
+    """decode_step_checked for an INT8 cache (codes k, v and scales k, v):
+    fused equals step by step bit for bit, the cache write is the oracle's
+    quantisation of the GPU's own k/v bit for bit, and every (sequence, head)
+    of attention matches the oracle's INT8 attention over that cache."""
+    B = x_host.shape[0]
+    before = tuple(t.cpu().numpy() for t in caches)
+    c2 = tuple(t.clone() for t in caches)
+    xd = to_dev(x_host, torch.float32)
+    ws = fused_ws(layer, B, B, 0, int(ctx.max()))
+    y = layer.decode(xd, ctx, caches[0], caches[1], btd, ws=ws, ks=caches[2], vs=caches[3])
+    s = layer.steps_decode(xd, ctx, c2[0], c2[1], btd, ks=c2[2], vs=c2[3])
+    torch.cuda.synchronize()
+    assert torch.equal(y, s["y"]), f"{what}: fused decode differs from the step-by-step chain"
+    assert all(q8_equal(a, b) for a, b in zip(caches, c2)), f"{what}: caches differ"
+    del c2
+    pos = (ctx - 1).astype(np.int32)
+    rows = np.arange(B) if rows is None else rows
+    check_head(layer, s, x_host, pos, rows, what)
+    want = tuple(a.copy() for a in before)
+    del before
+    oracle.reshape_and_cache_q8(host(s["k"]), host(s["v"]), np.arange(B, dtype=np.int32), pos,
+                                bt.table, *want)
+    for got, w, name in zip(caches, want, ("k codes", "v codes", "k scales", "v scales")):
+        g = got.cpu().numpy()
+        same = (g.view(np.uint32) == w.view(np.uint32)) if g.dtype == np.float32 else (g == w)
+        assert same.all(), f"{what}: {int((~same).sum())} {name} differ from the oracle"
+    ref = oracle.attn_decode_paged_q8(host(s["q"]), *want, bt.table, ctx, mode=oracle.BF16)
+    del want
+    assert_bf16_close(host(s["attn"]), ref, f"{what} attn")
+    check_tail(layer, s, x_host, rows, what)
+    return y
+
+
+def run_full_decode_q8(layer, ctx, case, rows=None):
+    cfg = layer.cfg
+    bt = gen.block_table(cfg, ctx)
+    caches = tuple(cache_dev(a) for a in gen.synthetic_cache_q8(cfg, bt, ctx, case=case))
+    x = gen.hidden(cfg, ctx.size, step=1 + case)
+    say(f"{cfg.name} INT8 cache: B={ctx.size} ctx {ctx.min()}..{ctx.max()} "
+        f"({bt.num_blocks} blocks)")
+    decode_step_checked_q8(layer, x, ctx, caches, bt, i32(bt.table),
+                           f"{cfg.name} int8 case {case}", rows=rows)
+
+
+def test_llama2_7b_decode_int8_cache_full_size():
+    cfg = gen.CONFIGS[3]
+    ctx = gen.decode_context_lens(cfg)
+    layer = DeviceLayer.build(cfg, max_pos=int(ctx.max()) + 1)
+    run_full_decode_q8(layer, ctx, 0, rows=sample_rows(ctx.size, 12, 5, must=[0, ctx.size - 1]))
+
+
+def test_llama_70b_decode_int8_cache_full_size(layer_70b):
+    run_full_decode_q8(layer_70b, gen.decode_context_lens(layer_70b.cfg, 1), 1)

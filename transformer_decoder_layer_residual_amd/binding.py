@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libdl_layer.so")
 DL_OK = 0
 DL_F32, DL_BF16 = 0, 1
 DL_FUSED, DL_UNFUSED = 0, 1
+DL_KV_LAYER, DL_KV_INT8 = 0, 1
+ABI_VERSION = 2
 
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -47,7 +49,8 @@ class LayerWeights(ctypes.Structure):
 
 
 class KVCache(ctypes.Structure):
-    _fields_ = [("k_cache", _vp), ("v_cache", _vp), ("num_blocks", _c_int)]
+    _fields_ = [("k_cache", _vp), ("v_cache", _vp), ("num_blocks", _c_int),
+                ("format", ctypes.c_int), ("k_scale", _vp), ("v_scale", _vp)]
 
 
 # (name, restype, argtypes)
@@ -161,8 +164,16 @@ def _ws(nbytes: int, ws, device):
     return ws, ws.numel() * ws.element_size()
 
 
-def _cache(k_cache, v_cache) -> KVCache:
-    return KVCache(_p(k_cache), _p(v_cache), int(k_cache.shape[0]))
+def _cache(k_cache, v_cache, k_scale=None, v_scale=None) -> KVCache:
+    """int8 cache tensors describe a DL_KV_INT8 cache (codes) and need the
+    [num_blocks, Hkv, BS] float32 row scales; any other dtype is the layer
+    dtype."""
+    if k_cache.dtype == torch.int8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an int8 KV cache needs k_scale and v_scale")
+        return KVCache(_p(k_cache), _p(v_cache), int(k_cache.shape[0]), DL_KV_INT8, _p(k_scale),
+                       _p(v_scale))
+    return KVCache(_p(k_cache), _p(v_cache), int(k_cache.shape[0]), DL_KV_LAYER, None, None)
 
 
 # ---------------------------------------------------------------------------
@@ -193,7 +204,7 @@ def dl_qkv_rope(x, w_q, w_k, w_v, positions, cos_sin, q, k, v, ws=None):
 
 
 def dl_qkv_rope_cache(x, w_q, w_k, w_v, positions, cos_sin, q, k, v, seq_of_token, block_table,
-                      k_cache, v_cache, Hkv=None, ws=None):
+                      k_cache, v_cache, Hkv=None, ws=None, k_scale=None, v_scale=None):
     """k, v: [T, Hkv, D] tensors, or both None (K/V then go to the cache only;
     pass Hkv)."""
     T, H = x.shape
@@ -202,16 +213,17 @@ def dl_qkv_rope_cache(x, w_q, w_k, w_v, positions, cos_sin, q, k, v, seq_of_toke
     dt = dtype_code(x.dtype)
     L = lib()
     ws, nb = _ws(L.dl_qkv_rope_workspace_size(T, H, Hq, Hkv, D, dt), ws, x.device)
-    c = _cache(k_cache, v_cache)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
     _check(L.dl_qkv_rope_cache(_p(x), _p(w_q), _p(w_k), _p(w_v), _p(positions), _p(cos_sin),
                                cos_sin.shape[0], _p(q), _p(k), _p(v), _p(seq_of_token),
                                _p(block_table), block_table.shape[1], ctypes.byref(c), T, H, Hq,
                                Hkv, D, k_cache.shape[2], dt, _p(ws), nb, _stream()))
 
 
-def dl_reshape_and_cache(k, v, seq_of_token, positions, block_table, k_cache, v_cache):
+def dl_reshape_and_cache(k, v, seq_of_token, positions, block_table, k_cache, v_cache,
+                         k_scale=None, v_scale=None):
     T, Hkv, D = k.shape
-    c = _cache(k_cache, v_cache)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
     _check(lib().dl_reshape_and_cache(_p(k), _p(v), _p(seq_of_token), _p(positions),
                                       _p(block_table), block_table.shape[1], ctypes.byref(c), T,
                                       Hkv, D, k_cache.shape[2], dtype_code(k.dtype), _stream()))
@@ -227,14 +239,14 @@ def dl_attn_prefill(q, k, v, cu_seqlens, max_seqlen: int, out, scale=None):
 
 
 def dl_attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len: int,
-                         out, scale=None, ws=None):
+                         out, scale=None, ws=None, k_scale=None, v_scale=None):
     B, Hq, D = q.shape
     Hkv, BS = k_cache.shape[1], k_cache.shape[2]
     scale = D ** -0.5 if scale is None else scale
     L = lib()
     ws, nb = _ws(L.dl_attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, BS), ws,
                  q.device)
-    c = _cache(k_cache, v_cache)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
     _check(L.dl_attn_decode_paged(_p(q), ctypes.byref(c), _p(block_table), block_table.shape[1],
                                   _p(context_lens), max_context_len, B, Hq, Hkv, D, BS, scale,
                                   _p(out), dtype_code(q.dtype), _p(ws), nb, _stream()))
@@ -304,7 +316,7 @@ def dl_layer_workspace_size(dims: LayerDims, max_tokens, max_batch, max_seqlen, 
 
 def dl_layer_prefill(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_out, positions,
                      seq_of_token, cu_seqlens, max_seqlen, k_cache, v_cache, block_table,
-                     mode=DL_FUSED, ws=None):
+                     mode=DL_FUSED, ws=None, k_scale=None, v_scale=None):
     T = hidden_in.shape[0]
     B = cu_seqlens.shape[0] - 1
     L = lib()
@@ -312,7 +324,7 @@ def dl_layer_prefill(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_
         n = L.dl_layer_workspace_size(ctypes.byref(dims), T, B, max_seqlen, 0, mode)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=hidden_in.device)
     wts = make_weights(weights)
-    c = _cache(k_cache, v_cache)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
     _check(L.dl_layer_prefill(ctypes.byref(dims), ctypes.byref(wts), _p(cos_sin),
                               cos_sin.shape[0], _p(hidden_in), _p(hidden_out), _p(positions),
                               _p(seq_of_token), _p(cu_seqlens), B, T, max_seqlen, ctypes.byref(c),
@@ -322,14 +334,14 @@ def dl_layer_prefill(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_
 
 def dl_layer_decode(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_out, positions,
                     context_lens, max_context_len, k_cache, v_cache, block_table, mode=DL_FUSED,
-                    ws=None):
+                    ws=None, k_scale=None, v_scale=None):
     B = hidden_in.shape[0]
     L = lib()
     if ws is None:
         n = L.dl_layer_workspace_size(ctypes.byref(dims), B, B, 0, max_context_len, mode)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=hidden_in.device)
     wts = make_weights(weights)
-    c = _cache(k_cache, v_cache)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
     _check(L.dl_layer_decode(ctypes.byref(dims), ctypes.byref(wts), _p(cos_sin), cos_sin.shape[0],
                              _p(hidden_in), _p(hidden_out), _p(positions), _p(context_lens),
                              max_context_len, B, ctypes.byref(c), _p(block_table),

@@ -29,6 +29,18 @@
 //     wave owns, so the block loop needs no barrier; waves merge once;
 //   * each split writes (o, m, l) in fp32; a second kernel combines the
 //     splits in fixed order.
+//
+// INT8 cache (ATB KV-cache page, section "KV cache quantisation": the paged
+// attention dequantises the blocks as it loads them; one fp32 scale per
+// token row of K and of V): each thread reads an 8-byte slice of codes and
+// the row's scale.  A code byte c is read as the unsigned byte u = c + 128
+// (one XOR per four codes, then one byte-to-float convert per code), so
+//   q . k = s_k * (sum_d q_d u_d - 128 * sum_d q_d)
+//   sum_j p_j v_j = sum_j (p_j s_v,j) u_j - 128 * sum_j p_j s_v,j
+// where the query sums are taken once per thread and the second correction
+// is carried next to the softmax denominator.
+#include <type_traits>
+
 #include "dl_internal.hpp"
 
 namespace dl {
@@ -53,9 +65,35 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int B
   return pl;
 }
 
-template <typename T, int D, int G>
+// How a thread reads its slice of a cached row.
+template <typename T, typename KV>
+struct DecSlice {  // cache in the layer dtype: 16-byte slices
+  static constexpr bool kQ8 = false;
+  static constexpr int VE = 16 / sizeof(T);
+  using L = u32x4;
+  static __device__ __forceinline__ L load(const KV* p) { return ld16(p); }
+  static __device__ __forceinline__ void unpack(L v, float* f) { unpack16(v, f, T()); }
+};
+template <typename T>
+struct DecSlice<T, int8_t> {  // INT8 codes: 8-byte slices, read as code + 128
+  static constexpr bool kQ8 = true;
+  static constexpr int VE = 8;
+  using L = u32x2;
+  static __device__ __forceinline__ L load(const int8_t* p) { return ld8(p); }
+  static __device__ __forceinline__ void unpack(L v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w = v[i] ^ 0x80808080u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * i + e] = (float)((w >> (8 * e)) & 0xffu);
+    }
+  }
+};
+
+template <typename T, typename KV, int D, int G>
 __global__ void __launch_bounds__(kDecThreads)
-attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV* __restrict__ vc,
+                   const float* __restrict__ ksc, const float* __restrict__ vsc,
                    const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ ctx,
                    int B, int Hq, int Hkv, int BS, float scale_log2, int chunk_blocks,
                    int max_splits, float* __restrict__ ws, int num_blocks) {
@@ -65,7 +103,11 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   // shuffles; every wave keeps its own online softmax (m, l, o) over the
   // tokens it owns, so the block loop has no workgroup barrier; the four
   // waves are merged once at the end of the split.
-  constexpr int NT = kDecThreads, VE = 16 / sizeof(T);
+  using Sl = DecSlice<T, KV>;
+  using Ld = typename Sl::L;
+  constexpr bool Q8 = Sl::kQ8;
+  constexpr int NT = kDecThreads, VE = Sl::VE;
+  constexpr int QE = 16 / sizeof(T);           // query elements per 16-byte load
   constexpr int LPT = D / VE;                 // lanes per token row
   constexpr int TPI = NT / LPT;               // tokens per load step (whole workgroup)
   constexpr int NI = (kDecMaxBS + TPI - 1) / TPI;
@@ -112,19 +154,27 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   const int c = tid % LPT, tok0 = tid / LPT;
 
   // this thread's slice of the (pre-scaled) query of every head in the group
-  float qf[G][VE];
+  float qf[G][VE], qs[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float tmp[VE];
-    unpack16(ld16(q + ((int64_t)b * Hq + g * G + h) * D + c * VE), tmp, T());
+    const T* qp = q + ((int64_t)b * Hq + g * G + h) * D + c * VE;
 #pragma unroll
-    for (int e = 0; e < VE; ++e) qf[h][e] = tmp[e] * scale_log2;
+    for (int u = 0; u < VE / QE; ++u) unpack16(ld16(qp + u * QE), tmp + u * QE, T());
+    qs[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      qf[h][e] = tmp[e] * scale_log2;
+      qs[h] += qf[h][e];
+    }
   }
-  float m[G], l[G], o[G][VE];
+  // m, l: running max and denominator; W: running sum of p * s_v (INT8 only)
+  float m[G], l[G], W[G], o[G][VE];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
+    W[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < VE; ++e) o[h][e] = 0.f;
   }
@@ -141,27 +191,38 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   // clamped into the block (their scores are masked), and past the split's
   // last block the loads repeat that block (cache hits, never used), so the
   // compiler's in-order load counting never has to drain the queue.
-  auto gload = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], int j) {
+  // Slot s of the block: codes or values of row (phys, g, s); INT8 rows also
+  // bring their K and V scales (ks, vs; unused otherwise).
+  struct Buf {
+    Ld k[NI], v[NI];
+    float ks[NI], vs[NI];
+  };
+  auto gload = [&](Buf& r, int j) {
     const bool past = j >= nb;  // look-ahead past the split: one cached row
     const int phys = __builtin_amdgcn_readlane(my_phys, min(j, nb - 1));
-    const int64_t base = (((int64_t)phys * Hkv + g) * BS) * D + c * VE;
+    const int64_t srow = ((int64_t)phys * Hkv + g) * BS;
+    const int64_t base = srow * D + c * VE;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = past ? 0 : min(tok0 + i * TPI, BS - 1);
-      kr[i] = ld16(kc + base + (int64_t)tok * D);
-      vr[i] = ld16(vc + base + (int64_t)tok * D);
+      r.k[i] = Sl::load(kc + base + (int64_t)tok * D);
+      r.v[i] = Sl::load(vc + base + (int64_t)tok * D);
+      if constexpr (Q8) {
+        r.ks[i] = ksc[srow + tok];
+        r.vs[i] = vsc[srow + tok];
+      }
     }
   };
-  auto process = [&](const u32x4 (&kcur)[NI], const u32x4 (&vcur)[NI], int blk) {
+  auto process = [&](const Buf& r, int blk) {
     const int ntok = min(BS, n - blk * BS);
     float sc[NI][G];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kv[VE];
-      unpack16(kcur[i], kv, T());
+      Sl::unpack(r.k[i], kv);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
+        float acc = Q8 ? -128.f * qs[h] : 0.f;
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc += qf[h][e] * kv[e];
         sc[i][h] = acc;
@@ -174,6 +235,12 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int h = 0; h < G; ++h) sc[i][h] += __shfl_xor(sc[i][h], off, kWave);
+    if constexpr (Q8) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[i][h] *= r.ks[i];
+    }
     // mask, then the wave's online softmax over its tokens of this block
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -190,6 +257,7 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
       const float alpha = m_new == -INFINITY ? 1.f : exp2f(m[h] - m_new);
       m[h] = m_new;
       l[h] *= alpha;
+      W[h] *= alpha;
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[h][e] *= alpha;
 #pragma unroll
@@ -204,11 +272,14 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
       const int tok = tok0 + i * TPI;
       if (tok < ntok) {
         float vv[VE];
-        unpack16(vcur[i], vv, T());
+        Sl::unpack(r.v[i], vv);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h) {
+          const float w = Q8 ? sc[i][h] * r.vs[i] : sc[i][h];
+          if constexpr (Q8) W[h] += w;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) o[h][e] += sc[i][h] * vv[e];
+          for (int e = 0; e < VE; ++e) o[h][e] += w * vv[e];
+        }
       }
     }
   };
@@ -216,25 +287,31 @@ attn_decode_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* _
   if constexpr (G <= 2) {
     // unrolled over the largest split; leaving early is a branch out, so no
     // join point ever mixes different numbers of loads in flight
-    u32x4 ka[NI], va[NI], kb[NI], vb[NI];
-    gload(ka, va, 0);
-    gload(kb, vb, 1);
+    Buf ba, bb;
+    gload(ba, 0);
+    gload(bb, 1);
 #pragma unroll
     for (int j = 0; j < kDecMaxSplitBlocks; j += 2) {
-      process(ka, va, blk_begin + j);
+      process(ba, blk_begin + j);
       if (j + 1 >= nb) break;
-      gload(ka, va, j + 2);
-      process(kb, vb, blk_begin + j + 1);
+      gload(ba, j + 2);
+      process(bb, blk_begin + j + 1);
       if (j + 2 >= nb) break;
-      gload(kb, vb, j + 3);
+      gload(bb, j + 3);
     }
   } else {
     // larger query groups keep G x D of state per thread: one block in flight
     for (int j = 0; j < nb; ++j) {
-      u32x4 ka[NI], va[NI];
-      gload(ka, va, j);
-      process(ka, va, blk_begin + j);
+      Buf ba;
+      gload(ba, j);
+      process(ba, blk_begin + j);
     }
+  }
+  if constexpr (Q8) {  // the -128 offset of the value codes
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[h][e] -= 128.f * W[h];
   }
 
   // merge the token lanes of each wave (fixed order), then the waves
@@ -304,48 +381,49 @@ attn_decode_combine(const float* __restrict__ ws, const int32_t* __restrict__ ct
   out[((int64_t)b * Hq + h) * D + d] = from_f32<T>(num / den);
 }
 
-template <typename T, int D, int G>
-static hipError_t launch_dec(const T* q, const T* kc, const T* vc, const int32_t* bt,
-                             int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int BS,
-                             float sl2, const DecodePlan& pl, float* ws, int num_blocks,
-                             hipStream_t st) {
+template <typename T, typename KV, int D, int G>
+static hipError_t launch_dec(const T* q, const KV* kc, const KV* vc, const float* ks,
+                             const float* vs, const int32_t* bt, int max_blocks,
+                             const int32_t* ctx, int B, int Hq, int Hkv, int BS, float sl2,
+                             const DecodePlan& pl, float* ws, int num_blocks, hipStream_t st) {
   const dim3 grid(pl.max_splits * Hkv * B);
-  hipLaunchKernelGGL((attn_decode_kernel<T, D, G>), grid, dim3(kDecThreads), 0, st, q, kc, vc,
-                     bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl.chunk_blocks, pl.max_splits,
-                     ws, num_blocks);
+  hipLaunchKernelGGL((attn_decode_kernel<T, KV, D, G>), grid, dim3(kDecThreads), 0, st, q, kc,
+                     vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl.chunk_blocks,
+                     pl.max_splits, ws, num_blocks);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t dispatch_g(const T* q, const T* kc, const T* vc, const int32_t* bt,
-                             int max_blocks, const int32_t* ctx, int B, int Hq, int Hkv, int BS,
-                             float sl2, const DecodePlan& pl, float* ws, int num_blocks,
-                             hipStream_t st) {
+template <typename T, typename KV, int D>
+static hipError_t dispatch_g(const T* q, const KV* kc, const KV* vc, const float* ks,
+                             const float* vs, const int32_t* bt, int max_blocks,
+                             const int32_t* ctx, int B, int Hq, int Hkv, int BS, float sl2,
+                             const DecodePlan& pl, float* ws, int num_blocks, hipStream_t st) {
   switch (Hq / Hkv) {
-    case 1: return launch_dec<T, D, 1>(q, kc, vc, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
-    case 2: return launch_dec<T, D, 2>(q, kc, vc, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
-    case 4: return launch_dec<T, D, 4>(q, kc, vc, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
-    case 8: return launch_dec<T, D, 8>(q, kc, vc, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
+    case 1: return launch_dec<T, KV, D, 1>(q, kc, vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
+    case 2: return launch_dec<T, KV, D, 2>(q, kc, vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
+    case 4: return launch_dec<T, KV, D, 4>(q, kc, vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
+    case 8: return launch_dec<T, KV, D, 8>(q, kc, vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl, ws, num_blocks, st);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T>
-hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
-                             const int32_t* block_table, int max_blocks,
-                             const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
-                             float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
-                             hipStream_t st) {
+template <typename T, typename KV>
+static hipError_t decode_impl(const T* q, const KV* k_cache, const KV* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                              float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
+                              hipStream_t st) {
   if (B == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
   float* w = reinterpret_cast<float*>(ws);
   hipError_t e;
   if (D == 128)
-    e = dispatch_g<T, 128>(q, k_cache, v_cache, block_table, max_blocks, context_lens, B, Hq, Hkv,
-                           BS, sl2, pl, w, num_blocks, st);
+    e = dispatch_g<T, KV, 128>(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks,
+                               context_lens, B, Hq, Hkv, BS, sl2, pl, w, num_blocks, st);
   else if (D == 64)
-    e = dispatch_g<T, 64>(q, k_cache, v_cache, block_table, max_blocks, context_lens, B, Hq, Hkv,
-                          BS, sl2, pl, w, num_blocks, st);
+    e = dispatch_g<T, KV, 64>(q, k_cache, v_cache, k_scale, v_scale, block_table, max_blocks,
+                              context_lens, B, Hq, Hkv, BS, sl2, pl, w, num_blocks, st);
   else
     return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
@@ -358,6 +436,28 @@ hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
+                             const int32_t* block_table, int max_blocks,
+                             const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                             float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
+                             hipStream_t st) {
+  return decode_impl<T, T>(q, k_cache, v_cache, nullptr, nullptr, block_table, max_blocks,
+                           context_lens, B, Hq, Hkv, D, BS, scale, out, pl, ws, num_blocks, st);
+}
+
+template <typename T>
+hipError_t attn_decode_paged_q8(const T* q, const int8_t* k_codes, const int8_t* v_codes,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int max_blocks,
+                                const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                                int BS, float scale, T* out, const DecodePlan& pl, void* ws,
+                                int num_blocks, hipStream_t st) {
+  return decode_impl<T, int8_t>(q, k_codes, v_codes, k_scale, v_scale, block_table, max_blocks,
+                                context_lens, B, Hq, Hkv, D, BS, scale, out, pl, ws, num_blocks,
+                                st);
+}
+
 template hipError_t attn_decode_paged<bf16>(const bf16*, const bf16*, const bf16*, const int32_t*,
                                             int, const int32_t*, int, int, int, int, int, float,
                                             bf16*, const DecodePlan&, void*, int, hipStream_t);
@@ -365,5 +465,14 @@ template hipError_t attn_decode_paged<float>(const float*, const float*, const f
                                              const int32_t*, int, const int32_t*, int, int, int,
                                              int, int, float, float*, const DecodePlan&, void*,
                                              int, hipStream_t);
+template hipError_t attn_decode_paged_q8<bf16>(const bf16*, const int8_t*, const int8_t*,
+                                               const float*, const float*, const int32_t*, int,
+                                               const int32_t*, int, int, int, int, int, float,
+                                               bf16*, const DecodePlan&, void*, int, hipStream_t);
+template hipError_t attn_decode_paged_q8<float>(const float*, const int8_t*, const int8_t*,
+                                                const float*, const float*, const int32_t*, int,
+                                                const int32_t*, int, int, int, int, int, float,
+                                                float*, const DecodePlan&, void*, int,
+                                                hipStream_t);
 
 }  // namespace dl

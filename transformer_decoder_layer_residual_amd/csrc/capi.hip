@@ -212,8 +212,16 @@ dl_status check_cache(const dl_kv_cache* c) {
   CHECK_PTR(c->k_cache);
   CHECK_PTR(c->v_cache);
   if (c->num_blocks <= 0) return fail(DL_ERR_INVALID_ARG, "cache num_blocks must be positive");
+  if (c->format != DL_KV_LAYER && c->format != DL_KV_INT8)
+    return fail(DL_ERR_INVALID_ARG, "unknown cache format %d", (int)c->format);
+  if (c->format == DL_KV_INT8) {
+    CHECK_IDX(c->k_scale);
+    CHECK_IDX(c->v_scale);
+  }
   return DL_OK;
 }
+
+bool is_q8(const dl_kv_cache* c) { return c->format == DL_KV_INT8; }
 
 // ---- layer bodies ------------------------------------------------------------
 template <typename T>
@@ -247,9 +255,20 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
   const T* wd = static_cast<const T*>(w->w_down);
   T* kc = static_cast<T*>(cache->k_cache);
   T* vc = static_cast<T*>(cache->v_cache);
+  const bool q8 = is_q8(cache);
+  int8_t* kq = static_cast<int8_t*>(cache->k_cache);
+  int8_t* vq = static_cast<int8_t*>(cache->v_cache);
 
   DL_HIP((rmsnorm_residual<float, T>(x, nullptr, nullptr, g1, n1, Tn, H, d->rms_eps, st)), "norm1");
-  if (m == DL_FUSED && is_decode) {
+  if (q8) {
+    // INT8 cache (fused mode only): the projection writes k and v, and the
+    // quantising cache write reduces each row to its codes and scale
+    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, k, v, Tn, H, Hq, Hkv, D,
+                            plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st), "qkv_rope");
+    DL_HIP(reshape_and_cache_q8<T>(k, v, seq, pos, bt, maxblk, kq, vq, cache->k_scale,
+                                   cache->v_scale, Tn, Hkv, D, BS, cache->num_blocks, st),
+           "reshape_and_cache_q8");
+  } else if (m == DL_FUSED && is_decode) {
     // decode: the projection's epilogue writes rotated k and v straight into
     // the paged cache (attention reads them only from there)
     KVSink kv;
@@ -292,7 +311,12 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
       DL_HIP(unf_pv<T>(P, v, cu, B, S_or_ctx, Hq, Hkv, D, attn, st), "pv");
     }
   } else {
-    if (m == DL_FUSED) {
+    if (m == DL_FUSED && q8) {
+      const DecodePlan dp = plan_decode(B, Hq, Hkv, D, S_or_ctx, BS);
+      DL_HIP(attn_decode_paged_q8<T>(q, kq, vq, cache->k_scale, cache->v_scale, bt, maxblk, ctx,
+                                     B, Hq, Hkv, D, BS, scale, attn, dp, at<void>(ws, L, kDec),
+                                     cache->num_blocks, st), "attn_decode_q8");
+    } else if (m == DL_FUSED) {
       const DecodePlan dp = plan_decode(B, Hq, Hkv, D, S_or_ctx, BS);
       DL_HIP(attn_decode_paged<T>(q, kc, vc, bt, maxblk, ctx, B, Hq, Hkv, D, BS, scale, attn, dp,
                                   at<void>(ws, L, kDec), cache->num_blocks, st), "attn_decode");
@@ -346,7 +370,7 @@ const char* dl_status_string(dl_status s) {
 
 const char* dl_last_error(void) { return g_last_error.c_str(); }
 
-int32_t dl_abi_version(void) { return 1; }
+int32_t dl_abi_version(void) { return 2; }
 
 dl_status dl_rope_table_fill(float* cos_sin, int32_t max_pos, int32_t head_dim, double theta,
                              void* stream) {
@@ -438,6 +462,9 @@ dl_status dl_qkv_rope_cache(const void* x, const void* w_q, const void* w_k, con
   if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
   if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
   TRY(check_cache(cache));
+  if (is_q8(cache))
+    return fail(DL_ERR_UNSUPPORTED, "the epilogue cache write takes layer-dtype caches; write an "
+                                    "INT8 cache with dl_qkv_rope + dl_reshape_and_cache");
   if (T == 0) return ok();
   CHECK_PTR(x);
   CHECK_PTR(w_q);
@@ -490,6 +517,15 @@ dl_status dl_reshape_and_cache(const void* k, const void* v, const int32_t* seq_
   CHECK_IDX(positions);
   CHECK_IDX(block_table);
   hipStream_t st = (hipStream_t)stream;
+  if (is_q8(cache)) {
+    int8_t* kq = static_cast<int8_t*>(cache->k_cache);
+    int8_t* vq = static_cast<int8_t*>(cache->v_cache);
+    hipError_t e = dt == DL_BF16
+        ? reshape_and_cache_q8<bf16>((const bf16*)k, (const bf16*)v, seq_of_token, positions, block_table, max_blocks_per_seq, kq, vq, cache->k_scale, cache->v_scale, T, Hkv, D, BS, cache->num_blocks, st)
+        : reshape_and_cache_q8<float>((const float*)k, (const float*)v, seq_of_token, positions, block_table, max_blocks_per_seq, kq, vq, cache->k_scale, cache->v_scale, T, Hkv, D, BS, cache->num_blocks, st);
+    DL_HIP(e, "reshape_and_cache_q8");
+    return ok();
+  }
   hipError_t e = dt == DL_BF16
       ? reshape_and_cache<bf16>((const bf16*)k, (const bf16*)v, seq_of_token, positions, block_table, max_blocks_per_seq, (bf16*)cache->k_cache, (bf16*)cache->v_cache, T, Hkv, D, BS, cache->num_blocks, st)
       : reshape_and_cache<float>((const float*)k, (const float*)v, seq_of_token, positions, block_table, max_blocks_per_seq, (float*)cache->k_cache, (float*)cache->v_cache, T, Hkv, D, BS, cache->num_blocks, st);
@@ -547,6 +583,15 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
     return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
   CHECK_PTR(ws);
   hipStream_t st = (hipStream_t)stream;
+  if (is_q8(cache)) {
+    const int8_t* kq = static_cast<const int8_t*>(cache->k_cache);
+    const int8_t* vq = static_cast<const int8_t*>(cache->v_cache);
+    hipError_t e = dt == DL_BF16
+        ? attn_decode_paged_q8<bf16>((const bf16*)q, kq, vq, cache->k_scale, cache->v_scale, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (bf16*)out, pl, ws, cache->num_blocks, st)
+        : attn_decode_paged_q8<float>((const float*)q, kq, vq, cache->k_scale, cache->v_scale, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (float*)out, pl, ws, cache->num_blocks, st);
+    DL_HIP(e, "attn_decode_paged_q8");
+    return ok();
+  }
   hipError_t e = dt == DL_BF16
       ? attn_decode_paged<bf16>((const bf16*)q, (const bf16*)cache->k_cache, (const bf16*)cache->v_cache, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (bf16*)out, pl, ws, cache->num_blocks, st)
       : attn_decode_paged<float>((const float*)q, (const float*)cache->k_cache, (const float*)cache->v_cache, block_table, max_blocks_per_seq, context_lens, B, Hq, Hkv, D, BS, scale, (float*)out, pl, ws, cache->num_blocks, st);
@@ -714,6 +759,8 @@ dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
   TRY(check_weights(w));
   TRY(check_cache(cache));
   if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (is_q8(cache) && m != DL_FUSED)
+    return fail(DL_ERR_UNSUPPORTED, "INT8 caches run in DL_FUSED mode only");
   if (B < 0 || T < 0 || max_seqlen < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
   if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
   if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
@@ -753,6 +800,8 @@ dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
   TRY(check_weights(w));
   TRY(check_cache(cache));
   if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (is_q8(cache) && m != DL_FUSED)
+    return fail(DL_ERR_UNSUPPORTED, "INT8 caches run in DL_FUSED mode only");
   if (B < 0) return fail(DL_ERR_INVALID_ARG, "B must be >= 0");
   if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
   if (max_context_len <= 0) return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");

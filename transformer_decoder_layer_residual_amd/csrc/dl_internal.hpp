@@ -84,6 +84,13 @@ hipError_t reshape_and_cache(const T* k, const T* v, const int32_t* seq_of_token
                              T* k_cache, T* v_cache, int T_, int Hkv, int D, int BS,
                              int num_blocks, hipStream_t st);
 
+// INT8 cache: codes [num_blocks][Hkv][BS][D], row scales [num_blocks][Hkv][BS].
+template <typename T>
+hipError_t reshape_and_cache_q8(const T* k, const T* v, const int32_t* seq_of_token,
+                                const int32_t* pos, const int32_t* block_table, int max_blocks,
+                                int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
+                                int T_, int Hkv, int D, int BS, int num_blocks, hipStream_t st);
+
 template <typename T>
 hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_seqlens, int B,
                         int max_seqlen, int Hq, int Hkv, int D, float scale, T* out,
@@ -102,6 +109,13 @@ hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                              float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
                              hipStream_t st);
+template <typename T>
+hipError_t attn_decode_paged_q8(const T* q, const int8_t* k_codes, const int8_t* v_codes,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* block_table, int max_blocks,
+                                const int32_t* context_lens, int B, int Hq, int Hkv, int D,
+                                int BS, float scale, T* out, const DecodePlan& pl, void* ws,
+                                int num_blocks, hipStream_t st);
 
 // Kernel-per-op baseline pieces (the unfused chain).
 template <typename T>

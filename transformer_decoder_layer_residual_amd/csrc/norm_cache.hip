@@ -159,6 +159,104 @@ hipError_t reshape_and_cache(const T* k, const T* v, const int32_t* seq_of_token
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Reshape-and-cache into an INT8 cache, quantising each row on the way in
+// (ATB KV-cache page, section "KV cache quantisation": per-token granularity,
+// one fp32 scale for a token's K and one for its V, computed online when the
+// token is written).  A row is one (token, kv head) D-vector of K or of V:
+//   scale = max|x| / 127, code = x / scale rounded half to even, clamped to
+//   [-127, 127], both in fp32; an all-zero row gets scale 0 and zero codes.
+// Codes land where reshape_and_cache would put the values; the scale of a row
+// sits at the same (block, head, slot) of a [num_blocks][Hkv][BS] fp32 array.
+// One group of D / VE lanes (one 16-byte slice each) per (token, kv head);
+// the group's absolute maximum is reduced with lane shuffles.  A group is
+// never split across waves (64 is a multiple of D / VE), and every lane of a
+// group shares its row, so the shuffles only ever pair lanes of one row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t quant4(const float* x, float s) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float r = 0.f;
+    if (s != 0.f) r = fminf(fmaxf(rintf(x[e] / s), -127.f), 127.f);
+    w |= ((uint32_t)(int32_t)r & 0xffu) << (8 * e);
+  }
+  return w;
+}
+
+template <typename T>
+__device__ __forceinline__ void quant_slice(const T* src, int lpr, int8_t* dst, float* sdst,
+                                            bool lead) {
+  constexpr int VE = 16 / sizeof(T);
+  float x[VE];
+  unpack16(ld16(src), x, T());
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  for (int off = 1; off < lpr; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  const float s = amax / 127.0f;
+  if (!dst) return;
+  if constexpr (VE == 8) {
+    u32x2 w = {quant4(x, s), quant4(x + 4, s)};
+    *reinterpret_cast<u32x2*>(dst) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(dst) = quant4(x, s);
+  }
+  if (lead) *sdst = s;
+}
+
+template <typename T>
+__global__ void reshape_and_cache_q8_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                            const int32_t* __restrict__ seq_of_token,
+                                            const int32_t* __restrict__ pos,
+                                            const int32_t* __restrict__ block_table,
+                                            int max_blocks, int8_t* __restrict__ kq,
+                                            int8_t* __restrict__ vq, float* __restrict__ ks,
+                                            float* __restrict__ vs, int T_, int Hkv, int D, int BS,
+                                            int num_blocks) {
+  constexpr int VE = 16 / sizeof(T);
+  const int lpr = D / VE;  // lanes per row, a power of two dividing 64
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rows = (int64_t)T_ * Hkv;
+  const int64_t row = min(idx / lpr, rows - 1);  // the grid's tail repeats the last row
+  const int c = (int)(idx % lpr);
+  const int g = (int)(row % Hkv);
+  const int t = (int)(row / Hkv);
+  const int s = seq_of_token ? seq_of_token[t] : t, p = pos[t];
+  bool keep = idx / lpr < rows && p >= 0 && p / BS < max_blocks;
+  int blk = 0;
+  if (keep) {
+    blk = block_table[(int64_t)s * max_blocks + p / BS];
+    keep = blk >= 0 && blk < num_blocks;
+  }
+  const int64_t drow = ((int64_t)blk * Hkv + g) * BS + (p % BS);
+  const int64_t src = ((int64_t)t * Hkv + g) * D + c * VE;
+  quant_slice(k + src, lpr, keep ? kq + drow * D + c * VE : nullptr, ks + drow, c == 0);
+  quant_slice(v + src, lpr, keep ? vq + drow * D + c * VE : nullptr, vs + drow, c == 0);
+}
+
+template <typename T>
+hipError_t reshape_and_cache_q8(const T* k, const T* v, const int32_t* seq_of_token,
+                                const int32_t* pos, const int32_t* block_table, int max_blocks,
+                                int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale,
+                                int T_, int Hkv, int D, int BS, int num_blocks, hipStream_t st) {
+  const int64_t n = (int64_t)T_ * Hkv * (D / (16 / (int)sizeof(T)));
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL((reshape_and_cache_q8_kernel<T>), dim3((unsigned)((n + 255) / 256)),
+                     dim3(256), 0, st, k, v, seq_of_token, pos, block_table, max_blocks, k_codes,
+                     v_codes, k_scale, v_scale, T_, Hkv, D, BS, num_blocks);
+  return hipGetLastError();
+}
+
+template hipError_t reshape_and_cache_q8<bf16>(const bf16*, const bf16*, const int32_t*,
+                                               const int32_t*, const int32_t*, int, int8_t*,
+                                               int8_t*, float*, float*, int, int, int, int, int,
+                                               hipStream_t);
+template hipError_t reshape_and_cache_q8<float>(const float*, const float*, const int32_t*,
+                                                const int32_t*, const int32_t*, int, int8_t*,
+                                                int8_t*, float*, float*, int, int, int, int, int,
+                                                hipStream_t);
+
 template hipError_t reshape_and_cache<bf16>(const bf16*, const bf16*, const int32_t*,
                                             const int32_t*, const int32_t*, int, bf16*, bf16*,
                                             int, int, int, int, int, hipStream_t);

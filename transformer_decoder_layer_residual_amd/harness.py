@@ -30,9 +30,12 @@ def i32(a):
 
 
 def cache_dev(bits):
+    """Host cache -> device: bf16 / fp32 bit patterns, int8 codes or fp32 scales."""
     if bits.dtype == np.uint16:
         return torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
-    return torch.from_numpy(bits.view(np.float32)).to(DEV)
+    if bits.dtype == np.int8:
+        return torch.from_numpy(np.ascontiguousarray(bits)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.float32)).to(DEV)
 
 
 @dataclasses.dataclass
@@ -55,23 +58,24 @@ class DeviceLayer:
         dl.dl_rope_table_fill(cs, max_pos, cfg.head_dim, cfg.rope_theta)
         return cls(cfg, w_host, w, dims, cs, max_pos)
 
-    # -- fused --------------------------------------------------------------
-    def prefill(self, x, pb, kc, vc, bt_dev, mode=dl.DL_FUSED, ws=None):
+    # -- fused (ks, vs: row scales of an int8 cache) -------------------------
+    def prefill(self, x, pb, kc, vc, bt_dev, mode=dl.DL_FUSED, ws=None, ks=None, vs=None):
         y = torch.empty_like(x)
         dl.dl_layer_prefill(self.dims, self.w, self.cs, x, y, i32(pb.positions),
                             i32(pb.seq_of_token), i32(pb.cu_seqlens), pb.max_seqlen, kc, vc,
-                            bt_dev, mode=mode, ws=ws)
+                            bt_dev, mode=mode, ws=ws, k_scale=ks, v_scale=vs)
         return y
 
-    def decode(self, x, ctx, kc, vc, bt_dev, mode=dl.DL_FUSED, ws=None):
+    def decode(self, x, ctx, kc, vc, bt_dev, mode=dl.DL_FUSED, ws=None, ks=None, vs=None):
         y = torch.empty_like(x)
         ctx = np.asarray(ctx, np.int32)
         dl.dl_layer_decode(self.dims, self.w, self.cs, x, y, i32(ctx - 1), i32(ctx),
-                           int(ctx.max()), kc, vc, bt_dev, mode=mode, ws=ws)
+                           int(ctx.max()), kc, vc, bt_dev, mode=mode, ws=ws, k_scale=ks,
+                           v_scale=vs)
         return y
 
     # -- step by step (exported step entry points) ---------------------------
-    def steps_prefill(self, x, pb, kc, vc, bt_dev, gu_events=None):
+    def steps_prefill(self, x, pb, kc, vc, bt_dev, gu_events=None, ks=None, vs=None):
         c, dt = self.cfg, torch_dtype(self.cfg)
         T, H, Hq, Hkv, D, I = pb.T, c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate
         s = {}
@@ -83,12 +87,13 @@ class DeviceLayer:
         pos = i32(pb.positions)
         dl.dl_qkv_rope(s["n1"], self.w["wq"], self.w["wk"], self.w["wv"], pos, self.cs, s["q"],
                        s["k"], s["v"])
-        dl.dl_reshape_and_cache(s["k"], s["v"], i32(pb.seq_of_token), pos, bt_dev, kc, vc)
+        dl.dl_reshape_and_cache(s["k"], s["v"], i32(pb.seq_of_token), pos, bt_dev, kc, vc,
+                                k_scale=ks, v_scale=vs)
         s["attn"] = torch.empty(T, Hq, D, dtype=dt, device=DEV)
         dl.dl_attn_prefill(s["q"], s["k"], s["v"], i32(pb.cu_seqlens), pb.max_seqlen, s["attn"])
         return self._tail(x, s, T, H, I, dt, gu_events)
 
-    def steps_decode(self, x, ctx, kc, vc, bt_dev):
+    def steps_decode(self, x, ctx, kc, vc, bt_dev, ks=None, vs=None):
         c, dt = self.cfg, torch_dtype(self.cfg)
         B, H, Hq, Hkv, D, I = x.shape[0], c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, \
             c.intermediate
@@ -102,9 +107,10 @@ class DeviceLayer:
         pos = i32(ctx - 1)
         dl.dl_qkv_rope(s["n1"], self.w["wq"], self.w["wk"], self.w["wv"], pos, self.cs, s["q"],
                        s["k"], s["v"])
-        dl.dl_reshape_and_cache(s["k"], s["v"], None, pos, bt_dev, kc, vc)
+        dl.dl_reshape_and_cache(s["k"], s["v"], None, pos, bt_dev, kc, vc, k_scale=ks, v_scale=vs)
         s["attn"] = torch.empty(B, Hq, D, dtype=dt, device=DEV)
-        dl.dl_attn_decode_paged(s["q"], kc, vc, bt_dev, i32(ctx), int(ctx.max()), s["attn"])
+        dl.dl_attn_decode_paged(s["q"], kc, vc, bt_dev, i32(ctx), int(ctx.max()), s["attn"],
+                                k_scale=ks, v_scale=vs)
         return self._tail(x, s, B, H, I, dt)
 
     def _tail(self, x, s, T, H, I, dt, gu_events=None):

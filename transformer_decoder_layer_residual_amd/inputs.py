@@ -17,7 +17,11 @@ Recipe (shapes from the five workload configurations):
     (sequence, logical block) order; unused table entries are -1; every slot
     that is not written holds a NaN sentinel;
   * decode with no prefill of its own (7B and 70B decode): earlier positions
-    hold synthetic K/V ~ N(0, H * 0.02^2), the variance W_k x would have.
+    hold synthetic K/V ~ N(0, H * 0.02^2), the variance W_k x would have;
+  * INT8 caches: codes uniform over the integers -127 .. 127 and row scales
+    uniform in [2.5, 3.5] * sigma / 127 (sigma the K/V spread above), drawn
+    directly; unwritten rows hold code -128 (never a quantiser output) and a
+    NaN scale.
 """
 from __future__ import annotations
 
@@ -30,9 +34,11 @@ import numpy as np
 # tensor ids of the seed sequence
 T_LN1, T_WQ, T_WK, T_WV, T_WO, T_LN2, T_WG, T_WU, T_WD = range(9)
 T_X, T_LENS, T_PERM, T_KCACHE, T_VCACHE, T_CTX, T_MISC = 20, 21, 22, 23, 24, 25, 26
+T_KCODES, T_VCODES, T_KSCALE, T_VSCALE = 27, 28, 29, 30
 
 BF16_SENTINEL = np.uint16(0x7FC1)          # quiet NaN with a payload
 F32_SENTINEL = np.uint32(0x7FC00001)
+CODE_SENTINEL = np.int8(-128)
 
 
 @dataclass(frozen=True)
@@ -287,6 +293,38 @@ def synthetic_cache(cfg: LayerConfig, bt: BlockTable, context_lens, case: int = 
                 phys = bt.table[b, j]
                 cache[phys, :, :ntok, :] = bits[j, :, :ntok, :]
     return kc, vc
+
+
+def empty_cache_q8(cfg: LayerConfig, num_blocks: int):
+    """Sentinel-filled INT8 cache: codes (k, v) [num_blocks, Hkv, BS, D] int8
+    and row scales (k, v) [num_blocks, Hkv, BS] float32."""
+    shape = (num_blocks, cfg.n_kv_heads, cfg.block_size, cfg.head_dim)
+    return (np.full(shape, CODE_SENTINEL, np.int8), np.full(shape, CODE_SENTINEL, np.int8),
+            np.full(shape[:3], np.nan, np.float32), np.full(shape[:3], np.nan, np.float32))
+
+
+def synthetic_cache_q8(cfg: LayerConfig, bt: BlockTable, context_lens, case: int = 0):
+    """INT8 counterpart of synthetic_cache: positions 0 .. ctx-2 of every
+    sequence hold drawn codes and scales, everything else the sentinels."""
+    kq, vq, ks, vs = empty_cache_q8(cfg, bt.num_blocks)
+    BS, Hkv, D = cfg.block_size, cfg.n_kv_heads, cfg.head_dim
+    sigma = float(np.sqrt(cfg.hidden) * 0.02)
+    for b, n in enumerate(np.asarray(context_lens)):
+        prior = int(n) - 1
+        if prior <= 0:
+            continue
+        nblk = (prior + BS - 1) // BS
+        for codes, scales, tc, tsc in ((kq, ks, T_KCODES, T_KSCALE), (vq, vs, T_VCODES, T_VSCALE)):
+            c = rng(cfg.config_id, tc, 1000 * case + b).integers(
+                -127, 128, (nblk, Hkv, BS, D), dtype=np.int16).astype(np.int8)
+            sc = (rng(cfg.config_id, tsc, 1000 * case + b).uniform(2.5, 3.5, (nblk, Hkv, BS))
+                  * (sigma / 127.0)).astype(np.float32)
+            for j in range(nblk):
+                ntok = min(BS, prior - j * BS)
+                phys = bt.table[b, j]
+                codes[phys, :, :ntok] = c[j, :, :ntok]
+                scales[phys, :, :ntok] = sc[j, :, :ntok]
+    return kq, vq, ks, vs
 
 
 def cache_to_f32(bits: np.ndarray) -> np.ndarray:
