@@ -15,6 +15,8 @@ Beside it the JSON line carries:
   decode        one decode step of the same layer shape at batch 64 with
                 context lengths U{128..4096} over a paged cache (tokens/s and
                 the paged attention kernel against HBM peak);
+  decode_kv_int8  the same decode step over an INT8 KV cache with per-token
+                scales (quantised on write, dequantised by the attention);
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill.
 
 Inputs are resident in HBM before the timed region; weights and activations
@@ -77,6 +79,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-int8", action="store_true", help="skip the INT8-cache decode line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="prefix length of the CPU-oracle sample")
@@ -188,15 +191,19 @@ def main():
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ decode
-    if not args.no_decode:
+    def run_decode(int8: bool):
         dcfg = gen.CONFIGS[3]          # same layer shape (and weights) as the prefill
         ctx = gen.decode_context_lens(dcfg)
         B = ctx.size
-        log(f"[bench] generating {dcfg.name} cache (B={B}, mean ctx {ctx.mean():.0f})")
+        kind = "INT8" if int8 else "bf16"
+        log(f"[bench] generating {dcfg.name} {kind} cache (B={B}, mean ctx {ctx.mean():.0f})")
         dbt = gen.block_table(dcfg, ctx)
-        dkb, dvb = gen.synthetic_cache(dcfg, dbt, ctx)
-        dkc, dvc = cache_dev(dkb), cache_dev(dvb)
-        del dkb, dvb
+        host_cache = gen.synthetic_cache_q8(dcfg, dbt, ctx) if int8 else \
+            gen.synthetic_cache(dcfg, dbt, ctx)
+        caches = [cache_dev(a) for a in host_cache]
+        del host_cache
+        kc, vc = caches[0], caches[1]
+        sc = {"k_scale": caches[2], "v_scale": caches[3]} if int8 else {}
         dbtd = i32(dbt.table)
         xd = to_dev(gen.hidden(dcfg, B), torch.float32)
         yd = torch.empty_like(xd)
@@ -206,8 +213,8 @@ def main():
         dws = torch.empty(dws_n, dtype=torch.uint8, device="cuda:0")
 
         def dstep():
-            dl.dl_layer_decode(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, dkc,
-                               dvc, dbtd, mode=mode, ws=dws)
+            dl.dl_layer_decode(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, kc,
+                               vc, dbtd, mode=mode, ws=dws, **sc)
 
         for _ in range(args.warmup):
             dstep()
@@ -220,32 +227,44 @@ def main():
         aws = torch.empty(aws_n, dtype=torch.uint8, device="cuda:0")
 
         def dattn():
-            dl.dl_attn_decode_paged(q, dkc, dvc, dbtd, dctx, max_ctx, ao, ws=aws)
+            dl.dl_attn_decode_paged(q, kc, vc, dbtd, dctx, max_ctx, ao, ws=aws, **sc)
 
         for _ in range(3):
             dattn()
         a_ms = time_launches(dattn, max(args.steps, 20), stream)
-        kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv * D * 2
+        # per cached token and kv head: K and V rows of D elements (+ a 4-byte
+        # scale each for INT8)
+        row_bytes = 2.0 * ((D + 4) if int8 else D * 2)
+        kv_bytes = float(ctx.astype(np.int64).sum()) * Hkv * row_bytes
         a_bytes = kv_bytes + 2.0 * B * Hq * D * 2
         a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
         w_bytes = 2.0 * (H * (Hq + 2 * Hkv) * D + Hq * D * H + 3 * H * I)
         step_bytes = w_bytes + kv_bytes
-        result["decode"] = {
-            "workload": "llama2-7b-layer-decode", "batch": B,
+        out = {
+            "workload": "llama2-7b-layer-decode" + ("-kv-int8" if int8 else ""), "batch": B,
             "context": "uniform 128..4096 (mean %.0f)" % ctx.mean(),
+            "kv_cache": "int8 codes + fp32 per-token scales" if int8 else "bf16",
             "value": round(B / (dms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(dms, 4),
             "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)",
+            "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)"
+                         + (" over INT8 blocks" if int8 else ""),
                          "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(a_gbs / PEAK_HBM_GBS, 4),
-                         "traffic": load_traffic("attn_decode_paged"),
+                         "traffic": load_traffic("attn_decode_paged_int8" if int8
+                                                 else "attn_decode_paged"),
                          "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         }
-        log(f"[bench] decode: {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} tokens/s; attention "
-            f"{a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
-        del dkc, dvc, dws, aws
+        log(f"[bench] decode ({kind} cache): {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} "
+            f"tokens/s; attention {a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
+        del caches, kc, vc, sc, dws, aws
         torch.cuda.empty_cache()
+        return out
+
+    if not args.no_decode:
+        result["decode"] = run_decode(False)
+        if not args.no_int8:
+            result["decode_kv_int8"] = run_decode(True)
 
     # ------------------------------------------------------------ cpu baseline
     if not args.no_cpu_baseline:

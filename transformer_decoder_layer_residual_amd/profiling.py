@@ -39,7 +39,8 @@ WRITE_SCALE = 1.0
 KERNELS = {
     "gemm_gateup_silu_prefill": (r"gemm_pp_kernel.*MapSwiglu",
                                  ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
-    "attn_decode_paged": (r"attn_decode_kernel", ("attn_decode.hip", "dl_common.hpp")),
+    "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16b", ("attn_decode.hip", "dl_common.hpp")),
+    "attn_decode_paged_int8": (r"attn_decode_kernelIDF16ba", ("attn_decode.hip", "dl_common.hpp")),
 }
 
 
