@@ -85,6 +85,8 @@ def _declare(L):
                                    _d, _f32p, _i]
     L.orc_attn_decode_paged.argtypes = [_f32p, _f32p, _f32p, _i32p, _i, _i32p,
                                         _i, _i, _i, _i, _i, _d, _f32p, _i]
+    L.orc_attn_paged_qlens.argtypes = [_f32p, _f32p, _f32p, _i32p, _i, _i32p, _i32p, _i,
+                                       _i, _i, _i, _i, _d, _f32p, _i]
     L.orc_attn_decode_contig.argtypes = [_f32p, _f32p, _f32p, _i, _i32p, _i, _i,
                                          _i, _i, _d, _f32p, _i]
     L.orc_swiglu.argtypes = [_f32p, _f32p, _f32p, _f32p, _i, _i, _i, _i]
@@ -279,6 +281,24 @@ def attn_decode_paged_q8(q, k_codes, v_codes, k_scale, v_scale, block_table,
     lib().orc_attn_decode_paged_q8(_p(q), _p(kq), _p(vq), _p(ks), _p(vs), _p(bt),
                                    bt.shape[1], _p(_ii(context_lens)), B, Hq, Hkv, D,
                                    BS, scale, _p(out), mode)
+    return out
+
+
+def attn_paged_qlens(q, k_cache, v_cache, block_table, cu_q, context_lens, scale=None,
+                     mode=EXACT):
+    """q [Tq, Hq, D] packed by cu_q [B+1]; the new tokens are the last
+    cu_q[b+1]-cu_q[b] of the context_lens[b] cached positions."""
+    q = _f(q)
+    Tq, Hq, D = q.shape
+    kc, vc = _f(k_cache), _f(v_cache)
+    Hkv, BS = kc.shape[1], kc.shape[2]
+    bt = _ii(block_table)
+    cu = _ii(cu_q)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    out = np.empty_like(q)
+    lib().orc_attn_paged_qlens(_p(q), _p(kc), _p(vc), _p(bt), bt.shape[1], _p(cu),
+                               _p(_ii(context_lens)), cu.size - 1, Hq, Hkv, D, BS, scale,
+                               _p(out), mode)
     return out
 
 

@@ -51,6 +51,10 @@
  *   [mlp]    ATB fusion-strategy page (gitcode.csdn.net), section "MLP
  *            fusion": residual add fused into the last dense layer; section
  *            "configuration": LLaMA uses SiLU.
+ *   [spec]   ATB KV-cache page, section "speculative decoding": the paged
+ *            attention verifies K candidate tokens of a sequence in one
+ *            pass, qLens giving each sequence's number of query tokens and
+ *            contextLens its cached length.
  *   [kvquant] ATB KV-cache page (hwcomputing.csdn.net), section "KV cache
  *            quantisation (INT8/INT4 precision-latency trade-off)": at
  *            per-token granularity each token's K and its V carry their own
@@ -65,6 +69,9 @@
  *   GQA kv head = q head div (Hq/Hkv); SwiGLU a = silu(gate) * up;
  *   decode writes the new token to the cache before attending, and
  *   context_lens counts that token;
+ *   several new tokens per sequence (qLens): they are the last q_len
+ *   positions of the cache, written before attending, and each sees the
+ *   positions up to its own (causal among the new tokens, as in prefill);
  *   INT8 KV rows: symmetric (no offset), one scale per (token, kv head) row
  *   of K and of V, scale = max|x| / 127, code = x / scale rounded to the
  *   nearest integer (ties to even) and clamped to [-127, 127], both in fp32
@@ -337,6 +344,46 @@ void orc_attn_decode_paged(const float* q, const float* k_cache,
       free(vals);
       free(sc);
     }
+}
+
+/*
+ * Paged attention for several new query tokens per sequence   [kvpage], [spec]
+ * Sequence b brings q_len_b = cu_q[b+1] - cu_q[b] query rows (packed in q
+ * [Tq][Hq][D]); its cache already holds all ctx_b = context_lens[b]
+ * positions, the new tokens being the last q_len_b of them.  New token i
+ * sits at position p_i = ctx_b - q_len_b + i and attends over the cached
+ * positions 0 .. p_i (the earlier new tokens included, the later ones not).
+ * q_len_b = 1 is the decode step.
+ */
+void orc_attn_paged_qlens(const float* q, const float* k_cache,
+                          const float* v_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* cu_q,
+                          const int32_t* context_lens, int B, int Hq, int Hkv,
+                          int D, int BS, double scale, float* out, int mode) {
+  const int grp = Hq / Hkv;
+  for (int b = 0; b < B; ++b) {
+    const int q0 = cu_q[b], ql = cu_q[b + 1] - cu_q[b];
+    const int first = context_lens[b] - ql; /* position of the first new token */
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int i = 0; i < ql; ++i)
+      for (int h = 0; h < Hq; ++h) {
+        const int g = h / grp, n = first + i + 1;
+        const float** keys = (const float**)malloc(sizeof(float*) * (size_t)n);
+        const float** vals = (const float**)malloc(sizeof(float*) * (size_t)n);
+        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+        for (int j = 0; j < n; ++j) {
+          int blk = block_table[(int64_t)b * max_blocks_per_seq + j / BS];
+          int64_t off = (((int64_t)blk * Hkv + g) * BS + j % BS) * D;
+          keys[j] = k_cache + off;
+          vals[j] = v_cache + off;
+        }
+        attend(q + ((int64_t)(q0 + i) * Hq + h) * D, keys, vals, NULL, NULL, n, D,
+               scale, out + ((int64_t)(q0 + i) * Hq + h) * D, mode, sc);
+        free(keys);
+        free(vals);
+        free(sc);
+      }
+  }
 }
 
 /*

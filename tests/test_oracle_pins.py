@@ -337,6 +337,71 @@ def test_paged_decode_equals_contiguous_under_permutation():
 
 
 # ---------------------------------------------------------------------------
+# paged attention with several new tokens per sequence (qLens)
+# ---------------------------------------------------------------------------
+
+def _paged_from_contiguous(kcont, vcont, ctx, BS, seed):
+    """Scatter contiguous per-sequence K/V ([B][S][Hkv][D]) into a permuted
+    paged pool; returns (k_cache, v_cache, block_table)."""
+    B, _, Hkv, D = kcont.shape
+    nblk = [(c + BS - 1) // BS for c in ctx]
+    pool = sum(nblk) + 5
+    perm = np.random.default_rng(seed).permutation(pool)
+    bt = np.full((B, max(nblk)), -1, np.int32)
+    kc = np.full((pool, Hkv, BS, D), np.nan, np.float32)
+    vc = kc.copy()
+    j = 0
+    for b in range(B):
+        for lb in range(nblk[b]):
+            p = perm[j]
+            j += 1
+            bt[b, lb] = p
+            n = min(BS, ctx[b] - lb * BS)
+            kc[p, :, :n] = kcont[b, lb * BS: lb * BS + n].transpose(1, 0, 2)
+            vc[p, :, :n] = vcont[b, lb * BS: lb * BS + n].transpose(1, 0, 2)
+    return kc, vc, bt
+
+
+def test_paged_qlens_equals_prefill_rows():
+    ctx = [40, 17, 64, 5]
+    qlens = [7, 1, 64, 0]          # verification, decode, whole sequence, nothing new
+    B, Hq, Hkv, D, BS, S = len(ctx), 4, 2, 64, 16, max(ctx)
+    kcont = R.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    vcont = R.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    qfull = R.standard_normal((B, S, Hq, D)).astype(np.float32)
+    kc, vc, bt = _paged_from_contiguous(kcont, vcont, ctx, BS, 3)
+    cu = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = np.concatenate([qfull[b, ctx[b] - qlens[b]: ctx[b]] for b in range(B)])
+    got = oracle.attn_paged_qlens(q, kc, vc, bt, cu, ctx)
+    for b in range(B):
+        n = ctx[b]
+        pre = oracle.attn_prefill(qfull[b, :n], kcont[b, :n], vcont[b, :n], [0, n])
+        assert np.array_equal(got[cu[b]: cu[b + 1]], pre[n - qlens[b]:])
+
+
+def test_paged_qlens_one_token_is_decode_and_causal_within_new_tokens():
+    ctx = np.array([33, 20, 48], np.int32)
+    B, Hq, Hkv, D, BS = 3, 8, 2, 128, 16
+    kcont = R.standard_normal((B, 48, Hkv, D)).astype(np.float32)
+    vcont = R.standard_normal((B, 48, Hkv, D)).astype(np.float32)
+    kc, vc, bt = _paged_from_contiguous(kcont, vcont, ctx, BS, 4)
+    q1 = R.standard_normal((B, Hq, D)).astype(np.float32)
+    got = oracle.attn_paged_qlens(q1, kc, vc, bt, np.arange(B + 1, dtype=np.int32), ctx)
+    assert np.array_equal(got, oracle.attn_decode_paged(q1, kc, vc, bt, ctx))
+    # 5 new tokens in sequence 0: changing a later new token's K/V leaves the
+    # earlier rows alone and changes the later ones
+    q5 = R.standard_normal((5, Hq, D)).astype(np.float32)
+    cu = np.array([0, 5, 5, 5], np.int32)
+    base = oracle.attn_paged_qlens(q5, kc, vc, bt, cu, ctx)
+    blk, slot = bt[0, 31 // BS], 31 % BS           # position 31 = new token 3 of 5
+    kc2 = kc.copy()
+    kc2[blk, :, slot] += 3.0
+    pert = oracle.attn_paged_qlens(q5, kc2, vc, bt, cu, ctx)
+    assert np.array_equal(pert[:3], base[:3])
+    assert not np.allclose(pert[3:], base[3:])
+
+
+# ---------------------------------------------------------------------------
 # INT8 KV cache: per-row quantisation on write, dequantisation in attention
 # ---------------------------------------------------------------------------
 
