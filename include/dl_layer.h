@@ -241,6 +241,32 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
                                void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Paged attention for several new tokens per sequence (ATB KV-cache page,
+ * section "speculative decoding": the paged attention verifies every
+ * sequence's candidate tokens in one pass, with per-sequence query lengths
+ * qLens and context lengths contextLens).  Sequence b brings q_len_b =
+ * cu_q_lens[b+1] - cu_q_lens[b] query tokens (q, out [Tq][Hq][D] packed in
+ * that order, cu_q_lens [B+1] int32 with cu_q_lens[B] == Tq, every q_len_b
+ * <= max_q_len); they are the last q_len_b of its context_lens[b] cached
+ * positions (written before the call), and new token i, at position
+ * context_lens[b] - q_len_b + i, attends over cached positions 0 .. its own
+ * (causal among the new tokens).  q_len 1 everywhere is dl_attn_decode_paged;
+ * q_len = context_lens is a prefill that reads its keys from the cache; a
+ * q_len of 0 is allowed.  Preconditions as for dl_attn_decode_paged, plus
+ * q_len_b <= context_lens[b] <= max_context_len.  Layer-dtype caches only
+ * (an INT8 cache returns DL_ERR_UNSUPPORTED).
+ */
+size_t dl_attn_paged_qlens_workspace_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                                          int32_t D, int32_t max_q_len,
+                                          int32_t max_context_len, int32_t BS);
+dl_status dl_attn_paged_qlens(const void* q, const dl_kv_cache* cache, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                              const int32_t* context_lens, int32_t B, int32_t Tq,
+                              int32_t max_q_len, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t BS, float scale, void* out, dl_dtype dt,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Plain projection out = x W^T (the attention output linear of the chain,
  * exported for step-by-step use).  x [M][K], w [N][K], out [M][N], dtype dt.
  */

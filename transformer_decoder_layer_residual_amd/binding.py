@@ -77,6 +77,11 @@ _SIGS = [
     ("dl_attn_decode_paged", ctypes.c_int, [_vp, ctypes.POINTER(KVCache), _vp, _c_int, _vp,
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             ctypes.c_float, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    ("dl_attn_paged_qlens_workspace_size", _sz, [_c_int] * 8),
+    ("dl_attn_paged_qlens", ctypes.c_int, [_vp, ctypes.POINTER(KVCache), _vp, _c_int, _vp, _vp,
+                                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, ctypes.c_float, _vp, ctypes.c_int,
+                                           _vp, _sz, _vp]),
     ("dl_linear_workspace_size", _sz, [_c_int, _c_int, _c_int, ctypes.c_int]),
     ("dl_linear", ctypes.c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, ctypes.c_int, _vp, _sz,
                                  _vp]),
@@ -250,6 +255,24 @@ def dl_attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_con
     _check(L.dl_attn_decode_paged(_p(q), ctypes.byref(c), _p(block_table), block_table.shape[1],
                                   _p(context_lens), max_context_len, B, Hq, Hkv, D, BS, scale,
                                   _p(out), dtype_code(q.dtype), _p(ws), nb, _stream()))
+
+
+def dl_attn_paged_qlens(q, k_cache, v_cache, block_table, cu_q_lens, context_lens,
+                        max_q_len: int, max_context_len: int, out, scale=None, ws=None):
+    """q, out [Tq, Hq, D] packed by cu_q_lens [B+1]; the new tokens are the
+    last q_len of each sequence's context_lens cached positions."""
+    Tq, Hq, D = q.shape
+    Hkv, BS = k_cache.shape[1], k_cache.shape[2]
+    B = cu_q_lens.shape[0] - 1
+    scale = D ** -0.5 if scale is None else scale
+    L = lib()
+    ws, nb = _ws(L.dl_attn_paged_qlens_workspace_size(B, Tq, Hq, Hkv, D, max_q_len,
+                                                      max_context_len, BS), ws, q.device)
+    c = _cache(k_cache, v_cache)
+    _check(L.dl_attn_paged_qlens(_p(q), ctypes.byref(c), _p(block_table), block_table.shape[1],
+                                 _p(cu_q_lens), _p(context_lens), B, Tq, max_q_len,
+                                 max_context_len, Hq, Hkv, D, BS, scale, _p(out),
+                                 dtype_code(q.dtype), _p(ws), nb, _stream()))
 
 
 def dl_linear(x, w, out, ws=None):

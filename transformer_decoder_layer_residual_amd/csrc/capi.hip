@@ -599,6 +599,51 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
   return ok();
 }
 
+size_t dl_attn_paged_qlens_workspace_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                                          int32_t D, int32_t max_q_len,
+                                          int32_t max_context_len, int32_t BS) {
+  if (B <= 0 || Tq <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || max_q_len <= 0 ||
+      max_context_len <= 0 || Hq % Hkv)
+    return 0;
+  return plan_paged(B, Hq, Hkv, max_q_len, max_context_len, BS, D, Tq).ws_bytes;
+}
+
+dl_status dl_attn_paged_qlens(const void* q, const dl_kv_cache* cache, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                              const int32_t* context_lens, int32_t B, int32_t Tq,
+                              int32_t max_q_len, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t BS, float scale, void* out, dl_dtype dt,
+                              void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_dtype(dt));
+  TRY(check_heads(Hq, Hkv, D));
+  TRY(check_bs(BS));
+  if (B < 0 || Tq < 0 || max_q_len < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
+  if (max_context_len <= 0) return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");
+  if (max_q_len > max_context_len) return fail(DL_ERR_INVALID_ARG, "max_q_len exceeds max_context_len");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * BS < max_context_len)
+    return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq * BS must cover max_context_len");
+  TRY(check_cache(cache));
+  if (is_q8(cache)) return fail(DL_ERR_UNSUPPORTED, "q_len > 1 paged attention takes layer-dtype caches");
+  if (B == 0 || Tq == 0 || max_q_len == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(out);
+  CHECK_IDX(block_table);
+  CHECK_IDX(cu_q_lens);
+  CHECK_IDX(context_lens);
+  const PagedPlan pl = plan_paged(B, Hq, Hkv, max_q_len, max_context_len, BS, D, Tq);
+  if ((int64_t)B * pl.max_qt * pl.max_sp * Hkv > 0x7fffffff)
+    return fail(DL_ERR_UNSUPPORTED, "grid too large");
+  if (!ws || ws_bytes < pl.ws_bytes)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
+  CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dt == DL_BF16
+      ? attn_paged_qlens<bf16>((const bf16*)q, (const bf16*)cache->k_cache, (const bf16*)cache->v_cache, block_table, max_blocks_per_seq, cu_q_lens, context_lens, B, Tq, Hq, Hkv, D, BS, max_context_len, scale, (bf16*)out, pl, ws, cache->num_blocks, st)
+      : attn_paged_qlens<float>((const float*)q, (const float*)cache->k_cache, (const float*)cache->v_cache, block_table, max_blocks_per_seq, cu_q_lens, context_lens, B, Tq, Hq, Hkv, D, BS, max_context_len, scale, (float*)out, pl, ws, cache->num_blocks, st);
+  DL_HIP(e, "attn_paged_qlens");
+  return ok();
+}
+
 size_t dl_linear_workspace_size(int32_t M, int32_t N, int32_t K, dl_dtype dt) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return plan_lin(M, N, K, dt).ws_bytes;

@@ -117,6 +117,23 @@ hipError_t attn_decode_paged_q8(const T* q, const int8_t* k_codes, const int8_t*
                                 int BS, float scale, T* out, const DecodePlan& pl, void* ws,
                                 int num_blocks, hipStream_t st);
 
+// Paged attention for q_len >= 1 new tokens per sequence.
+struct PagedPlan {
+  int qb;         // query tokens per workgroup tile (128 rows / group size)
+  int max_qt;     // query tiles per sequence at max_q_len
+  int ck;         // keys per split
+  int max_sp;     // splits per sequence at max_context_len
+  size_t ws_bytes;
+};
+PagedPlan plan_paged(int B, int Hq, int Hkv, int max_q_len, int max_context_len, int BS, int D,
+                     int Tq);
+template <typename T>
+hipError_t attn_paged_qlens(const T* q, const T* k_cache, const T* v_cache,
+                            const int32_t* block_table, int max_blocks, const int32_t* cu_q,
+                            const int32_t* context_lens, int B, int Tq, int Hq, int Hkv, int D,
+                            int BS, int max_context_len, float scale, T* out, const PagedPlan& pl,
+                            void* ws, int num_blocks, hipStream_t st);
+
 // Kernel-per-op baseline pieces (the unfused chain).
 template <typename T>
 hipError_t unf_rope(T* u, const int32_t* pos, const float* cos_sin, int max_pos, int T_, int nh,
