@@ -110,6 +110,9 @@ def _declare(L):
     L.orc_layer_decode_q8.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
                                       _f32p, _f32p, _f32p, _i32p, _i, _i8p, _i8p,
                                       _f32p, _f32p, _i32p, _i, _i]
+    L.orc_layer_decode_qlens.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
+                                         _f32p, _f32p, _f32p, _i32p, _i32p, _i32p, _i32p, _i,
+                                         _i, _f32p, _f32p, _i32p, _i, _i]
     L.orc_kv_cache_bytes.argtypes = [_i, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, _i]
     L.orc_kv_cache_bytes.restype = _d
@@ -391,6 +394,27 @@ def layer_decode(dims, weights, x, context_lens, k_cache, v_cache, block_table,
     lib().orc_layer_decode(ctypes.byref(d), ctypes.byref(w), _p(x), _p(y), _p(h),
                            _p(_ii(context_lens)), B, _p(k_cache), _p(v_cache), _p(bt),
                            bt.shape[1], mode)
+    del keep
+    return y, h
+
+
+def layer_decode_qlens(dims, weights, x, pos, seq_of_token, cu_q, context_lens, k_cache,
+                       v_cache, block_table, mode=EXACT):
+    """New tokens (packed by cu_q) appended to cached sequences; caches
+    (float32) updated in place.  Returns (y, h)."""
+    d, w, keep = _pack(dims, weights)
+    x = _f(x)
+    T, H = x.shape
+    y = np.empty_like(x)
+    h = np.empty_like(x)
+    cu = _ii(cu_q)
+    bt = _ii(block_table)
+    assert k_cache.dtype == np.float32 and k_cache.flags.c_contiguous
+    assert v_cache.dtype == np.float32 and v_cache.flags.c_contiguous
+    lib().orc_layer_decode_qlens(ctypes.byref(d), ctypes.byref(w), _p(x), _p(y), _p(h),
+                                 _p(_ii(pos)), _p(_ii(seq_of_token)), _p(cu),
+                                 _p(_ii(context_lens)), cu.size - 1, T, _p(k_cache),
+                                 _p(v_cache), _p(bt), bt.shape[1], mode)
     del keep
     return y, h
 

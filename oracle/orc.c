@@ -719,6 +719,42 @@ void orc_layer_decode(const orc_dims* d, const orc_weights* w, const float* x,
                max_blocks_per_seq, mode);
 }
 
+/*
+ * A step that brings q_len_b new tokens to every sequence (speculative
+ * verification, or a chunk of a prefill over a cached prefix)   [spec]
+ * x, y [T][H] packed by cu_q; pos [T] = context_lens[b] - q_len_b + i;
+ * seq_of_token [T].  The new tokens' K/V are written to the cache first;
+ * attention is orc_attn_paged_qlens over the cache.
+ */
+void orc_layer_decode_qlens(const orc_dims* d, const orc_weights* w, const float* x,
+                            float* y, float* h_out, const int32_t* pos,
+                            const int32_t* seq_of_token, const int32_t* cu_q,
+                            const int32_t* context_lens, int B, int T,
+                            float* k_cache, float* v_cache,
+                            const int32_t* block_table, int max_blocks_per_seq,
+                            int mode) {
+  const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim;
+  float* n1 = (float*)malloc(sizeof(float) * (size_t)T * H);
+  float* q = (float*)malloc(sizeof(float) * (size_t)T * Hq * D);
+  float* k = (float*)malloc(sizeof(float) * (size_t)T * Hkv * D);
+  float* v = (float*)malloc(sizeof(float) * (size_t)T * Hkv * D);
+  float* attn = (float*)malloc(sizeof(float) * (size_t)T * Hq * D);
+  orc_rmsnorm(x, NULL, NULL, w->ln1, n1, T, H, d->rms_eps, mode);
+  orc_qkv_rope(n1, w->wq, w->wk, w->wv, pos, d->rope_theta, q, k, v, T, H, Hq,
+               Hkv, D, mode);
+  orc_reshape_and_cache(k, v, seq_of_token, pos, block_table, max_blocks_per_seq,
+                        k_cache, v_cache, T, Hkv, D, d->block_size);
+  orc_attn_paged_qlens(q, k_cache, v_cache, block_table, max_blocks_per_seq, cu_q,
+                       context_lens, B, Hq, Hkv, D, d->block_size,
+                       1.0 / sqrt((double)D), attn, mode);
+  layer_tail(d, w, x, attn, y, h_out, T, mode);
+  free(n1);
+  free(q);
+  free(k);
+  free(v);
+  free(attn);
+}
+
 /* INT8 cache: codes [num_blocks][Hkv][BS][D], scales [num_blocks][Hkv][BS]. */
 void orc_layer_prefill_q8(const orc_dims* d, const orc_weights* w, const float* x,
                           float* y, float* h_out, const int32_t* pos,

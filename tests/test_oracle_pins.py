@@ -646,6 +646,34 @@ def test_decode_after_prefill_equals_prefill_row():
     np.testing.assert_allclose(yd[0], yp[n], rtol=1e-6, atol=1e-6)
 
 
+def test_layer_qlens_step_equals_prefill_rows():
+    # prefill n0 tokens of each sequence, then bring the rest as new tokens:
+    # the new rows equal the rows of a single prefill over the whole sequences
+    cfg, gen, w = _tiny()
+    d = cfg.dims()
+    full, head = [30, 9, 20], [26, 8, 13]
+    qlens = [a - b for a, b in zip(full, head)]
+    pf = gen.packed(full)
+    x = gen.hidden(cfg, pf.T)
+    y_full, _ = oracle.layer_prefill(d, w, x, pf.positions, pf.seq_of_token, pf.cu_seqlens)
+    bt = gen.block_table(cfg, full)
+    kc = np.full((bt.num_blocks, 4, 16, 64), np.nan, np.float32)
+    vc = kc.copy()
+    rows_head = np.concatenate([np.arange(pf.cu_seqlens[b], pf.cu_seqlens[b] + head[b])
+                                for b in range(3)])
+    rows_new = np.concatenate([np.arange(pf.cu_seqlens[b] + head[b], pf.cu_seqlens[b + 1])
+                               for b in range(3)])
+    ph = gen.packed(head)
+    oracle.layer_prefill(d, w, x[rows_head], ph.positions, ph.seq_of_token, ph.cu_seqlens, kc,
+                         vc, bt.table)
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    seq = np.repeat(np.arange(3, dtype=np.int32), qlens)
+    pos = pf.positions[rows_new]
+    y_new, _ = oracle.layer_decode_qlens(d, w, x[rows_new], pos, seq, cu_q,
+                                         np.array(full, np.int32), kc, vc, bt.table)
+    assert np.array_equal(y_new, y_full[rows_new])
+
+
 def _q8_cache(nb, Hkv=4, BS=16, D=64):
     return (np.full((nb, Hkv, BS, D), -128, np.int8), np.full((nb, Hkv, BS, D), -128, np.int8),
             np.full((nb, Hkv, BS), np.nan, np.float32), np.full((nb, Hkv, BS), np.nan, np.float32))
