@@ -342,6 +342,35 @@ dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
                           int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
                           void* stream);
 
+/*
+ * One step that brings q_len_b new tokens to each of B cached sequences:
+ * speculative verification of candidate tokens, or a chunk of a prefill over
+ * a cached prefix (ATB KV-cache page, section "speculative decoding": the
+ * target model's layers run the candidates of all sequences in one pass with
+ * PagedAttention given qLens and contextLens).
+ *   hidden_in [T][H] fp32 -> hidden_out [T][H] fp32 (must not alias), T =
+ *   sum of q_len_b, packed by cu_q_lens [B+1]; seq_of_token [T];
+ *   positions [T] = context_lens[b] - q_len_b + i for new token i;
+ *   context_lens [B] count the new tokens.
+ * The new K/V are written to the cache first; attention is
+ * dl_attn_paged_qlens over the cache; the rest is the prefill layer.
+ * DL_FUSED and layer-dtype caches only.  Workspace from
+ * dl_layer_decode_qlens_workspace_size (T <= max_tokens, B <= max_batch,
+ * q_len_b <= max_q_len, context_lens <= max_context_len).
+ */
+size_t dl_layer_decode_qlens_workspace_size(const dl_layer_dims* d, int32_t max_tokens,
+                                            int32_t max_batch, int32_t max_q_len,
+                                            int32_t max_context_len);
+dl_status dl_layer_decode_qlens(const dl_layer_dims* d, const dl_layer_weights* w,
+                                const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                                float* hidden_out, const int32_t* positions,
+                                const int32_t* seq_of_token, const int32_t* cu_q_lens,
+                                const int32_t* context_lens, int32_t B, int32_t T,
+                                int32_t max_q_len, int32_t max_context_len,
+                                const dl_kv_cache* cache, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,13 @@ _SIGS = [
                                        _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                        ctypes.POINTER(KVCache), _vp, _c_int, ctypes.c_int, _vp,
                                        _sz, _vp]),
+    ("dl_layer_decode_qlens_workspace_size", _sz, [ctypes.POINTER(LayerDims), _c_int, _c_int,
+                                                   _c_int, _c_int]),
+    ("dl_layer_decode_qlens", ctypes.c_int, [ctypes.POINTER(LayerDims),
+                                             ctypes.POINTER(LayerWeights), _vp, _c_int, _vp, _vp,
+                                             _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                             ctypes.POINTER(KVCache), _vp, _c_int, ctypes.c_int,
+                                             _vp, _sz, _vp]),
 ]
 
 EXPORTED = tuple(n for n, _, _ in _SIGS)
@@ -370,3 +377,23 @@ def dl_layer_decode(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_o
                              max_context_len, B, ctypes.byref(c), _p(block_table),
                              block_table.shape[1], mode, _p(ws), ws.numel() * ws.element_size(),
                              _stream()))
+
+
+def dl_layer_decode_qlens(dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_out,
+                          positions, seq_of_token, cu_q_lens, context_lens, max_q_len: int,
+                          max_context_len: int, k_cache, v_cache, block_table, ws=None):
+    T = hidden_in.shape[0]
+    B = cu_q_lens.shape[0] - 1
+    L = lib()
+    if ws is None:
+        n = L.dl_layer_decode_qlens_workspace_size(ctypes.byref(dims), T, B, max_q_len,
+                                                   max_context_len)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=hidden_in.device)
+    wts = make_weights(weights)
+    c = _cache(k_cache, v_cache)
+    _check(L.dl_layer_decode_qlens(ctypes.byref(dims), ctypes.byref(wts), _p(cos_sin),
+                                   cos_sin.shape[0], _p(hidden_in), _p(hidden_out), _p(positions),
+                                   _p(seq_of_token), _p(cu_q_lens), _p(context_lens), B, T,
+                                   max_q_len, max_context_len, ctypes.byref(c), _p(block_table),
+                                   block_table.shape[1], DL_FUSED, _p(ws),
+                                   ws.numel() * ws.element_size(), _stream()))

@@ -137,9 +137,11 @@ size_t part_bytes(const dl_layer_dims* d, int M, dl_mode m) {
   return p;
 }
 
-// is_decode: T = B tokens, S_or_ctx = max context; else S_or_ctx = max_seqlen
+// is_decode: T = B tokens, S_or_ctx = max context; else S_or_ctx = max_seqlen.
+// max_q_len > 0: a step with several new tokens per sequence (S_or_ctx = max
+// context), whose attention partials take the decode slot.
 Layout layout(const dl_layer_dims* d, int T, int B, int S_or_ctx, bool is_decode, dl_mode m,
-              size_t part) {
+              size_t part, int max_q_len = 0) {
   const size_t es = esize(d->dtype);
   const size_t H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
                I = d->intermediate;
@@ -157,6 +159,9 @@ Layout layout(const dl_layer_dims* d, int T, int B, int S_or_ctx, bool is_decode
   L.size[kDec] = is_decode && m == DL_FUSED
                      ? plan_decode(B, (int)Hq, (int)Hkv, (int)D, S_or_ctx, d->block_size).ws_bytes
                      : 0;
+  if (max_q_len > 0)
+    L.size[kDec] = plan_paged(B, (int)Hq, (int)Hkv, max_q_len, S_or_ctx, d->block_size, (int)D, T)
+                       .ws_bytes;
   if (m == DL_UNFUSED) {
     const size_t rows = is_decode ? (size_t)B * Hq : (size_t)B * Hq * S_or_ctx;
     L.size[kS] = rows * S_or_ctx * 4;
@@ -224,12 +229,14 @@ dl_status check_cache(const dl_kv_cache* c) {
 bool is_q8(const dl_kv_cache* c) { return c->format == DL_KV_INT8; }
 
 // ---- layer bodies ------------------------------------------------------------
+// max_q_len > 0: new tokens appended to cached sequences (cu = cu_q_lens,
+// ctx = context lengths, S_or_ctx = max context); attention reads the cache.
 template <typename T>
 dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const float* cs,
                      int max_pos, const float* x, float* y, const int32_t* pos, const int32_t* seq,
                      const int32_t* cu, const int32_t* ctx, int B, int Tn, int S_or_ctx,
                      bool is_decode, const dl_kv_cache* cache, const int32_t* bt, int maxblk,
-                     dl_mode m, void* ws, const Layout& L, hipStream_t st) {
+                     dl_mode m, void* ws, const Layout& L, hipStream_t st, int max_q_len = 0) {
   const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
             I = d->intermediate, BS = d->block_size;
   const dl_dtype dt = d->dtype;
@@ -300,7 +307,12 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
     DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
                                 cache->num_blocks, st), "reshape_and_cache");
   }
-  if (!is_decode) {
+  if (max_q_len > 0) {
+    const PagedPlan pp = plan_paged(B, Hq, Hkv, max_q_len, S_or_ctx, BS, D, Tn);
+    DL_HIP(attn_paged_qlens<T>(q, kc, vc, bt, maxblk, cu, ctx, B, Tn, Hq, Hkv, D, BS, S_or_ctx,
+                               scale, attn, pp, at<void>(ws, L, kDec), cache->num_blocks, st),
+           "attn_paged_qlens");
+  } else if (!is_decode) {
     if (m == DL_FUSED) {
       DL_HIP(attn_prefill<T>(q, k, v, cu, B, S_or_ctx, Hq, Hkv, D, scale, attn, st), "attn_prefill");
     } else {
@@ -832,6 +844,69 @@ dl_status dl_layer_prefill(const dl_layer_dims* d, const dl_layer_weights* w,
   return layer_body<float>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, seq_of_token,
                            cu_seqlens, nullptr, B, T, max_seqlen, false, cache, block_table,
                            max_blocks_per_seq, m, ws, L, st);
+}
+
+size_t dl_layer_decode_qlens_workspace_size(const dl_layer_dims* d, int32_t max_tokens,
+                                            int32_t max_batch, int32_t max_q_len,
+                                            int32_t max_context_len) {
+  if (check_dims(d) != DL_OK || max_tokens <= 0 || max_batch <= 0 || max_q_len <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  size_t part = 0;
+  for (int M = 1; M <= std::min(max_tokens, 512); ++M)
+    part = std::max(part, part_bytes(d, M, DL_FUSED));
+  part = std::max(part, part_bytes(d, max_tokens, DL_FUSED));
+  return layout(d, max_tokens, max_batch, max_context_len, false, DL_FUSED, part, max_q_len).total;
+}
+
+dl_status dl_layer_decode_qlens(const dl_layer_dims* d, const dl_layer_weights* w,
+                                const float* cos_sin, int32_t max_pos, const float* hidden_in,
+                                float* hidden_out, const int32_t* positions,
+                                const int32_t* seq_of_token, const int32_t* cu_q_lens,
+                                const int32_t* context_lens, int32_t B, int32_t T,
+                                int32_t max_q_len, int32_t max_context_len,
+                                const dl_kv_cache* cache, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
+                                void* stream) {
+  TRY(check_dims(d));
+  TRY(check_weights(w));
+  TRY(check_cache(cache));
+  if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (m != DL_FUSED) return fail(DL_ERR_UNSUPPORTED, "q_len > 1 steps run in DL_FUSED mode only");
+  if (is_q8(cache)) return fail(DL_ERR_UNSUPPORTED, "q_len > 1 steps take layer-dtype caches");
+  if (B < 0 || T < 0 || max_q_len < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
+  if (max_pos <= 0) return fail(DL_ERR_INVALID_ARG, "max_pos must be positive");
+  if (max_context_len <= 0) return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");
+  if (max_q_len > max_context_len) return fail(DL_ERR_INVALID_ARG, "max_q_len exceeds max_context_len");
+  if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * d->block_size < max_context_len)
+    return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq * BS must cover max_context_len");
+  if (T == 0 || B == 0 || max_q_len == 0) return ok();
+  CHECK_PTR(cos_sin);
+  CHECK_PTR(hidden_in);
+  CHECK_PTR(hidden_out);
+  if (hidden_in == hidden_out) return fail(DL_ERR_INVALID_ARG, "hidden_out must not alias hidden_in");
+  CHECK_IDX(positions);
+  CHECK_IDX(seq_of_token);
+  CHECK_IDX(cu_q_lens);
+  CHECK_IDX(context_lens);
+  CHECK_IDX(block_table);
+  const PagedPlan pp = plan_paged(B, d->n_q_heads, d->n_kv_heads, max_q_len, max_context_len,
+                                  d->block_size, d->head_dim, T);
+  if ((int64_t)B * pp.max_qt * pp.max_sp * d->n_kv_heads > 0x7fffffff)
+    return fail(DL_ERR_UNSUPPORTED, "grid too large");
+  const size_t part = part_bytes(d, T, m);
+  const Layout L = layout(d, T, B, max_context_len, false, m, part, max_q_len);
+  if (!ws || ws_bytes < L.total)
+    return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, L.total);
+  CHECK_PTR(ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (d->dtype == DL_BF16)
+    return layer_body<bf16>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, seq_of_token,
+                            cu_q_lens, context_lens, B, T, max_context_len, false, cache,
+                            block_table, max_blocks_per_seq, m, ws, L, st, max_q_len);
+  return layer_body<float>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, seq_of_token,
+                           cu_q_lens, context_lens, B, T, max_context_len, false, cache,
+                           block_table, max_blocks_per_seq, m, ws, L, st, max_q_len);
 }
 
 dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,

@@ -74,6 +74,18 @@ class DeviceLayer:
                            v_scale=vs)
         return y
 
+    def decode_qlens(self, x, qb, ctx, kc, vc, bt_dev, ws=None):
+        """New tokens appended to cached sequences: qb is the packed batch of
+        the new tokens (lens = q_len per sequence), ctx the context lengths
+        after the step."""
+        y = torch.empty_like(x)
+        ctx = np.asarray(ctx, np.int32)
+        pos = (np.repeat(ctx - qb.lens, qb.lens) + qb.positions).astype(np.int32)
+        dl.dl_layer_decode_qlens(self.dims, self.w, self.cs, x, y, i32(pos), i32(qb.seq_of_token),
+                                 i32(qb.cu_seqlens), i32(ctx), qb.max_seqlen, int(ctx.max()), kc,
+                                 vc, bt_dev, ws=ws)
+        return y
+
     # -- step by step (exported step entry points) ---------------------------
     def steps_prefill(self, x, pb, kc, vc, bt_dev, gu_events=None, ks=None, vs=None):
         c, dt = self.cfg, torch_dtype(self.cfg)
