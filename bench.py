@@ -17,6 +17,8 @@ Beside it the JSON line carries:
                 the paged attention kernel against HBM peak);
   decode_kv_int8  the same decode step over an INT8 KV cache with per-token
                 scales (quantised on write, dequantised by the attention);
+  verify_qlen4  the same batch verifying 4 candidate tokens per sequence in
+                one layer step (paged attention with per-sequence q_len);
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill.
 
 Inputs are resident in HBM before the timed region; weights and activations
@@ -80,6 +82,7 @@ def main():
     ap.add_argument("--mode", choices=["fused", "unfused"], default="fused")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-int8", action="store_true", help="skip the INT8-cache decode line")
+    ap.add_argument("--no-verify", action="store_true", help="skip the q_len 4 verification line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="prefix length of the CPU-oracle sample")
@@ -261,10 +264,72 @@ def main():
         torch.cuda.empty_cache()
         return out
 
+    # ------------------------------------------- verification step (q_len > 1)
+    def run_verify(qlen: int):
+        """Every sequence of the decode workload verifies qlen candidate tokens
+        in one layer step (attention over the paged cache with per-sequence
+        query lengths)."""
+        dcfg = gen.CONFIGS[3]
+        ctx = gen.decode_context_lens(dcfg)   # context lengths after the step
+        B = ctx.size
+        log(f"[bench] generating {dcfg.name} cache for {qlen}-token verification")
+        dbt = gen.block_table(dcfg, ctx)
+        kb, vb = gen.synthetic_cache(dcfg, dbt, ctx - (qlen - 1))   # positions before the step
+        kc, vc = cache_dev(kb), cache_dev(vb)
+        del kb, vb
+        qb = gen.packed(np.full(B, qlen, np.int32))
+        T = qb.T
+        xq = to_dev(gen.hidden(dcfg, T, step=3), torch.float32)
+        dbtd = i32(dbt.table)
+        vws_n = dl.lib().dl_layer_decode_qlens_workspace_size(layer.dims, T, B, qlen,
+                                                              int(ctx.max()))
+        vws = torch.empty(vws_n, dtype=torch.uint8, device="cuda:0")
+
+        def vstep():
+            layer.decode_qlens(xq, qb, ctx, kc, vc, dbtd, ws=vws)
+
+        for _ in range(args.warmup):
+            vstep()
+        torch.cuda.synchronize()
+        vms = time_launches(vstep, args.steps, stream)
+        q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device="cuda:0").normal_()
+        ao = torch.empty_like(q)
+        cu, dctx = i32(qb.cu_seqlens), i32(ctx)
+        aws_n = dl.lib().dl_attn_paged_qlens_workspace_size(B, T, Hq, Hkv, D, qlen, int(ctx.max()),
+                                                            dcfg.block_size)
+        aws = torch.empty(aws_n, dtype=torch.uint8, device="cuda:0")
+
+        def vattn():
+            dl.dl_attn_paged_qlens(q, kc, vc, dbtd, cu, dctx, qlen, int(ctx.max()), ao, ws=aws)
+
+        for _ in range(3):
+            vattn()
+        a_ms = time_launches(vattn, max(args.steps, 20), stream)
+        kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv * D * 2
+        a_bytes = kv_bytes + 2.0 * T * Hq * D * 2
+        a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+        out = {
+            "workload": "llama2-7b-layer-verify-%d" % qlen, "batch": B, "q_len": qlen,
+            "context": "uniform 128..4096 (mean %.0f) after the step" % ctx.mean(),
+            "value": round(T / (vms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(vms, 4),
+            "roofline": {"bound": "hbm", "kernel": "paged attention, q_len %d (split-KV + combine)"
+                         % qlen, "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
+        }
+        log(f"[bench] verify q_len {qlen}: {vms:.3f} ms/step, {T / (vms * 1e-3):,.0f} tokens/s; "
+            f"attention {a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
+        del kc, vc, vws, aws
+        torch.cuda.empty_cache()
+        return out
+
     if not args.no_decode:
         result["decode"] = run_decode(False)
         if not args.no_int8:
             result["decode_kv_int8"] = run_decode(True)
+        if not args.no_verify:
+            result["verify_qlen4"] = run_verify(4)
 
     # ------------------------------------------------------------ cpu baseline
     if not args.no_cpu_baseline:
