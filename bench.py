@@ -19,6 +19,10 @@ Beside it the JSON line carries:
                 scales (quantised on write, dequantised by the attention);
   verify_qlen4  the same batch verifying 4 candidate tokens per sequence in
                 one layer step (paged attention with per-sequence q_len);
+  decode_small_batch  the Llama-3-8B-shaped layer at B8, eager calls against
+                the step replayed as one HIP graph, back to back and with a
+                host synchronisation after every step (decode lines above also
+                carry their graph timing);
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill.
 
 Inputs are resident in HBM before the timed region; weights and activations
@@ -60,6 +64,17 @@ def load_traffic(kernel_key: str):
     if not rec or rec.get("source_sha") != profiling.source_sha(*srcs):
         return None
     return rec.get("bytes_per_launch")
+
+
+def time_synced(fn, n, stream):
+    """Wall time of n steps that each end with a host synchronisation (the
+    serving-loop pattern, where host launch latency is not hidden)."""
+    stream.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+        stream.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / n
 
 
 def time_launches(fn, n, stream):
@@ -223,6 +238,17 @@ def main():
             dstep()
         torch.cuda.synchronize()
         dms = time_launches(dstep, args.steps, stream)
+        # the same step replayed as one HIP graph (dl_layer_decode_graph_create)
+        side = torch.cuda.Stream()
+        graph = dl.DecodeGraph(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, kc, vc,
+                               dbtd, side, ws=dws,
+                               **({"k_scale": sc["k_scale"], "v_scale": sc["v_scale"]} if int8
+                                  else {}))
+        for _ in range(args.warmup):
+            graph.launch()
+        side.synchronize()
+        gms = time_launches(graph.launch, args.steps, side)
+        graph.close()
         # dominant kernel: paged decode attention (split + combine)
         q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda:0").normal_()
         ao = torch.empty_like(q)
@@ -249,6 +275,8 @@ def main():
             "kv_cache": "int8 codes + fp32 per-token scales" if int8 else "bf16",
             "value": round(B / (dms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(dms, 4),
+            "graph_ms_per_step": round(gms, 4),
+            "graph_tokens_per_s": round(B / (gms * 1e-3), 1),
             "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)"
                          + (" over INT8 blocks" if int8 else ""),
@@ -259,7 +287,7 @@ def main():
                          "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         }
         log(f"[bench] decode ({kind} cache): {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} "
-            f"tokens/s; attention {a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
+            f"tokens/s (graph {gms:.3f} ms); attention {a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
         del caches, kc, vc, sc, dws, aws
         torch.cuda.empty_cache()
         return out
@@ -324,7 +352,66 @@ def main():
         torch.cuda.empty_cache()
         return out
 
+    # --------------------------------- small-batch GQA decode, eager vs graph
+    def run_small_decode():
+        """Llama-3-8B-shaped layer (random weights), B8 at the contexts its own
+        workload reaches after prefill (U{256..1024} + 64): a step of ~80 us
+        where host launch gaps show."""
+        c4 = gen.CONFIGS[4]
+        lay = DeviceLayer.build(c4, max_pos=1200)
+        ctx = (gen.prefill_batch(c4).lens + 64).astype(np.int32)
+        B4 = ctx.size
+        bt4 = gen.block_table(c4, ctx)
+        kb, vb = gen.synthetic_cache(c4, bt4, ctx)
+        kc4, vc4 = cache_dev(kb), cache_dev(vb)
+        del kb, vb
+        bt4d = i32(bt4.table)
+        x4 = to_dev(gen.hidden(c4, B4, step=9), torch.float32)
+        y4 = torch.empty_like(x4)
+        p4, c4d = i32(ctx - 1), i32(ctx)
+        mx = int(ctx.max())
+        ws4 = torch.empty(dl.dl_layer_workspace_size(lay.dims, B4, B4, 0, mx, mode),
+                          dtype=torch.uint8, device="cuda:0")
+
+        def step4():
+            dl.dl_layer_decode(lay.dims, lay.w, lay.cs, x4, y4, p4, c4d, mx, kc4, vc4, bt4d,
+                               ws=ws4)
+
+        for _ in range(args.warmup):
+            step4()
+        torch.cuda.synchronize()
+        ems = time_launches(step4, max(args.steps, 50), stream)
+        side = torch.cuda.Stream()
+        g4 = dl.DecodeGraph(lay.dims, lay.w, lay.cs, x4, y4, p4, c4d, mx, kc4, vc4, bt4d, side,
+                            ws=ws4)
+        for _ in range(args.warmup):
+            g4.launch()
+        side.synchronize()
+        gms = time_launches(g4.launch, max(args.steps, 50), side)
+        ems_sync = time_synced(step4, max(args.steps, 50), stream)
+        gms_sync = time_synced(g4.launch, max(args.steps, 50), side)
+        g4.close()
+        H4, Hq4, Hkv4, D4, I4 = c4.hidden, c4.n_q_heads, c4.n_kv_heads, c4.head_dim, \
+            c4.intermediate
+        w_bytes = 2.0 * (H4 * (Hq4 + 2 * Hkv4) * D4 + Hq4 * D4 * H4 + 3 * H4 * I4)
+        kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv4 * D4 * 2
+        out = {"workload": "llama3-8b-layer-decode-b8", "batch": B4,
+               "context": "prefill lengths U{256..1024} + 64 (mean %.0f)" % ctx.mean(),
+               "eager_ms_per_step": round(ems, 4), "graph_ms_per_step": round(gms, 4),
+               "synced_eager_ms_per_step": round(ems_sync, 4),
+               "synced_graph_ms_per_step": round(gms_sync, 4),
+               "eager_tokens_per_s": round(B4 / (ems * 1e-3), 1),
+               "graph_tokens_per_s": round(B4 / (gms * 1e-3), 1),
+               "graph_step_hbm_frac": round((w_bytes + kv_bytes) / (gms * 1e-3) / 1e9
+                                            / PEAK_HBM_GBS, 4)}
+        log(f"[bench] 8B decode B{B4}: eager {ems:.4f} ms, graph {gms:.4f} ms per step; with a "
+            f"host sync per step: eager {ems_sync:.4f} ms, graph {gms_sync:.4f} ms")
+        del kc4, vc4, ws4, lay
+        torch.cuda.empty_cache()
+        return out
+
     if not args.no_decode:
+        result["decode_small_batch"] = run_small_decode()
         result["decode"] = run_decode(False)
         if not args.no_int8:
             result["decode_kv_int8"] = run_decode(True)

@@ -371,6 +371,38 @@ dl_status dl_layer_decode_qlens(const dl_layer_dims* d, const dl_layer_weights* 
                                 int32_t max_blocks_per_seq, dl_mode m, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/*
+ * A decode step recorded once as a HIP graph and replayed per step, so the
+ * step's 9-13 kernels go to the GPU in one launch with no host gaps between
+ * them (ATB KV-cache page, section "KV cache memory bottleneck": the
+ * GraphOpBuilder groups ReshapeAndCache and PagedAttention into one graph
+ * operation so no stream bubble opens between them; ATB decoder-layer page,
+ * "graph execution engine").
+ *
+ * dl_layer_decode_graph_create records dl_layer_decode with exactly these
+ * arguments on `stream` (which must not be NULL: the legacy default stream
+ * cannot be captured) and instantiates it.  Nothing runs during creation.
+ * Every pointer is baked into the graph: between replays the caller rewrites
+ * the CONTENTS of hidden_in, positions and context_lens (and of the caches
+ * and block_table) in place; B is fixed, and every context length must stay
+ * <= the max_context_len given here (the launch grids are sized for it).
+ * dl_graph_launch replays it on any stream; dl_graph_destroy frees the
+ * host-side graph objects.  The graph holds no device memory of its own.
+ * Errors: those of dl_layer_decode (nothing recorded, *graph untouched), or
+ * DL_ERR_HIP if capture or instantiation fails.
+ */
+typedef struct dl_graph_s* dl_graph;
+dl_status dl_layer_decode_graph_create(const dl_layer_dims* d, const dl_layer_weights* w,
+                                       const float* cos_sin, int32_t max_pos,
+                                       const float* hidden_in, float* hidden_out,
+                                       const int32_t* positions, const int32_t* context_lens,
+                                       int32_t max_context_len, int32_t B,
+                                       const dl_kv_cache* cache, const int32_t* block_table,
+                                       int32_t max_blocks_per_seq, void* ws, size_t ws_bytes,
+                                       void* stream, dl_graph* graph);
+dl_status dl_graph_launch(dl_graph graph, void* stream);
+dl_status dl_graph_destroy(dl_graph graph);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,100 @@
+"""The decode step recorded as a HIP graph: every replay, with its inputs
+rewritten in place and eager work and synchronisations in between, gives
+the same output and cache bits as the eager dl_layer_decode call with the
+same arguments."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from transformer_decoder_layer_residual_amd import binding as dl
+from transformer_decoder_layer_residual_amd import inputs as gen
+from transformer_decoder_layer_residual_amd.harness import (DeviceLayer, cache_dev, i32,
+                                                            prefill_inputs, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def small_gqa_cfg():
+    return dataclasses.replace(gen.CONFIGS[4], config_id=43, name="gqa-small-graph", hidden=512,
+                               n_q_heads=8, n_kv_heads=2, head_dim=128, intermediate=1408,
+                               block_size=16)
+
+
+@pytest.mark.parametrize("cfg_name,int8", [("tiny-f32", False), ("gqa-bf16", False),
+                                           ("gqa-bf16", True)])
+def test_decode_graph_replays_equal_eager(cfg_name, int8):
+    cfg = gen.CONFIGS[1] if cfg_name == "tiny-f32" else small_gqa_cfg()
+    print(f"decode graph {cfg_name} int8={int8}", flush=True)
+    lens, steps = [17, 1, 40, 9], 4
+    pb = gen.packed(lens)
+    layer = DeviceLayer.build(cfg, max_pos=64, gamma="uniform")
+    bt = gen.block_table(cfg, pb.lens + steps)
+    btd = i32(bt.table)
+    if int8:
+        host_cache = gen.empty_cache_q8(cfg, bt.num_blocks)
+    else:
+        host_cache = gen.empty_cache(cfg, bt.num_blocks)
+    a = [cache_dev(c) for c in host_cache]        # replayed by the graph
+    x0 = to_dev(gen.hidden(cfg, pb.T), torch.float32)
+    sc = {"ks": a[2], "vs": a[3]} if int8 else {}
+    layer.prefill(x0, pb, a[0], a[1], btd, **sc)
+    torch.cuda.synchronize()
+    b = [t.clone() for t in a]                    # eager reference
+    B = pb.B
+    max_ctx = int(pb.lens.max()) + steps          # the grid bound for every replay
+    xin = torch.zeros(B, cfg.hidden, device="cuda:0")
+    yout = torch.zeros_like(xin)
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda:0")
+    ctx = torch.zeros(B, dtype=torch.int32, device="cuda:0")
+    side = torch.cuda.Stream()
+    scales = {"k_scale": a[2], "v_scale": a[3]} if int8 else {}
+    graph = dl.DecodeGraph(layer.dims, layer.w, layer.cs, xin, yout, pos, ctx, max_ctx, a[0], a[1],
+                           btd, side, **scales)
+    try:
+        for s in range(steps):
+            c = (pb.lens + s + 1).astype(np.int32)
+            xs = to_dev(gen.hidden(cfg, B, step=50 + s), torch.float32)
+            xin.copy_(xs)
+            pos.copy_(i32(c - 1))
+            ctx.copy_(i32(c))
+            torch.cuda.synchronize()
+            graph.launch()
+            side.synchronize()
+            y_graph = yout.clone()
+            # the eager call with the same arguments (same max_context_len)
+            y_ref = torch.empty_like(xs)
+            esc = {"k_scale": b[2], "v_scale": b[3]} if int8 else {}
+            dl.dl_layer_decode(layer.dims, layer.w, layer.cs, xs, y_ref, i32(c - 1), i32(c),
+                               max_ctx, b[0], b[1], btd, **esc)
+            torch.cuda.synchronize()
+            assert torch.equal(y_graph, y_ref), f"replay {s}: output differs from eager"
+            for ta, tb in zip(a, b):
+                if ta.dtype == torch.float32:
+                    assert torch.equal(ta.view(torch.int32), tb.view(torch.int32)), f"replay {s}"
+                elif ta.dtype == torch.bfloat16:
+                    assert torch.equal(ta.view(torch.int16), tb.view(torch.int16)), f"replay {s}"
+                else:
+                    assert torch.equal(ta, tb), f"replay {s}: cache differs"
+    finally:
+        graph.close()
+
+
+def test_decode_graph_rejects_default_stream_and_bad_args():
+    cfg = small_gqa_cfg()
+    layer = DeviceLayer.build(cfg, max_pos=16)
+    bt = gen.block_table(cfg, [8])
+    kb, vb = gen.empty_cache(cfg, bt.num_blocks)
+    x = torch.zeros(1, cfg.hidden, device="cuda:0")
+    z = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+
+    class Null:
+        cuda_stream = 0
+
+    with pytest.raises(dl.DLError, match="default"):
+        dl.DecodeGraph(layer.dims, layer.w, layer.cs, x, torch.empty_like(x), z, z, 8,
+                       cache_dev(kb), cache_dev(vb), i32(bt.table), Null())
+    with pytest.raises(dl.DLError, match="alias"):
+        dl.DecodeGraph(layer.dims, layer.w, layer.cs, x, x, z, z, 8, cache_dev(kb),
+                       cache_dev(vb), i32(bt.table), torch.cuda.Stream())

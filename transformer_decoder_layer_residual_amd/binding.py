@@ -104,6 +104,12 @@ _SIGS = [
                                        _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                        ctypes.POINTER(KVCache), _vp, _c_int, ctypes.c_int, _vp,
                                        _sz, _vp]),
+    ("dl_layer_decode_graph_create", ctypes.c_int,
+     [ctypes.POINTER(LayerDims), ctypes.POINTER(LayerWeights), _vp, _c_int, _vp, _vp, _vp, _vp,
+      _c_int, _c_int, ctypes.POINTER(KVCache), _vp, _c_int, _vp, _sz, _vp,
+      ctypes.POINTER(_vp)]),
+    ("dl_graph_launch", ctypes.c_int, [_vp, _vp]),
+    ("dl_graph_destroy", ctypes.c_int, [_vp]),
     ("dl_layer_decode_qlens_workspace_size", _sz, [ctypes.POINTER(LayerDims), _c_int, _c_int,
                                                    _c_int, _c_int]),
     ("dl_layer_decode_qlens", ctypes.c_int, [ctypes.POINTER(LayerDims),
@@ -397,3 +403,45 @@ def dl_layer_decode_qlens(dims: LayerDims, weights: dict, cos_sin, hidden_in, hi
                                    max_q_len, max_context_len, ctypes.byref(c), _p(block_table),
                                    block_table.shape[1], DL_FUSED, _p(ws),
                                    ws.numel() * ws.element_size(), _stream()))
+
+
+class DecodeGraph:
+    """dl_layer_decode recorded once (dl_layer_decode_graph_create) and
+    replayed with dl_graph_launch.  The tensors passed here are baked into
+    the graph: update their contents in place between launches.  Capture and
+    replay run on `stream` (a torch.cuda.Stream, not the default stream)."""
+
+    def __init__(self, dims: LayerDims, weights: dict, cos_sin, hidden_in, hidden_out, positions,
+                 context_lens, max_context_len: int, k_cache, v_cache, block_table, stream,
+                 ws=None, k_scale=None, v_scale=None):
+        B = hidden_in.shape[0]
+        L = lib()
+        if ws is None:
+            n = L.dl_layer_workspace_size(ctypes.byref(dims), B, B, 0, max_context_len, DL_FUSED)
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=hidden_in.device)
+        self._keep = (dims, weights, cos_sin, hidden_in, hidden_out, positions, context_lens,
+                      k_cache, v_cache, block_table, ws, k_scale, v_scale)
+        self.stream = stream
+        self._wts = make_weights(weights)
+        self._cache = _cache(k_cache, v_cache, k_scale, v_scale)
+        h = _vp()
+        _check(L.dl_layer_decode_graph_create(
+            ctypes.byref(dims), ctypes.byref(self._wts), _p(cos_sin), cos_sin.shape[0],
+            _p(hidden_in), _p(hidden_out), _p(positions), _p(context_lens), max_context_len, B,
+            ctypes.byref(self._cache), _p(block_table), block_table.shape[1], _p(ws),
+            ws.numel() * ws.element_size(), stream.cuda_stream, ctypes.byref(h)))
+        self._h = h
+
+    def launch(self):
+        _check(lib().dl_graph_launch(self._h, self.stream.cuda_stream))
+
+    def close(self):
+        if self._h:
+            _check(lib().dl_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -950,4 +950,59 @@ dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
                            max_blocks_per_seq, m, ws, L, st);
 }
 
+struct dl_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+dl_status dl_layer_decode_graph_create(const dl_layer_dims* d, const dl_layer_weights* w,
+                                       const float* cos_sin, int32_t max_pos,
+                                       const float* hidden_in, float* hidden_out,
+                                       const int32_t* positions, const int32_t* context_lens,
+                                       int32_t max_context_len, int32_t B,
+                                       const dl_kv_cache* cache, const int32_t* block_table,
+                                       int32_t max_blocks_per_seq, void* ws, size_t ws_bytes,
+                                       void* stream, dl_graph* graph) {
+  if (!graph) return fail(DL_ERR_INVALID_ARG, "graph must not be NULL");
+  if (!stream) return fail(DL_ERR_INVALID_ARG, "capture needs a stream other than the default (NULL) one");
+  hipStream_t st = (hipStream_t)stream;
+  DL_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal), "begin capture");
+  const dl_status s = dl_layer_decode(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions,
+                                      context_lens, max_context_len, B, cache, block_table,
+                                      max_blocks_per_seq, DL_FUSED, ws, ws_bytes, stream);
+  const std::string why = g_last_error;
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(st, &g);
+  if (s != DL_OK) {
+    if (e == hipSuccess && g) hipGraphDestroy(g);
+    g_last_error = why;
+    return s;
+  }
+  if (e != hipSuccess) return hip_fail(e, "end capture");
+  hipGraphExec_t x = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    hipGraphDestroy(g);
+    return hip_fail(ei, "graph instantiate");
+  }
+  *graph = new dl_graph_s{g, x};
+  return ok();
+}
+
+dl_status dl_graph_launch(dl_graph graph, void* stream) {
+  if (!graph) return fail(DL_ERR_INVALID_ARG, "graph must not be NULL");
+  DL_HIP(hipGraphLaunch(graph->exec, (hipStream_t)stream), "graph launch");
+  return ok();
+}
+
+dl_status dl_graph_destroy(dl_graph graph) {
+  if (!graph) return ok();
+  const hipError_t e1 = hipGraphExecDestroy(graph->exec);
+  const hipError_t e2 = hipGraphDestroy(graph->graph);
+  delete graph;
+  if (e1 != hipSuccess) return hip_fail(e1, "graph exec destroy");
+  if (e2 != hipSuccess) return hip_fail(e2, "graph destroy");
+  return ok();
+}
+
 }  // extern "C"
