@@ -36,11 +36,19 @@ FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 
 # dominant kernels reported by bench.py: key -> (kernel-name regex, sources)
+# (rocprofv3 reports some kernel names mangled and some demangled, with
+# __bf16 printed as "bool _Accum"; each pattern accepts both forms of the one
+# instance the benchmark's roofline line times)
 KERNELS = {
-    "gemm_gateup_silu_prefill": (r"gemm_pp_kernel.*MapSwiglu",
+    "gemm_gateup_silu_prefill": (r"gemm_pp_kernelILi256ELi64ENS_9MapSwiglu"
+                                 r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
                                  ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
-    "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16b", ("attn_decode.hip", "dl_common.hpp")),
-    "attn_decode_paged_int8": (r"attn_decode_kernelIDF16ba", ("attn_decode.hip", "dl_common.hpp")),
+    "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16bLi128ELi1E"
+                          r"|attn_decode_kernel<bool _Accum, bool _Accum, 128, 1,",
+                          ("attn_decode.hip", "dl_common.hpp")),
+    "attn_decode_paged_int8": (r"attn_decode_kernelIDF16baLi128ELi1E"
+                               r"|attn_decode_kernel<bool _Accum, (signed char, )?128, 1,",
+                               ("attn_decode.hip", "dl_common.hpp")),
 }
 
 
