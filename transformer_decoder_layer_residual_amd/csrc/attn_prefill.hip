@@ -227,7 +227,11 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 // the score registers with the key order of its k-slots matched by the V^T
 // reads.  Waves skip tiles entirely above their causal diagonal.  Blocks are
 // ordered so that every q-tile of a head runs on the same XCD (K/V of a head
-// stay in that XCD's L2), heaviest q-tiles first.
+// stay in that XCD's L2): the heavier half of the q-tiles first, heaviest
+// first, then the lighter half lightest first.  With two workgroups per CU
+// filled in dispatch order, a CU then holds tiles t and n-1-t, whose causal
+// work adds up to the same total on every CU (heaviest-first alone paired
+// heavy with middle tiles: up to 1.4x the average work on one CU).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256, 2)
@@ -247,16 +251,18 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- block -> (q-tile, head): XCD-aware when the head count allows
   const int L = blockIdx.x;
-  int qt, hh;
+  int u, hh;                                            // u: rank of the q-tile in launch order
   if ((n_heads_total & 7) == 0) {
     const int xcd = L & 7, idx = L >> 3;
     const int hpx = n_heads_total >> 3;                 // heads per XCD
-    qt = n_qtiles - 1 - idx / hpx;                      // heaviest first
+    u = idx / hpx;
     hh = xcd * hpx + idx % hpx;
   } else {
-    qt = n_qtiles - 1 - L / n_heads_total;
+    u = L / n_heads_total;
     hh = L % n_heads_total;
   }
+  const int heavy = (n_qtiles + 1) / 2;
+  const int qt = u < heavy ? n_qtiles - 1 - u : u - heavy;
   const int b = hh / Hq, h = hh % Hq;
   const int t0 = cu[b], S = cu[b + 1] - t0;
   const int q_begin = qt * BQ;
