@@ -143,6 +143,16 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
+// Store 8 consecutive floats as T (one 16-byte store for bf16).
+__device__ __forceinline__ void store8(bf16* p, const float* v) {
+  bf16x8 w = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3],
+              (bf16)v[4], (bf16)v[5], (bf16)v[6], (bf16)v[7]};
+  *reinterpret_cast<bf16x8*>(p) = w;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
 __device__ __forceinline__ void load4(const bf16* p, float* o) {
   bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
   o[0] = (float)v[0];

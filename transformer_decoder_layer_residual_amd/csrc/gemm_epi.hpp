@@ -67,19 +67,38 @@ struct MapQKV {
 
 // ---------------------------------------------------------------------------
 // epilogues: (row m, tile tn, first-half column j (multiple of 4), 4 values of
-// columns j..j+3 and 4 values of their partners j+P..j+P+3)
+// columns j..j+3 and 4 values of their partners j+P..j+P+3).  An epilogue that
+// reads memory (RoPE table, residual) splits into prefetch(m, tn, j), which
+// issues those loads, and the call with their result, so a GEMM can fetch the
+// next output group's operands before it does the current group's math and
+// stores; the five-argument call does both back to back.  apply8 is the same
+// computation for 8 consecutive columns and their partners (j a multiple of
+// 8), used where a GEMM hands out its output rows from LDS in row order, so
+// that a row's chunks leave as whole 128-byte lines.
 // ---------------------------------------------------------------------------
+struct NoPre {};
 // Plain store; columns at or beyond N (the ragged last tile) are dropped.
 // N is a multiple of 16, so a group of 4 columns is either all in or all out.
 template <typename To>
 struct EpiPlain {
   To* out;
   int ldo, BN, P;
+  using Pre = NoPre;
+  __device__ Pre prefetch(int, int, int) const { return {}; }
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b, const Pre&) const {
+    (*this)(m, tn, j, a, b);
+  }
   __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
     const int n = tn * BN + j;
     To* p = out + (int64_t)m * ldo + n;
     if (n < ldo) store4(p, a[0], a[1], a[2], a[3]);
     if (n + P < ldo) store4(p + P, b[0], b[1], b[2], b[3]);
+  }
+  __device__ void apply8(int m, int tn, int j, const float* a, const float* b) const {
+    const int n = tn * BN + j;
+    To* p = out + (int64_t)m * ldo + n;
+    if (n < ldo) store8(p, a);
+    if (n + P < ldo) store8(p + P, b);
   }
 };
 
@@ -87,16 +106,44 @@ struct EpiResid {
   float* out;
   const float* resid;
   int ldo, BN, P;
-  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+  struct Pre {
+    f32x4 r0, r1;
+  };
+  __device__ Pre prefetch(int m, int tn, int j) const {
     const int n = tn * BN + j;
     const int64_t o = (int64_t)m * ldo + n;
+    Pre p{};
+    if (n < ldo) p.r0 = *reinterpret_cast<const f32x4*>(resid + o);
+    if (n + P < ldo) p.r1 = *reinterpret_cast<const f32x4*>(resid + o + P);
+    return p;
+  }
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b, const Pre& p) const {
+    const int n = tn * BN + j;
+    const int64_t o = (int64_t)m * ldo + n;
+    if (n < ldo) store4(out + o, p.r0[0] + a[0], p.r0[1] + a[1], p.r0[2] + a[2], p.r0[3] + a[3]);
+    if (n + P < ldo)
+      store4(out + o + P, p.r1[0] + b[0], p.r1[1] + b[1], p.r1[2] + b[2], p.r1[3] + b[3]);
+  }
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    (*this)(m, tn, j, a, b, prefetch(m, tn, j));
+  }
+  __device__ void apply8(int m, int tn, int j, const float* a, const float* b) const {
+    const int n = tn * BN + j;
+    const int64_t o = (int64_t)m * ldo + n;
+    float r[8];
     if (n < ldo) {
-      const f32x4 r0 = *reinterpret_cast<const f32x4*>(resid + o);
-      store4(out + o, r0[0] + a[0], r0[1] + a[1], r0[2] + a[2], r0[3] + a[3]);
+      load4(resid + o, r);
+      load4(resid + o + 4, r + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] += a[e];
+      store8(out + o, r);
     }
     if (n + P < ldo) {
-      const f32x4 r1 = *reinterpret_cast<const f32x4*>(resid + o + P);
-      store4(out + o + P, r1[0] + b[0], r1[1] + b[1], r1[2] + b[2], r1[3] + b[3]);
+      load4(resid + o + P, r);
+      load4(resid + o + P + 4, r + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] += b[e];
+      store8(out + o + P, r);
     }
   }
 };
@@ -105,9 +152,20 @@ template <typename To>
 struct EpiSwiglu {
   To* out;
   int I, P;
+  using Pre = NoPre;
+  __device__ Pre prefetch(int, int, int) const { return {}; }
+  __device__ void operator()(int m, int tn, int j, f32x4 g, f32x4 u, const Pre&) const {
+    (*this)(m, tn, j, g, u);
+  }
   __device__ void operator()(int m, int tn, int j, f32x4 g, f32x4 u) const {
     To* p = out + (int64_t)m * I + (int64_t)tn * P + j;
     store4(p, silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2], silu(g[3]) * u[3]);
+  }
+  __device__ void apply8(int m, int tn, int j, const float* g, const float* u) const {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = silu(g[e]) * u[e];
+    store8(out + (int64_t)m * I + (int64_t)tn * P + j, r);
   }
 };
 
@@ -142,13 +200,30 @@ struct EpiRope {
   const float* cs;
   int Hq, Hkv, D, P, max_pos;
   CacheSink<To> sink;
-  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+  struct Pre {
+    f32x4 c0, c1;  // cos c, sin c, cos c+1, sin c+1 | cos c+2, sin c+2, cos c+3, sin c+3
+  };
+  __device__ Pre prefetch(int m, int tn, int j) const {
     const int half = D / 2;
     const int pc = tn * P + j;
-    const int head = pc / half, c = pc - head * half;
-    To* dst;
-    To* cdst = nullptr;
-    bool rot = true;
+    const int c = pc % half;
+    const int p = min(max(pos[m], 0), max_pos - 1);  // out-of-table positions clamp
+    const float* cp = cs + ((int64_t)p * half + c) * 2;
+    return Pre{*reinterpret_cast<const f32x4*>(cp), *reinterpret_cast<const f32x4*>(cp + 4)};
+  }
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b) const {
+    (*this)(m, tn, j, a, b, prefetch(m, tn, j));
+  }
+  // where pair-column j of tile tn of row m goes: the head row in q/k/v (dst,
+  // null when k/v go to the cache only), its cache row (cdst or null), the
+  // column c within the first half, and whether it is rotated (q, k) or not (v)
+  __device__ void route(int m, int tn, int j, int& c, bool& rot, To*& dst, To*& cdst) const {
+    const int half = D / 2;
+    const int pc = tn * P + j;
+    const int head = pc / half;
+    c = pc - head * half;
+    cdst = nullptr;
+    rot = true;
     if (head < Hq) {
       dst = q + ((int64_t)m * Hq + head) * D;
     } else if (head < Hq + Hkv) {
@@ -161,11 +236,49 @@ struct EpiRope {
       if (sink.kc) cdst = sink.slot(sink.vc, m, g, Hkv, D, pos[m]);
       rot = false;
     }
+  }
+  __device__ void apply8(int m, int tn, int j, const float* a, const float* b) const {
+    const int half = D / 2;
+    int c;
+    bool rot;
+    To *dst, *cdst;
+    route(m, tn, j, c, rot, dst, cdst);
+    float o1[8], o2[8];
     if (rot) {
       const int p = min(max(pos[m], 0), max_pos - 1);  // out-of-table positions clamp
       const float* cp = cs + ((int64_t)p * half + c) * 2;
-      f32x4 c0 = *reinterpret_cast<const f32x4*>(cp);      // cos c, sin c, cos c+1, sin c+1
-      f32x4 c1 = *reinterpret_cast<const f32x4*>(cp + 4);  // cos c+2, sin c+2, cos c+3, sin c+3
+      float t[16];  // cos c, sin c, cos c+1, sin c+1, ...
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load4(cp + 4 * u, t + 4 * u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o1[e] = a[e] * t[2 * e] - b[e] * t[2 * e + 1];
+        o2[e] = b[e] * t[2 * e] + a[e] * t[2 * e + 1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o1[e] = a[e];
+        o2[e] = b[e];
+      }
+    }
+    if (dst) {
+      store8(dst + c, o1);
+      store8(dst + half + c, o2);
+    }
+    if (cdst) {  // the same rounding as the buffer store: identical bits
+      store8(cdst + c, o1);
+      store8(cdst + half + c, o2);
+    }
+  }
+  __device__ void operator()(int m, int tn, int j, f32x4 a, f32x4 b, const Pre& pf) const {
+    const int half = D / 2;
+    int c;
+    bool rot;
+    To *dst, *cdst;
+    route(m, tn, j, c, rot, dst, cdst);
+    if (rot) {
+      const f32x4 c0 = pf.c0, c1 = pf.c1;
       float co[4] = {c0[0], c0[2], c1[0], c1[2]};
       float si[4] = {c0[1], c0[3], c1[1], c1[3]};
       float o1[4], o2[4];

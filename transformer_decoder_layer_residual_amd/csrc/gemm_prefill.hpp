@@ -186,8 +186,11 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
   constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
   constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
   constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
+  constexpr int OPITCH = BN + 8;                    // fp32 row pitch of the output staging
+  constexpr int SMEM_MAIN = NSTAGE * STAGE, SMEM_OUT = GR * OPITCH * 4;
   static_assert(NSTAGE >= 2 && LA <= 3, "stages");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE];
+  __shared__ __attribute__((aligned(1024)))
+  unsigned char smem[SMEM_MAIN > SMEM_OUT ? SMEM_MAIN : SMEM_OUT];
 
   int bid = blockIdx.x;
   const int total = tiles_m * tiles_n;
@@ -306,21 +309,48 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
   if (grp == 0) DL_PHASE_END();                     // balance group 1's extra barrier
 #undef DL_PHASE_END
 
-  // epilogue: lane owns column m and rows n = 8 q + 4 (lane / 32) + j of each block
+  // Epilogue through LDS, one group's 128 (BM 256) or 64 (BM 128) rows at a
+  // time: the group's waves park their fp32 accumulators row-major in LDS,
+  // then all 512 threads take 8-column chunks in row order and run the
+  // epilogue on them, so the 16 chunks of an output row (and of its partner
+  // half) leave as whole 128-byte lines.  Lane l holds column m = ... + l % 32
+  // and rows n = 8 q + 4 (l / 32) + j of each 32x32 block.
+  float* stage = reinterpret_cast<float*>(smem);
+  __syncthreads();                                  // every main-loop LDS read is done
 #pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    const int m = tm * BM + grp * GR + wm * WR + i * 32 + fr;
-    if (m >= M) continue;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (grp == pass) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int i = 0; i < MS; ++i) {
+        const int r = wm * WR + i * 32 + fr;          // row within the group
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int j = (2 * wn + b) * 32 + 8 * q + 4 * fh;
-        const f32x4 lo = {acc[i][b][4 * q], acc[i][b][4 * q + 1], acc[i][b][4 * q + 2], acc[i][b][4 * q + 3]};
-        const f32x4 hi = {acc[i][b + 2][4 * q], acc[i][b + 2][4 * q + 1], acc[i][b + 2][4 * q + 2],
-                          acc[i][b + 2][4 * q + 3]};
-        epi(m, tn, j, lo, hi);
+        for (int s = 0; s < NS; ++s) {
+          const int col = (s < 2 ? 0 : BN / 2) + (2 * wn + (s & 1)) * 32 + 4 * fh;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(stage + r * OPITCH + col + 8 * q) =
+                f32x4{acc[i][s][4 * q], acc[i][s][4 * q + 1], acc[i][s][4 * q + 2],
+                      acc[i][s][4 * q + 3]};
+        }
       }
+    }
+    __syncthreads();
+    constexpr int CH = (BN / 2) / 8;                  // 8-column chunks per half row
+#pragma unroll
+    for (int it = 0; it < GR * CH / 512; ++it) {
+      const int idx = t + it * 512;
+      const int r = idx / CH, j = (idx % CH) * 8;
+      const int m = tm * BM + pass * GR + r;
+      if (m < M) {
+        float a[8], b[8];
+        load4(stage + r * OPITCH + j, a);
+        load4(stage + r * OPITCH + j + 4, a + 4);
+        load4(stage + r * OPITCH + BN / 2 + j, b);
+        load4(stage + r * OPITCH + BN / 2 + j + 4, b + 4);
+        epi.apply8(m, tn, j, a, b);
+      }
+    }
+    __syncthreads();
   }
 }
 
