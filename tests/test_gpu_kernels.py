@@ -79,6 +79,8 @@ GEMM_SHAPES = [
     (700, 22000, 200),   # 256x256 prefill tile: M tail, ragged N, K tail
     (40, 1008, 264),     # decode weight-streaming kernel: ragged last tile, K tail
     (64, 4096, 11008),   # decode down-projection shape: 16 K slices
+    (2048, 12288, 128),  # 384 tiles of 256: 256-row tiles then 128-row tiles in one launch
+    (2000, 12288, 192),  # the same with a ragged last row tile
 ]
 
 
@@ -382,9 +384,14 @@ def _rows(M):
     return np.unique(np.concatenate([np.arange(8), R.integers(0, M, 40), [M - 1]]))
 
 
-def test_qkv_rope_large_tile():
-    T, H, Hq, Hkv, D = 2048, 256, 32, 16, 128      # 8 x 32 tiles of 256
-    print(f"qkv_rope large T={T}", flush=True)
+@pytest.mark.parametrize("T,Hq,Hkv", [
+    (2048, 32, 16),     # 8 x 32 tiles of 256
+    (2048, 32, 32),     # 8 x 48: 256-row tiles, then 128-row tiles for the last 16 columns
+    (1900, 32, 32),     # the same with a ragged last row tile
+])
+def test_qkv_rope_large_tile(T, Hq, Hkv):
+    H, D = 256, 128
+    print(f"qkv_rope large T={T} {Hq}/{Hkv}", flush=True)
     x = rnd(T, H)
     wq, wk, wv = (rnd(h * D, H, scale=0.05) for h in (Hq, Hkv, Hkv))
     pos = R.integers(0, 4096, T).astype(np.int32)

@@ -36,6 +36,7 @@ struct GemmPlan {
   int splits;        // number of K slices (1 = direct epilogue)
   int k_per_split;   // multiple of the K tile
   size_t ws_bytes;   // fp32 partials when splits > 1
+  int mixed_tn;      // > 0: 256-row tiles for the first mixed_tn N-tiles, 128-row after
 };
 
 // N: logical output columns.  paired: the epilogue needs pair partners, so

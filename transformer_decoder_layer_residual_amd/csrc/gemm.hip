@@ -73,6 +73,20 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
                                       sizeof(float) : 0;
     return pl;
   }
+  if (cfg == kCfg256) {
+    // a last round at most half full: the columns it would cover go out as
+    // 128-row tiles (about 0.6 of a 256-row tile's time, measured), taken up
+    // by the CUs the full rounds free
+    const int tm = (M + 255) / 256, tn = tiles_n(cfg), tm128 = (M + 127) / 128;
+    const int full = nt / 256;
+    if (nt % 256 && full >= 1) {
+      const int big_tn = (256 * full) / tm;
+      const int small = (tn - big_tn) * tm128;
+      const double now = std::ceil(nt / 256.0);
+      const double mixed = std::ceil(tm * big_tn / 256.0) + 0.6 * std::ceil(small / 256.0);
+      if (big_tn >= 1 && big_tn < tn && mixed < now - 0.2) pl.mixed_tn = big_tn;
+    }
+  }
   int splits = 1;
   const bool single_pass = (cfg == kCfg256 || cfg == kCfgPP128);  // no split-K variant
   if (single_pass) {
@@ -117,8 +131,18 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
 
 template <class Map, class Epi>
 static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
-                             hipStream_t st, int bm = 256, int bk = 64) {
+                             hipStream_t st, int bm = 256, int bk = 64, int mixed_tn = 0) {
   const int tiles_n = (NL + 255) / 256;
+  if (K % 64 == 0 && bm == 256 && mixed_tn > 0 && mixed_tn < tiles_n) {
+    const int grid = ((M + 255) / 256) * mixed_tn + ((M + 127) / 128) * (tiles_n - mixed_tn);
+    if (bk == 32)
+      hipLaunchKernelGGL((gemm_pp_mixed_kernel<32, Map, Epi>), dim3(grid), dim3(512), 0, st, x, M,
+                         K, map, epi, mixed_tn, tiles_n);
+    else
+      hipLaunchKernelGGL((gemm_pp_mixed_kernel<64, Map, Epi>), dim3(grid), dim3(512), 0, st, x, M,
+                         K, map, epi, mixed_tn, tiles_n);
+    return hipGetLastError();
+  }
   if (K % 64 == 0 && bm == 128) {
     const int tiles_m = (M + 127) / 128;
     if (bk == 32)
@@ -194,7 +218,9 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
     return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
   } else {
     switch (pl.cfg) {
-      case kCfg256: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 256);
+      case kCfg256:
+        return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 256, 64,
+                          pl.mixed_tn);
       case kCfgPP128: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 128);
       case kCfg128: return launch_cfg<T, T128>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);

@@ -169,30 +169,41 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// LDS footprint of one tile shape: the k-tile stages, or the fp32 staging of
+// one group's output rows, whichever is larger.
+template <int BM, int BK>
+struct PPGeom {
+  static constexpr int BN = 256;
+  static constexpr int STAGE = (BM + BN) * BK * 2;
+  static constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
+  static constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
+  static constexpr int OPITCH = BN + 8;             // fp32 row pitch of the output staging
+  static constexpr int MAIN = NSTAGE * STAGE, OUT = (BM / 2) * OPITCH * 4;
+  static constexpr int SMEM = MAIN > OUT ? MAIN : OUT;
+};
+
+// One BM x 256 output tile: tile `bid` of a tiles_m x tiles_n grid whose
+// N-tiles start at tn0 (so a launch may cover a range of N with one shape).
 template <int BM, int BK, class Map, class Epi>
-__global__ void __launch_bounds__(512, 1)
-gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
-               int tiles_n) {
+__device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K, const Map& map,
+                                        const Epi& epi, int bid, int tiles_m, int tiles_n,
+                                        int tn0, unsigned char* smem) {
+  using Geo = PPGeom<BM, BK>;
   constexpr int BN = 256;
   constexpr int ROWB = BK * 2;                      // bytes per LDS row
   constexpr int CPR = BK / 8;                       // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;                     // rows per wave load instruction (1 KB)
-  constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
-  constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
+  constexpr int STAGE = Geo::STAGE;
+  constexpr int NSTAGE = Geo::NSTAGE;
   constexpr int LA = NSTAGE - 1;                    // k-tiles loaded ahead
   constexpr int MS = BM / 128, NS = 4;              // 32x32 blocks per wave
   constexpr int KS = BK / 16;                       // k16 steps per tile
   constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
   constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
   constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
-  constexpr int OPITCH = BN + 8;                    // fp32 row pitch of the output staging
-  constexpr int SMEM_MAIN = NSTAGE * STAGE, SMEM_OUT = GR * OPITCH * 4;
+  constexpr int OPITCH = Geo::OPITCH;
   static_assert(NSTAGE >= 2 && LA <= 3, "stages");
-  __shared__ __attribute__((aligned(1024)))
-  unsigned char smem[SMEM_MAIN > SMEM_OUT ? SMEM_MAIN : SMEM_OUT];
 
-  int bid = blockIdx.x;
   const int total = tiles_m * tiles_n;
   if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
   constexpr int GM = 8;
@@ -200,7 +211,7 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
   const int first_m = (bid / gsz) * GM;
   const int gm = min(tiles_m - first_m, GM);
   const int tm = first_m + (bid % gsz) % gm;
-  const int tn = (bid % gsz) / gm;
+  const int tn = tn0 + (bid % gsz) / gm;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int grp = wave >> 2, wig = wave & 3;        // group, wave in group
@@ -352,6 +363,33 @@ gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int t
     }
     __syncthreads();
   }
+}
+
+template <int BM, int BK, class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
+               int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[PPGeom<BM, BK>::SMEM];
+  pp_tile<BM, BK>(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, 0, smem);
+}
+
+// 256-row tiles for N-tiles [0, big_tn) and 128-row tiles for the rest, in one
+// launch: when 256-row tiles would leave a last round at most half full (the
+// 7B QKV projection: 384 tiles on 256 CUs), the remaining columns go out as
+// twice as many half-height tiles, which the CUs freed by the first round take
+// up at once.
+template <int BK, class Map, class Epi>
+__global__ void __launch_bounds__(512, 1)
+gemm_pp_mixed_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int big_tn,
+                     int tiles_n) {
+  constexpr int S256 = PPGeom<256, BK>::SMEM, S128 = PPGeom<128, BK>::SMEM;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S256 > S128 ? S256 : S128];
+  const int tm256 = (M + 255) / 256, n_big = tm256 * big_tn;
+  if ((int)blockIdx.x < n_big)
+    pp_tile<256, BK>(X, M, K, map, epi, blockIdx.x, tm256, big_tn, 0, smem);
+  else
+    pp_tile<128, BK>(X, M, K, map, epi, blockIdx.x - n_big, (M + 127) / 128, tiles_n - big_tn,
+                     big_tn, smem);
 }
 
 }  // namespace dl
