@@ -25,6 +25,12 @@ CASES = [  # dtype, context lengths, new tokens per sequence, Hq, Hkv, D, BS
     (torch.bfloat16, [300, 77], [300, 2], 8, 4, 64, 64),
     (torch.float32, [40, 17, 90], [7, 17, 1], 4, 4, 64, 16),
     (torch.float32, [129, 300], [5, 130], 8, 2, 128, 32),
+    # at most 32 rows per kv head: the narrow kernel
+    (torch.bfloat16, [133, 4, 700, 2056], [4, 4, 1, 4], 8, 1, 128, 128),
+    (torch.bfloat16, [513, 128, 1000, 7, 4096], [4, 9, 1, 7, 32], 32, 32, 128, 128),
+    (torch.bfloat16, [77, 2049, 300, 4000], [8, 3, 1, 0], 32, 8, 128, 16),
+    (torch.bfloat16, [65, 1000], [16, 2], 8, 4, 64, 32),
+    (torch.float32, [300, 31], [3, 31], 4, 4, 128, 64),
 ]
 
 
@@ -104,11 +110,12 @@ def test_paged_qlens_whole_sequence_matches_prefill_kernel():
     assert_bf16_close(host(out), host(pre), "whole sequence vs prefill kernel")
 
 
-def test_paged_qlens_permutation_bit_identical():
+@pytest.mark.parametrize("qlens", [[4, 9, 1, 7], [4, 8, 1, 7]])   # wide, narrow kernel
+def test_paged_qlens_permutation_bit_identical(qlens):
     dtype = torch.bfloat16
     outs = []
     for identity in (True, False):
-        ctx, bt, kbits, vbits, cu, q = setup(dtype, [513, 128, 1000, 7], [4, 9, 1, 7], 32, 8, 128,
+        ctx, bt, kbits, vbits, cu, q = setup(dtype, [513, 128, 1000, 7], qlens, 32, 8, 128,
                                              128, identity=identity)
         if identity:
             q0 = q

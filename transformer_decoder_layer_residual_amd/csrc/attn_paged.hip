@@ -76,17 +76,23 @@ PagedPlan plan_paged(int B, int Hq, int Hkv, int max_q_len, int max_context_len,
                      int Tq) {
   PagedPlan pl{};
   const int G = Hq / Hkv;
-  pl.qb = kPgRows / G;
+  // at most 32 rows per kv head: the narrow kernel (one workgroup per CU,
+  // splits of up to 8192 keys: its per-workgroup start and merge cost made
+  // 1024-key splits 20% slower than 4096-key ones); else 128-row tiles
+  pl.narrow = max_q_len * G <= 32 ? 1 : 0;
+  pl.qb = (pl.narrow ? 32 : kPgRows) / G;
   pl.max_qt = max_q_len > 0 ? (max_q_len + pl.qb - 1) / pl.qb : 0;
-  const int unit = BS > kPgBKV ? BS : kPgBKV;
-  // at least ~2048 workgroups at the longest context, splits of 256..1024 keys
+  const int unit = pl.narrow ? (BS > 128 ? BS : 128) : (BS > kPgBKV ? BS : kPgBKV);
+  // enough workgroups at the longest context (~2048 wide, ~1024 narrow)
   const long items = (long)B * Hkv * (pl.max_qt > 0 ? pl.max_qt : 1);
-  const int want = (int)((2048 + items - 1) / items);
+  const int target = pl.narrow ? 1024 : 2048;
+  const int want = (int)((target + items - 1) / items);
   int ck = (max_context_len + want - 1) / want;
   ck = (ck + unit - 1) / unit * unit;
   const int lo = unit > 256 ? unit : 256;
+  const int hi = pl.narrow ? 8192 : 1024;  // the narrow kernel's kPnMaxSplit
   if (ck < lo) ck = lo;
-  if (ck > 1024) ck = 1024;
+  if (ck > hi) ck = hi;
   pl.ck = ck;
   pl.max_sp = max_context_len > 0 ? (max_context_len + ck - 1) / ck : 1;
   pl.ws_bytes = (size_t)Tq * Hq * pl.max_sp * (D + 2) * sizeof(float);
@@ -337,6 +343,289 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow variant: at most 32 query rows per kv head (verification batches:
+// q_len * G <= 32), where the wide kernel above is memory-latency bound (one
+// tile in flight behind a workgroup barrier).  Here every wave runs its own
+// key stream over the split -- 32-key steps w, w + 4, w + 8, ... -- for all
+// 32 rows: K rows are loaded straight into the MFMA operand registers, V rows
+// go through a wave-private LDS area to be transposed (pairs of keys written
+// as 4-byte words), NB steps of loads are in flight per wave, and nothing in
+// the key loop waits on another wave.  The four waves' (m, l, o) are merged
+// through LDS at the end, and the split's partials go to the same workspace
+// layout as the wide kernel's, for the same combine.
+// ---------------------------------------------------------------------------
+constexpr int kPnKeys = 32;            // keys per wave step
+constexpr int kPnMaxSplit = 8192;      // keys per split, at most
+constexpr int kPnMaxSplitBlocks = kPnMaxSplit / 16;
+
+// DEPTH: wave steps in flight (2 measured best on the 7B verification batch:
+// 5.6 TB/s against 5.5 and 5.4 for 3 and 4, with 4096-key splits)
+template <typename T, int D, int DEPTH = 2>
+__global__ void __launch_bounds__(256, 1)
+attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
+                         const T* __restrict__ vc, const int32_t* __restrict__ bt, int max_blocks,
+                         const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens,
+                         int B, int Hq, int Hkv, int BS, float scale_log2, int ck, int max_qt,
+                         int max_sp, int max_ctx, float* __restrict__ ws, int num_blocks) {
+  constexpr int VE = 16 / sizeof(T);
+  constexpr int QS = 2, KTS = kPnKeys / 16, DC = D / 32, DS = D / 16;
+  constexpr int VLS = kPnKeys + VE;                      // padded V^T row (keys)
+  constexpr int V_IT = (kPnKeys / 2) * (D / VE) / 64;    // key-pair loads per lane per step
+  static_assert(V_IT * 64 == (kPnKeys / 2) * (D / VE), "V split");
+  __shared__ __attribute__((aligned(16))) T Vt[4][D * VLS];
+  __shared__ __attribute__((aligned(16))) float red_o[4][32][D + 4];
+  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ int phys_s[kPnMaxSplitBlocks];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const int G = Hq / Hkv, QB = 32 / G;
+  const int g = blockIdx.x % Hkv, item = blockIdx.x / Hkv;
+
+  // ---- item -> (sequence, query tile, split), as in the wide kernel
+  auto counts = [&](int bb, int& nqt, int& nsp) {
+    const PgSeq s(cu_q, ctx_lens, bb, max_blocks, BS, max_ctx);
+    nqt = s.ql > 0 ? min((s.ql + QB - 1) / QB, max_qt) : 0;
+    nsp = s.ctx > 0 ? min((s.ctx + ck - 1) / ck, max_sp) : 0;
+  };
+  int b = -1, local = 0;
+  for (int b0 = 0, base = 0; b0 < B; b0 += kWave) {
+    int nqt = 0, nsp = 0;
+    if (b0 + lane < B) counts(b0 + lane, nqt, nsp);
+    const int n = nqt * nsp;
+    int inc = n;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += y;
+    }
+    const int total = __shfl(inc, kWave - 1, kWave);
+    if (item < base + total) {
+      const bool mine = item >= base + inc - n && item < base + inc;
+      const int L = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      b = b0 + L;
+      local = item - base - __shfl(inc - n, L, kWave);
+      break;
+    }
+    base += total;
+  }
+  if (b < 0) return;
+  const PgSeq sq(cu_q, ctx_lens, b, max_blocks, BS, max_ctx);
+  int nqt, nsp;
+  counts(b, nqt, nsp);
+  const int qt = local / nsp, sp = local % nsp;
+  const int i_end = min(sq.ql, (qt + 1) * QB);
+  const int kbeg = sp * ck;
+  const int kend = min(min(sq.ctx, kbeg + ck), sq.first + i_end);
+  if (kend <= kbeg) return;
+  const int nb = (kend - kbeg + BS - 1) / BS;
+  if (tid < nb) {
+    const int p = bt[(int64_t)b * max_blocks + kbeg / BS + tid];
+    phys_s[tid] = (p < 0 || p >= num_blocks) ? 0 : p;
+  }
+
+  // ---- the 32 query rows r = 16 qs + fr: token r / G of the tile, head r % G
+  int tok[QS], lim[QS];
+  bool valid[QS];
+  Frag<T> qf[QS][DC];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    const int r = 16 * qs + fr;
+    tok[qs] = qt * QB + r / G;
+    valid[qs] = tok[qs] < sq.ql;
+    lim[qs] = valid[qs] ? sq.first + tok[qs] : -1;   // last visible position
+    const int head = g * G + r % G;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) {
+      if (valid[qs])
+        qf[qs][dc].load(q + ((int64_t)(sq.q0 + tok[qs]) * Hq + head) * D + dc * 32 + 8 * fg);
+      else
+        qf[qs][dc].zero();
+    }
+  }
+  f32x4 o[DS][QS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) o[ds][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_i[QS], l_i[QS];
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    m_i[qs] = -INFINITY;
+    l_i[qs] = 0.f;
+  }
+  __syncthreads();  // phys_s
+
+  // ---- this wave's key steps: 32 keys starting at kbeg + 32 (4 j + wave)
+  const int nsteps = (kend - kbeg + kPnKeys - 1) / kPnKeys;
+  const int my_steps = nsteps > wave ? (nsteps - wave + 3) / 4 : 0;
+  auto row_off = [&](int key) -> int64_t {  // element offset of position key's row (clamped)
+    const int kk = min(key, kend - 1);
+    return (((int64_t)phys_s[(kk - kbeg) / BS] * Hkv + g) * BS + kk % BS) * D;
+  };
+  struct Buf {
+    Frag<T> k[KTS][DC];
+    u32x4 v[V_IT][2];
+  };
+  auto gload = [&](Buf& bf, int j) {  // j: this wave's step index (past the end: reloads, unused)
+    const int k0 = kbeg + kPnKeys * (4 * min(j, max(my_steps - 1, 0)) + wave);
+#pragma unroll
+    for (int ks = 0; ks < KTS; ++ks) {
+      const int64_t ro = row_off(k0 + ks * 16 + fr);
+#pragma unroll
+      for (int dc = 0; dc < DC; ++dc) bf.k[ks][dc].load(kc + ro + dc * 32 + 8 * fg);
+    }
+#pragma unroll
+    for (int u = 0; u < V_IT; ++u) {
+      const int e = lane + 64 * u, kp = e % (kPnKeys / 2), c = e / (kPnKeys / 2);
+      bf.v[u][0] = ld16(vc + row_off(k0 + 2 * kp) + c * VE);
+      bf.v[u][1] = ld16(vc + row_off(k0 + 2 * kp + 1) + c * VE);
+    }
+  };
+  T* vt = Vt[wave];
+  const u32x4 zero = {0, 0, 0, 0};
+  auto process = [&](const Buf& bf, int j) {
+    const int k0 = kbeg + kPnKeys * (4 * j + wave);
+    // S^T = K Q^T: rows keys k0 + 16 ks + 4 fg + jj, columns this lane's rows
+    f32x4 sc[KTS][QS];
+#pragma unroll
+    for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) {
+        sc[ks][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DC; ++dc) sc[ks][qs] = mfma_k32(bf.k[ks][dc], qf[qs][dc], sc[ks][qs]);
+      }
+    // V^T into this wave's LDS area (keys past the split stored as zeros)
+#pragma unroll
+    for (int u = 0; u < V_IT; ++u) {
+      const int e = lane + 64 * u, kp = e % (kPnKeys / 2), c = e / (kPnKeys / 2);
+      const u32x4 a = k0 + 2 * kp < kend ? bf.v[u][0] : zero;
+      const u32x4 bb = k0 + 2 * kp + 1 < kend ? bf.v[u][1] : zero;
+      T ea[VE], eb[VE];
+      __builtin_memcpy(ea, &a, 16);
+      __builtin_memcpy(eb, &bb, 16);
+      typedef T pair_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int x = 0; x < VE; ++x)
+        *reinterpret_cast<pair_t*>(&vt[(c * VE + x) * VLS + 2 * kp]) = pair_t{ea[x], eb[x]};
+    }
+    // online softmax per row (log2 domain)
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = k0 + ks * 16 + 4 * fg + jj;
+          const float val =
+              (key <= lim[qs] && key < kend) ? sc[ks][qs][jj] * scale_log2 : -INFINITY;
+          sc[ks][qs][jj] = val;
+          mx = fmaxf(mx, val);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_i[qs], mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_i[qs] - m_new);
+      float ls = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KTS; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float pv = sc[ks][qs][jj] == -INFINITY ? 0.f : exp2f(sc[ks][qs][jj] - m_new);
+          sc[ks][qs][jj] = pv;
+          ls += pv;
+        }
+      l_i[qs] = l_i[qs] * alpha + ls;
+      m_i[qs] = m_new;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) o[ds][qs] *= alpha;
+    }
+    // the V^T writes of every lane of this wave before the fragment reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T += V^T P^T
+    Frag<T> pf[QS];
+#pragma unroll
+    for (int qs = 0; qs < QS; ++qs) scores_to_frag(pf[qs], sc[0][qs], sc[1][qs]);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      Frag<T> vf;
+      const T* row = &vt[(ds * 16 + fr) * VLS + 4 * fg];
+      load_split_frag(vf, row, row + 16);
+#pragma unroll
+      for (int qs = 0; qs < QS; ++qs) o[ds][qs] = mfma_k32(vf, pf[qs], o[ds][qs]);
+    }
+    // every lane's fragment reads before the next step overwrites the area
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  if (my_steps > 0) {
+    // whole groups of DEPTH steps: every iteration uses the buffers in the
+    // order it refills them, so the loads in flight at the loop head are the
+    // same on entry and on the back edge and no wait has to drain them; the
+    // last group's refills (clamped past the end) are never used
+    Buf bufs[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) gload(bufs[d], d);
+    int j = 0;
+    for (; j + DEPTH <= my_steps; j += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        process(bufs[d], j + d);
+        gload(bufs[d], j + d + DEPTH);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (j + d < my_steps) process(bufs[d], j + d);
+  }
+
+  // ---- merge the four waves (fixed order) and write the split's partials
+#pragma unroll
+  for (int qs = 0; qs < QS; ++qs) {
+    float l = l_i[qs];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const int r = 16 * qs + fr;
+    if (fg == 0) {
+      red_m[wave][r] = m_i[qs];
+      red_l[wave][r] = l;
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      *reinterpret_cast<f32x4*>(&red_o[wave][r][ds * 16 + 4 * fg]) = o[ds][qs];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 32 * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    const int tk = qt * QB + r / G;
+    if (tk >= sq.ql) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][r]);
+    float oa = 0.f, la = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sw = red_m[w][r] == -INFINITY ? 0.f : exp2f(red_m[w][r] - M);
+      oa += sw * red_o[w][r][d];
+      la += sw * red_l[w][r];
+    }
+    const int head = g * G + r % G;
+    float* dst = ws + (((int64_t)(sq.q0 + tk) * Hq + head) * max_sp + sp) * (D + 2);
+    dst[d] = oa;
+    if (d == 0) {
+      dst[D] = M;
+      dst[D + 1] = la;
+    }
+  }
+}
+
 // Merge the splits of one (query token, head) in fixed order.  Token t's
 // sequence is found by binary search over cu_q; its row saw splits
 // 0 .. ceil((p_t + 1) / ck) - 1.
@@ -376,9 +665,14 @@ static hipError_t launch_paged(const T* q, const T* kc, const T* vc, const int32
                                hipStream_t st) {
   const long wgs = (long)B * pl.max_qt * pl.max_sp * Hkv;
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_paged_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q, kc, vc,
-                     bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt, pl.max_sp,
-                     max_ctx, ws, num_blocks);
+  if (pl.narrow)
+    hipLaunchKernelGGL((attn_paged_narrow_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q,
+                       kc, vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
+                       pl.max_sp, max_ctx, ws, num_blocks);
+  else
+    hipLaunchKernelGGL((attn_paged_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q, kc,
+                       vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
+                       pl.max_sp, max_ctx, ws, num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_paged_combine<T, D>), dim3(Hq, Tq), dim3(D), 0, st, ws, cu_q, ctx, B,

@@ -120,7 +120,8 @@ hipError_t attn_decode_paged_q8(const T* q, const int8_t* k_codes, const int8_t*
 
 // Paged attention for q_len >= 1 new tokens per sequence.
 struct PagedPlan {
-  int qb;         // query tokens per workgroup tile (128 rows / group size)
+  int narrow;     // 1: at most 32 rows per kv head, the narrow kernel
+  int qb;         // query tokens per workgroup tile (128 or 32 rows / group size)
   int max_qt;     // query tiles per sequence at max_q_len
   int ck;         // keys per split
   int max_sp;     // splits per sequence at max_context_len
