@@ -96,8 +96,8 @@ struct DecSlice<T, int8_t, SB> {  // INT8 codes, read as code + 128
 };
 
 // SB: bytes of a row slice per thread; DEPTH: KV blocks in flight (query
-// groups of up to two heads); MAXCB: largest split, in blocks.
-template <typename T, typename KV, int D, int G, int SB, int DEPTH, int MAXCB>
+// groups of up to two heads).
+template <typename T, typename KV, int D, int G, int SB, int DEPTH>
 __global__ void __launch_bounds__(kDecThreads)
 attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV* __restrict__ vc,
                    const float* __restrict__ ksc, const float* __restrict__ vsc,
@@ -292,24 +292,25 @@ attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV*
   };
 
   if constexpr (G <= 2) {
-    // DEPTH blocks in flight, unrolled over the largest split; leaving early
-    // is a branch out, so no join point ever mixes different numbers of
-    // loads in flight
+    // DEPTH blocks in flight, in whole groups: every iteration uses the
+    // buffers in the order it refills them, so the loads in flight at the
+    // loop head are the same on entry and on the back edge and no wait has
+    // to drain them; the last group's refills (past the split: one cached
+    // row) are never used
     Buf bufs[DEPTH];
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) gload(bufs[u], u);
-#pragma unroll
-    for (int j = 0; j < MAXCB; j += DEPTH) {
+    int j = 0;
+    for (; j + DEPTH <= nb; j += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
-        if (j + u < MAXCB) {
-          process(bufs[u], blk_begin + j + u);
-          if (j + u + 1 >= nb) goto done;
-          gload(bufs[u], j + u + DEPTH);
-        }
+        process(bufs[u], blk_begin + j + u);
+        gload(bufs[u], j + u + DEPTH);
       }
     }
-  done:;
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u)
+      if (j + u < nb) process(bufs[u], blk_begin + j + u);
   } else {
     // larger query groups keep G x D of state per thread: one block in flight
     for (int j = 0; j < nb; ++j) {
@@ -414,7 +415,7 @@ static hipError_t launch_dec(const T* q, const KV* kc, const KV* vc, const float
                              const DecodePlan& pl, float* ws, int num_blocks, hipStream_t st) {
   const dim3 grid(pl.max_splits * Hkv * B);
   constexpr int SB = DecTune<KV, G>::SB, DEPTH = DecTune<KV, G>::DEPTH;
-  hipLaunchKernelGGL((attn_decode_kernel<T, KV, D, G, SB, DEPTH, kDecMaxSplitBlocks>), grid,
+  hipLaunchKernelGGL((attn_decode_kernel<T, KV, D, G, SB, DEPTH>), grid,
                      dim3(kDecThreads), 0, st, q, kc,
                      vc, ks, vs, bt, max_blocks, ctx, B, Hq, Hkv, BS, sl2, pl.chunk_blocks,
                      pl.max_splits, ws, num_blocks);
