@@ -410,7 +410,83 @@ def main():
         torch.cuda.empty_cache()
         return out
 
+    # ------------------------------------------------ 70B-shaped GQA decode
+    def run_gqa_decode():
+        """Llama-2-70B-shaped layer (random weights, 64/8 heads): decode at B4
+        with 4096-token contexts and at B1 with 32768.  At these batches the
+        step reads every weight once; attention reads the whole KV cache."""
+        c5 = gen.CONFIGS[5]
+        lay = DeviceLayer.build(c5, max_pos=max(c for _, c in c5.extra["cases"]) + 1)
+        H5, Hq5, Hkv5, D5, I5 = c5.hidden, c5.n_q_heads, c5.n_kv_heads, c5.head_dim, \
+            c5.intermediate
+        w_bytes = 2.0 * (H5 * (Hq5 + 2 * Hkv5) * D5 + Hq5 * D5 * H5 + 3 * H5 * I5)
+        outs = []
+        for case in range(len(c5.extra["cases"])):
+            ctx = gen.decode_context_lens(c5, case)
+            B5, mx = ctx.size, int(ctx.max())
+            bt5 = gen.block_table(c5, ctx)
+            kb, vb = gen.synthetic_cache(c5, bt5, ctx, case=case)
+            kc5, vc5 = cache_dev(kb), cache_dev(vb)
+            del kb, vb
+            bt5d = i32(bt5.table)
+            x5 = to_dev(gen.hidden(c5, B5, step=11 + case), torch.float32)
+            y5 = torch.empty_like(x5)
+            p5, c5d = i32(ctx - 1), i32(ctx)
+            ws5 = torch.empty(dl.dl_layer_workspace_size(lay.dims, B5, B5, 0, mx, mode),
+                              dtype=torch.uint8, device="cuda:0")
+
+            def step5():
+                dl.dl_layer_decode(lay.dims, lay.w, lay.cs, x5, y5, p5, c5d, mx, kc5, vc5, bt5d,
+                                   ws=ws5)
+
+            for _ in range(args.warmup):
+                step5()
+            torch.cuda.synchronize()
+            ems = time_launches(step5, max(args.steps, 20), stream)
+            side = torch.cuda.Stream()
+            g5 = dl.DecodeGraph(lay.dims, lay.w, lay.cs, x5, y5, p5, c5d, mx, kc5, vc5, bt5d,
+                                side, ws=ws5)
+            for _ in range(args.warmup):
+                g5.launch()
+            side.synchronize()
+            gms = time_launches(g5.launch, max(args.steps, 20), side)
+            g5.close()
+            q5 = torch.empty(B5, Hq5, D5, dtype=torch.bfloat16, device="cuda:0").normal_()
+            ao = torch.empty_like(q5)
+            aws = torch.empty(dl.lib().dl_attn_decode_workspace_size(B5, Hq5, Hkv5, D5, mx,
+                                                                     c5.block_size),
+                              dtype=torch.uint8, device="cuda:0")
+
+            def attn5():
+                dl.dl_attn_decode_paged(q5, kc5, vc5, bt5d, c5d, mx, ao, ws=aws)
+
+            for _ in range(3):
+                attn5()
+            a_ms = time_launches(attn5, max(args.steps, 20), stream)
+            kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv5 * D5 * 2
+            a_bytes = kv_bytes + 2.0 * B5 * Hq5 * D5 * 2
+            a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+            outs.append({
+                "workload": "llama2-70b-layer-decode-b%d-ctx%d" % (B5, mx), "batch": B5,
+                "context": mx, "value": round(B5 / (ems * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(ems, 4), "graph_ms_per_step": round(gms, 4),
+                "graph_step_hbm_frac": round((w_bytes + kv_bytes) / (gms * 1e-3) / 1e9
+                                             / PEAK_HBM_GBS, 4),
+                "attention": {"kernel": "paged decode attention, 8-head query groups "
+                              "(split-KV + combine)", "achieved": round(a_gbs, 1),
+                              "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4),
+                              "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)}})
+            log(f"[bench] 70B decode B{B5} x {mx}: eager {ems:.4f} ms, graph {gms:.4f} ms per "
+                f"step ({outs[-1]['graph_step_hbm_frac'] * 100:.0f}% of HBM peak); attention "
+                f"{a_ms * 1e3:.1f} us = {a_gbs:,.0f} GB/s")
+            del kc5, vc5, ws5, aws
+            torch.cuda.empty_cache()
+        del lay
+        torch.cuda.empty_cache()
+        return outs
+
     if not args.no_decode:
+        result["decode_gqa_70b"] = run_gqa_decode()
         result["decode_small_batch"] = run_small_decode()
         result["decode"] = run_decode(False)
         if not args.no_int8:

@@ -337,6 +337,12 @@ DECODE_CASES = [  # B, ctx list, Hq, Hkv, D, BS
     (1, [1], 4, 4, 64, 16), (3, [5, 16, 17], 4, 4, 64, 16), (4, [130, 1, 700, 2049], 8, 1, 128, 128),
     (5, [127, 128, 129, 300, 64], 32, 8, 128, 128), (2, [4096, 3000], 8, 8, 128, 128),
     (3, [33, 64, 65], 8, 4, 64, 32),
+    # query groups of 4 and 8 with at least 131072 (kv head, key) pairs at
+    # the longest context: the narrow paged kernel
+    (8, [2048, 1, 700, 1500, 129, 2047, 64, 1000], 32, 8, 128, 16),
+    (4, [4096, 1, 3000, 4095], 64, 8, 128, 128),
+    (16, [1024, 5, 300, 1023, 17, 640, 999, 128, 1, 77, 512, 800, 33, 1000, 256, 700],
+     32, 8, 64, 32),
 ]
 
 

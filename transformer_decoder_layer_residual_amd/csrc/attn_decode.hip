@@ -41,6 +41,7 @@
 // is carried next to the softmax denominator.
 #include <type_traits>
 
+#include "attn_combine.hpp"
 #include "dl_internal.hpp"
 
 namespace dl {
@@ -62,6 +63,20 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int B
   pl.chunk_blocks = cb;
   pl.max_splits = nblk > 0 ? (nblk + cb - 1) / cb : 1;
   pl.ws_bytes = (size_t)B * Hq * pl.max_splits * (D + 2) * sizeof(float);
+  // Query groups of 4 or 8 heads with enough work go through the narrow
+  // paged kernel (MFMA over the group's rows): every thread of this kernel
+  // would hold G x D of state and reduce G partial dots per token with lane
+  // shuffles, which held it to 1.5 TB/s at 70B (G 8) and 3.6-4.0 TB/s at 8B
+  // B64 (G 4) against 4.6 and 4.3 TB/s for the narrow kernel.  Below 131072
+  // (kv head, key) pairs at the longest context this kernel stays faster
+  // (8B B8 at contexts up to 1100: 11 us against 13 us).
+  const int G = Hq / Hkv;
+  if (G >= 4 && (double)B * Hkv * max_context_len >= 131072.0) {
+    pl.narrow_ck = narrow_split(B, Hkv, max_context_len, BS);
+    pl.narrow_sp = (max_context_len + pl.narrow_ck - 1) / pl.narrow_ck;
+    const size_t w = (size_t)B * Hq * pl.narrow_sp * (D + 2) * sizeof(float);
+    if (w > pl.ws_bytes) pl.ws_bytes = w;
+  }
   return pl;
 }
 
@@ -291,7 +306,7 @@ attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV*
     }
   };
 
-  if constexpr (G <= 2) {
+  if constexpr (DEPTH >= 2) {
     // DEPTH blocks in flight, in whole groups: every iteration uses the
     // buffers in the order it refills them, so the loads in flight at the
     // loop head are the same on entry and on the back edge and no wait has
@@ -312,7 +327,8 @@ attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV*
     for (int u = 0; u < DEPTH - 1; ++u)
       if (j + u < nb) process(bufs[u], blk_begin + j + u);
   } else {
-    // larger query groups keep G x D of state per thread: one block in flight
+    // one block in flight (for query groups whose G x D of state per thread
+    // leaves no registers for a second block)
     for (int j = 0; j < nb; ++j) {
       Buf ba;
       gload(ba, j);
@@ -374,38 +390,30 @@ attn_decode_kernel(const T* __restrict__ q, const KV* __restrict__ kc, const KV*
 
 // Combine the splits of one (sequence, head) in fixed order.
 template <typename T, int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kCombineThreads)
 attn_decode_combine(const float* __restrict__ ws, const int32_t* __restrict__ ctx,
                     T* __restrict__ out, int Hq, int BS, int chunk_blocks, int max_splits) {
-  const int b = blockIdx.y, h = blockIdx.x, d = threadIdx.x;
+  const int b = blockIdx.y, h = blockIdx.x;
   const int nblk = (ctx[b] + BS - 1) / BS;
   const int ns = min((nblk + chunk_blocks - 1) / chunk_blocks, max_splits);
-  const float* base = ws + ((int64_t)b * Hq + h) * max_splits * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* p = base + s * (D + 2);
-    const float w = exp2f(p[D] - M);
-    num += w * p[d];
-    den += w * p[D + 1];
-  }
-  out[((int64_t)b * Hq + h) * D + d] = from_f32<T>(num / den);
+  combine_row<T, D>(ws + ((int64_t)b * Hq + h) * max_splits * (D + 2), ns,
+                    out + ((int64_t)b * Hq + h) * D);
 }
 
 // Slice size and pipeline depth.  Layer-dtype caches: 16-byte slices, two
 // blocks in flight.  INT8: 16-byte slices (16 codes) for query groups of up
 // to two heads, measured 5.4 TB/s on the 7B decode shape against 4.7-5.3 TB/s
 // for 8-byte slices, whose blocks carry half the bytes per load; deeper
-// pipelines (3, 4 blocks) gained nothing.  Larger groups keep 8-byte slices,
-// since every thread holds G x VE query and output values.
+// pipelines (3, 4 blocks) gained nothing.  Larger groups keep 8-byte slices
+// and one block in flight, since every thread holds G x VE query and output
+// values (a second block spilled registers at G 8 and ran slower at G 4).
 template <typename KV, int G>
 struct DecTune {
-  static constexpr int SB = 16, DEPTH = 2;
+  static constexpr int SB = 16, DEPTH = G <= 2 ? 2 : 1;
 };
 template <int G>
 struct DecTune<int8_t, G> {
-  static constexpr int SB = G <= 2 ? 16 : 8, DEPTH = 2;
+  static constexpr int SB = G <= 2 ? 16 : 8, DEPTH = G <= 2 ? 2 : 1;
 };
 
 template <typename T, typename KV, int D, int G>
@@ -457,10 +465,10 @@ static hipError_t decode_impl(const T* q, const KV* k_cache, const KV* v_cache,
     return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
   if (D == 128)
-    hipLaunchKernelGGL((attn_decode_combine<T, 128>), dim3(Hq, B), dim3(128), 0, st, w,
+    hipLaunchKernelGGL((attn_decode_combine<T, 128>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w,
                        context_lens, out, Hq, BS, pl.chunk_blocks, pl.max_splits);
   else
-    hipLaunchKernelGGL((attn_decode_combine<T, 64>), dim3(Hq, B), dim3(64), 0, st, w,
+    hipLaunchKernelGGL((attn_decode_combine<T, 64>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w,
                        context_lens, out, Hq, BS, pl.chunk_blocks, pl.max_splits);
   return hipGetLastError();
 }
@@ -471,6 +479,10 @@ hipError_t attn_decode_paged(const T* q, const T* k_cache, const T* v_cache,
                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
                              float scale, T* out, const DecodePlan& pl, void* ws, int num_blocks,
                              hipStream_t st) {
+  if (pl.narrow_ck > 0)
+    return attn_decode_narrow<T>(q, k_cache, v_cache, block_table, max_blocks, context_lens, B, Hq,
+                                 Hkv, D, BS, pl.narrow_sp * pl.narrow_ck, scale, out,
+                                 pl.narrow_ck, pl.narrow_sp, ws, num_blocks, st);
   return decode_impl<T, T>(q, k_cache, v_cache, nullptr, nullptr, block_table, max_blocks,
                            context_lens, B, Hq, Hkv, D, BS, scale, out, pl, ws, num_blocks, st);
 }

@@ -29,6 +29,7 @@
 //     whose rows are padding or see none of a tile skip its MFMAs;
 //   * every (row, split) writes its unnormalised (o, m, l); a second kernel
 //     merges the splits of each row in fixed order.
+#include "attn_combine.hpp"
 #include "dl_internal.hpp"
 
 namespace dl {
@@ -58,19 +59,48 @@ __device__ __forceinline__ void load_split_frag(Frag<float>& f, const float* p0,
 }
 
 // Per-sequence geometry shared by both kernels; every count is clamped to
-// what the host sized the grid and the workspace for.
+// what the host sized the grid and the workspace for.  cu_q == nullptr: one
+// new token per sequence (the decode step).
 struct PgSeq {
   int q0, ql, ctx, first;  // first = position of new token 0
   __device__ PgSeq(const int32_t* cu_q, const int32_t* ctx_lens, int b, int max_blocks, int BS,
                    int max_ctx) {
-    q0 = cu_q[b];
-    ql = max(cu_q[b + 1] - q0, 0);
+    q0 = cu_q ? cu_q[b] : b;
+    ql = cu_q ? max(cu_q[b + 1] - q0, 0) : 1;
     ctx = min(min(ctx_lens[b], max_blocks * BS), max_ctx);
     first = ctx - ql;
   }
 };
 
+// Splits that hold keys of the row at position p (keys 0 .. p).
+__device__ __forceinline__ int row_splits(int p, int ck, int max_sp) {
+  return p >= 0 ? min((p + ck) / ck, max_sp) : 0;
+}
+
 }  // namespace
+
+constexpr int kPnKeys = 32;            // keys per wave step
+constexpr int kPnMaxSplit = 8192;      // keys per split, at most
+constexpr int kPnMaxSplitBlocks = kPnMaxSplit / 16;
+
+// Keys per split for the narrow kernel: as large as keeps about one (uniform
+// contexts, B <= 8) or two (ragged contexts) workgroups per CU over the
+// estimated work (every sequence at max_ctx, or at half of it when ragged).
+// Measured optimum on the 7B verification batch (4096), the 8B B64 decode
+// (2048), 70B B4 x 4096 (512) and 70B B1 x 32768 (1024).
+int narrow_split(int B, int Hkv, int max_ctx, int BS) {
+  const int unit = BS > 128 ? BS : 128;
+  const bool ragged = B > 8;
+  const double work = (double)B * Hkv * max_ctx * (ragged ? 0.5 : 1.0);
+  int ck = (int)(work / (256.0 * (ragged ? 2 : 1)));
+  const int cap = (max_ctx + unit - 1) / unit * unit;
+  if (ck > cap) ck = cap;
+  ck = (ck + unit - 1) / unit * unit;
+  const int lo = unit > 256 ? unit : 256;
+  if (ck < lo) ck = lo;
+  if (ck > kPnMaxSplit) ck = kPnMaxSplit / unit * unit;
+  return ck;
+}
 
 PagedPlan plan_paged(int B, int Hq, int Hkv, int max_q_len, int max_context_len, int BS, int D,
                      int Tq) {
@@ -82,19 +112,21 @@ PagedPlan plan_paged(int B, int Hq, int Hkv, int max_q_len, int max_context_len,
   pl.narrow = max_q_len * G <= 32 ? 1 : 0;
   pl.qb = (pl.narrow ? 32 : kPgRows) / G;
   pl.max_qt = max_q_len > 0 ? (max_q_len + pl.qb - 1) / pl.qb : 0;
-  const int unit = pl.narrow ? (BS > 128 ? BS : 128) : (BS > kPgBKV ? BS : kPgBKV);
-  // enough workgroups at the longest context (~2048 wide, ~1024 narrow)
-  const long items = (long)B * Hkv * (pl.max_qt > 0 ? pl.max_qt : 1);
-  const int target = pl.narrow ? 1024 : 2048;
-  const int want = (int)((target + items - 1) / items);
-  int ck = (max_context_len + want - 1) / want;
-  ck = (ck + unit - 1) / unit * unit;
-  const int lo = unit > 256 ? unit : 256;
-  const int hi = pl.narrow ? 8192 : 1024;  // the narrow kernel's kPnMaxSplit
-  if (ck < lo) ck = lo;
-  if (ck > hi) ck = hi;
-  pl.ck = ck;
-  pl.max_sp = max_context_len > 0 ? (max_context_len + ck - 1) / ck : 1;
+  if (pl.narrow) {
+    pl.ck = narrow_split(B, Hkv, max_context_len, BS);
+  } else {
+    // at least ~2048 workgroups at the longest context, splits of 256..1024 keys
+    const int unit = BS > kPgBKV ? BS : kPgBKV;
+    const long items = (long)B * Hkv * (pl.max_qt > 0 ? pl.max_qt : 1);
+    const int want = (int)((2048 + items - 1) / items);
+    int ck = (max_context_len + want - 1) / want;
+    ck = (ck + unit - 1) / unit * unit;
+    const int lo = unit > 256 ? unit : 256;
+    if (ck < lo) ck = lo;
+    if (ck > 1024) ck = 1024;
+    pl.ck = ck;
+  }
+  pl.max_sp = max_context_len > 0 ? (max_context_len + pl.ck - 1) / pl.ck : 1;
   pl.ws_bytes = (size_t)Tq * Hq * pl.max_sp * (D + 2) * sizeof(float);
   return pl;
 }
@@ -105,7 +137,7 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
                   const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ cu_q,
                   const int32_t* __restrict__ ctx_lens, int B, int Hq, int Hkv, int BS,
                   float scale_log2, int ck, int max_qt, int max_sp, int max_ctx,
-                  float* __restrict__ ws, int num_blocks) {
+                  float* __restrict__ ws, int num_blocks, T* __restrict__ out) {
   constexpr int NT = 256, BKV = kPgBKV, VE = 16 / sizeof(T);
   constexpr int QS = 2, KTS = BKV / 16, DC = D / 32, DS = D / 16, KC = BKV / 32;
   constexpr int KLS = D + VE, VLS = BKV + VE;
@@ -330,15 +362,26 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
     float l = l_i[qs];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
-    if (valid[qs]) {
-      float* dst = ws + (((int64_t)(sq.q0 + tok[qs]) * Hq + head[qs]) * max_sp + sp) * (D + 2);
+    if (!valid[qs]) continue;
+    const int64_t row = (int64_t)(sq.q0 + tok[qs]) * Hq + head[qs];
+    if (row_splits(sq.first + tok[qs], ck, max_sp) == 1) {
+      // the row's only split: its output, normalised (the combine skips it)
+      if (sp == 0) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        store4(dst + ds * 16 + 4 * fg, o[ds][qs][0], o[ds][qs][1], o[ds][qs][2], o[ds][qs][3]);
-      if (fg == 0) {
-        dst[D] = m_i[qs];
-        dst[D + 1] = l;
+        for (int ds = 0; ds < DS; ++ds)
+          store4(out + row * D + ds * 16 + 4 * fg, o[ds][qs][0] * inv, o[ds][qs][1] * inv,
+                 o[ds][qs][2] * inv, o[ds][qs][3] * inv);
       }
+      continue;
+    }
+    float* dst = ws + (row * max_sp + sp) * (D + 2);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      store4(dst + ds * 16 + 4 * fg, o[ds][qs][0], o[ds][qs][1], o[ds][qs][2], o[ds][qs][3]);
+    if (fg == 0) {
+      dst[D] = m_i[qs];
+      dst[D + 1] = l;
     }
   }
 }
@@ -355,9 +398,6 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
 // through LDS at the end, and the split's partials go to the same workspace
 // layout as the wide kernel's, for the same combine.
 // ---------------------------------------------------------------------------
-constexpr int kPnKeys = 32;            // keys per wave step
-constexpr int kPnMaxSplit = 8192;      // keys per split, at most
-constexpr int kPnMaxSplitBlocks = kPnMaxSplit / 16;
 
 // DEPTH: wave steps in flight (2 measured best on the 7B verification batch:
 // 5.6 TB/s against 5.5 and 5.4 for 3 and 4, with 4096-key splits)
@@ -367,7 +407,8 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
                          const T* __restrict__ vc, const int32_t* __restrict__ bt, int max_blocks,
                          const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens,
                          int B, int Hq, int Hkv, int BS, float scale_log2, int ck, int max_qt,
-                         int max_sp, int max_ctx, float* __restrict__ ws, int num_blocks) {
+                         int max_sp, int max_ctx, float* __restrict__ ws, int num_blocks,
+                         T* __restrict__ out) {
   constexpr int VE = 16 / sizeof(T);
   constexpr int QS = 2, KTS = kPnKeys / 16, DC = D / 32, DS = D / 16;
   constexpr int VLS = kPnKeys + VE;                      // padded V^T row (keys)
@@ -420,9 +461,9 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
   const int kend = min(min(sq.ctx, kbeg + ck), sq.first + i_end);
   if (kend <= kbeg) return;
   const int nb = (kend - kbeg + BS - 1) / BS;
-  if (tid < nb) {
-    const int p = bt[(int64_t)b * max_blocks + kbeg / BS + tid];
-    phys_s[tid] = (p < 0 || p >= num_blocks) ? 0 : p;
+  for (int i = tid; i < nb; i += 256) {  // up to kPnMaxSplitBlocks (512) entries
+    const int p = bt[(int64_t)b * max_blocks + kbeg / BS + i];
+    phys_s[i] = (p < 0 || p >= num_blocks) ? 0 : p;
   }
 
   // ---- the 32 query rows r = 16 qs + fr: token r / G of the tile, head r % G
@@ -616,8 +657,13 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
       oa += sw * red_o[w][r][d];
       la += sw * red_l[w][r];
     }
-    const int head = g * G + r % G;
-    float* dst = ws + (((int64_t)(sq.q0 + tk) * Hq + head) * max_sp + sp) * (D + 2);
+    const int64_t row = (int64_t)(sq.q0 + tk) * Hq + g * G + r % G;
+    if (row_splits(sq.first + tk, ck, max_sp) == 1) {
+      // the row's only split: its output, normalised (the combine skips it)
+      if (sp == 0) out[row * D + d] = from_f32<T>(la > 0.f ? oa / la : 0.f);
+      continue;
+    }
+    float* dst = ws + (row * max_sp + sp) * (D + 2);
     dst[d] = oa;
     if (d == 0) {
       dst[D] = M;
@@ -628,33 +674,25 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 
 // Merge the splits of one (query token, head) in fixed order.  Token t's
 // sequence is found by binary search over cu_q; its row saw splits
-// 0 .. ceil((p_t + 1) / ck) - 1.
+// 0 .. ceil((p_t + 1) / ck) - 1.  A row with one split was written by the
+// attention kernel itself.
 template <typename T, int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kCombineThreads)
 attn_paged_combine(const float* __restrict__ ws, const int32_t* __restrict__ cu_q,
                    const int32_t* __restrict__ ctx_lens, int B, int Hq, int BS, int max_blocks,
                    int ck, int max_sp, int max_ctx, T* __restrict__ out) {
-  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
-  int lo = 0, hi = B;  // largest b with cu_q[b] <= t
-  while (hi - lo > 1) {
+  const int h = blockIdx.x, t = blockIdx.y;
+  int lo = cu_q ? 0 : t, hi = B;  // largest b with cu_q[b] <= t
+  while (cu_q && hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cu_q[mid] <= t) lo = mid;
     else hi = mid;
   }
   const PgSeq sq(cu_q, ctx_lens, lo, max_blocks, BS, max_ctx);
-  const int p = sq.first + (t - sq.q0);
-  const int ns = p >= 0 ? min((p + ck) / ck, max_sp) : 0;
-  const float* base = ws + ((int64_t)t * Hq + h) * max_sp * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * (D + 2) + D]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* ps = base + s * (D + 2);
-    const float w = ps[D] == -INFINITY ? 0.f : exp2f(ps[D] - M);
-    num += w * ps[d];
-    den += w * ps[D + 1];
-  }
-  out[((int64_t)t * Hq + h) * D + d] = from_f32<T>(den > 0.f ? num / den : 0.f);
+  const int ns = row_splits(sq.first + (t - sq.q0), ck, max_sp);
+  if (ns == 1) return;  // written by the attention kernel
+  combine_row<T, D>(ws + ((int64_t)t * Hq + h) * max_sp * (D + 2), ns,
+                    out + ((int64_t)t * Hq + h) * D);
 }
 
 template <typename T, int D>
@@ -668,14 +706,14 @@ static hipError_t launch_paged(const T* q, const T* kc, const T* vc, const int32
   if (pl.narrow)
     hipLaunchKernelGGL((attn_paged_narrow_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q,
                        kc, vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
-                       pl.max_sp, max_ctx, ws, num_blocks);
+                       pl.max_sp, max_ctx, ws, num_blocks, out);
   else
     hipLaunchKernelGGL((attn_paged_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q, kc,
                        vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
-                       pl.max_sp, max_ctx, ws, num_blocks);
+                       pl.max_sp, max_ctx, ws, num_blocks, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_paged_combine<T, D>), dim3(Hq, Tq), dim3(D), 0, st, ws, cu_q, ctx, B,
+  hipLaunchKernelGGL((attn_paged_combine<T, D>), dim3(Hq, Tq), dim3(kCombineThreads), 0, st, ws, cu_q, ctx, B,
                      Hq, BS, max_blocks, pl.ck, pl.max_sp, max_ctx, out);
   return hipGetLastError();
 }
@@ -699,6 +737,49 @@ hipError_t attn_paged_qlens(const T* q, const T* k_cache, const T* v_cache,
                                st);
   return hipErrorInvalidValue;
 }
+
+// The decode step (one new token per sequence) through the narrow kernel.
+template <typename T>
+hipError_t attn_decode_narrow(const T* q, const T* k_cache, const T* v_cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                              int max_context_len, float scale, T* out, int ck, int max_sp,
+                              void* ws, int num_blocks, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const float sl2 = scale * 1.4426950408889634f;
+  float* w = reinterpret_cast<float*>(ws);
+  const long wgs = (long)B * max_sp * Hkv;
+  if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
+  if (D == 128) {
+    hipLaunchKernelGGL((attn_paged_narrow_kernel<T, 128>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, Hq,
+                       Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_paged_combine<T, 128>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w, nullptr,
+                       context_lens, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
+  } else if (D == 64) {
+    hipLaunchKernelGGL((attn_paged_narrow_kernel<T, 64>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, Hq,
+                       Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_paged_combine<T, 64>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w, nullptr,
+                       context_lens, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template hipError_t attn_decode_narrow<bf16>(const bf16*, const bf16*, const bf16*,
+                                             const int32_t*, int, const int32_t*, int, int, int,
+                                             int, int, int, float, bf16*, int, int, void*, int,
+                                             hipStream_t);
+template hipError_t attn_decode_narrow<float>(const float*, const float*, const float*,
+                                              const int32_t*, int, const int32_t*, int, int, int,
+                                              int, int, int, float, float*, int, int, void*, int,
+                                              hipStream_t);
 
 template hipError_t attn_paged_qlens<bf16>(const bf16*, const bf16*, const bf16*, const int32_t*,
                                            int, const int32_t*, const int32_t*, int, int, int,

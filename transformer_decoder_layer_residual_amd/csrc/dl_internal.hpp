@@ -101,6 +101,8 @@ struct DecodePlan {
   int chunk_blocks;  // KV blocks per split
   int max_splits;    // splits per sequence at max_context_len
   size_t ws_bytes;
+  int narrow_ck;     // > 0: layer-dtype caches go through the narrow paged kernel
+  int narrow_sp;     //      with splits of narrow_ck keys, narrow_sp of them at most
 };
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int max_context_len, int BS);
 
@@ -117,6 +119,16 @@ hipError_t attn_decode_paged_q8(const T* q, const int8_t* k_codes, const int8_t*
                                 const int32_t* context_lens, int B, int Hq, int Hkv, int D,
                                 int BS, float scale, T* out, const DecodePlan& pl, void* ws,
                                 int num_blocks, hipStream_t st);
+
+// Keys per split of the narrow paged kernel.
+int narrow_split(int B, int Hkv, int max_ctx, int BS);
+// Decode step (one token per sequence) through the narrow paged kernel.
+template <typename T>
+hipError_t attn_decode_narrow(const T* q, const T* k_cache, const T* v_cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* context_lens, int B, int Hq, int Hkv, int D, int BS,
+                              int max_context_len, float scale, T* out, int ck, int max_sp,
+                              void* ws, int num_blocks, hipStream_t st);
 
 // Paged attention for q_len >= 1 new tokens per sequence.
 struct PagedPlan {

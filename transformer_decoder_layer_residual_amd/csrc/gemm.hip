@@ -47,26 +47,17 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   const int nt = tiles(cfg);
   const int ktiles = (K + bk - 1) / bk;
   if (cfg == kCfgSkinny) {
-    // K slice of 2048, 1024 or 512 (whole stage pairs) with the least modelled
-    // time: the persistent workgroups take items in rounds; a round streams one
-    // item per busy workgroup at min(40 GB/s, 5.6 TB/s / busy workgroups)
-    // (measured per-workgroup and whole-chip streaming rates), plus the fp32
-    // partial sums written and re-read at 5.6 TB/s
-    int best_kc = 8 * kSkKS;
-    double best = 1e300;
-    for (int kc = 8 * kSkKS; kc >= 2 * kSkKS; kc /= 2) {
-      if (kc >= 2 * K && kc > 2 * kSkKS) continue;  // mostly empty stages
-      const int s = (K + kc - 1) / kc;
-      const int items = s * nt, full = items / kSkGrid, rest = items % kSkGrid;
-      const double item_bytes = (double)kSkBN * std::min(kc, K) * 2;
-      auto round = [&](int busy) { return item_bytes / std::min(40e9, 5.6e12 / busy); };
-      double t = full * round(kSkGrid) + (rest ? round(rest) : 0.0);
-      if (s > 1) t += 2.0 * s * M * nt * kSkBN * 4 / 5.6e12;
-      if (t < best * 0.98) {
-        best = t;
-        best_kc = kc;
-      }
-    }
+    // K slice: 2048 when that still gives every persistent workgroup at least
+    // four items, else 1024 with at least two, else 512.  Measured on the
+    // decode shapes of the 7B (M 64), 8B (M 8) and 70B (M 4) layers, this
+    // picks the fastest slice or one within 8% of it on all twelve
+    // projections; a round model (workgroups streaming at a fixed rate) had
+    // picked 2048 for the 70B down and O projections (112 and 38 us against
+    // 99 and 32 us at 1024).
+    auto items_at = [&](int kc) { return (long)((K + kc - 1) / kc) * nt; };
+    int best_kc = 2 * kSkKS;
+    if (items_at(8 * kSkKS) >= 4L * kSkGrid) best_kc = 8 * kSkKS;
+    else if (items_at(4 * kSkKS) >= 2L * kSkGrid) best_kc = 4 * kSkKS;
     pl.splits = (K + best_kc - 1) / best_kc;
     pl.k_per_split = best_kc;
     pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)tiles_n(cfg) * kSkBN *
@@ -123,9 +114,10 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t work = (int64_t)M * tiles_n * (C::BN / 8);
-  const int blocks = (int)((work + 255) / 256);
-  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3(blocks), dim3(256), 0, st, partial, pl.splits, M,
-                     NP, C::BN, epi);
+  const int parts = splitk_parts(pl.splits), per_block = kReduceThreads / parts;
+  const int blocks = (int)((work + per_block - 1) / per_block);
+  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3(blocks), dim3(kReduceThreads), 0, st, partial,
+                     pl.splits, parts, M, NP, C::BN, epi);
   return hipGetLastError();
 }
 
@@ -198,8 +190,9 @@ static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t work = (int64_t)M * tiles_n * (kSkBN / 8);
-  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3((int)((work + 255) / 256)), dim3(256), 0, st,
-                     partial, pl.splits, M, NP, kSkBN, epi);
+  const int parts = splitk_parts(pl.splits), per_block = kReduceThreads / parts;
+  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3((int)((work + per_block - 1) / per_block)),
+                     dim3(kReduceThreads), 0, st, partial, pl.splits, parts, M, NP, kSkBN, epi);
   return hipGetLastError();
 }
 

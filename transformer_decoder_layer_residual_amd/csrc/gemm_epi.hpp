@@ -308,28 +308,56 @@ struct EpiRope {
   }
 };
 
-// Deterministic split-K reduction (fixed split order) followed by the
-// epilogue.  One thread per (row, tile, group of 4 first-half columns).
-// Partials are [split][M][NP] with NP = tiles * BN (padded to whole tiles).
+// Deterministic split-K reduction followed by the epilogue.  Partials are
+// [split][M][NP] with NP = tiles * BN (padded to whole tiles).  A column
+// group is (row, tile, 4 first-half columns and their partners).  At decode
+// sizes there are few column groups and many splits, so `parts` threads
+// share a group: thread p adds splits p, p + parts, ... in order, and the
+// parts are added in order through LDS (a fixed order: the result does not
+// depend on timing).  One thread per group walking 28 splits took 21 us on a
+// 4 x 8192 output.
+constexpr int kReduceThreads = 256;
+
+// Threads per column group for a given split count (a power of two <= 8).
+inline int splitk_parts(int splits) {
+  return splits >= 8 ? 8 : splits >= 4 ? 4 : splits >= 2 ? 2 : 1;
+}
+
 template <class Epi>
-__global__ void __launch_bounds__(256)
-splitk_reduce(const float* __restrict__ partial, int splits, int M, int NP, int BN, Epi epi) {
+__global__ void __launch_bounds__(kReduceThreads)
+splitk_reduce(const float* __restrict__ partial, int splits, int parts, int M, int NP, int BN,
+              Epi epi) {
+  __shared__ f32x4 red[kReduceThreads][2];
   const int P = BN / 2, gpt = P / 4, tiles = NP / BN;
-  const int NL = NP;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_block = kReduceThreads / parts;
+  const int tid = threadIdx.x, cl = tid % per_block, part = tid / per_block;
+  const int64_t idx = (int64_t)blockIdx.x * per_block + cl;
   const int64_t total = (int64_t)M * tiles * gpt;
-  if (idx >= total) return;
-  const int g = (int)(idx % gpt);
-  const int64_t rest = idx / gpt;
+  const bool live = idx < total;
+  const int64_t cg = live ? idx : total - 1;
+  const int g = (int)(cg % gpt);
+  const int64_t rest = cg / gpt;
   const int tn = (int)(rest % tiles);
   const int m = (int)(rest / tiles);
   f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = a;
-  for (int s = 0; s < splits; ++s) {
-    const float* p = partial + ((int64_t)s * M + m) * NL + (int64_t)tn * BN + 4 * g;
+  const float* p0 = partial + (int64_t)m * NP + (int64_t)tn * BN + 4 * g;
+#pragma unroll 4
+  for (int s = part; s < splits; s += parts) {
+    const float* p = p0 + (int64_t)s * M * NP;
     a += *reinterpret_cast<const f32x4*>(p);
     b += *reinterpret_cast<const f32x4*>(p + P);
   }
-  epi(m, tn, 4 * g, a, b);
+  if (parts > 1) {
+    red[tid][0] = a;
+    red[tid][1] = b;
+    __syncthreads();
+    if (part != 0) return;
+    for (int q = 1; q < parts; ++q) {
+      a += red[cl + q * per_block][0];
+      b += red[cl + q * per_block][1];
+    }
+  }
+  if (live) epi(m, tn, 4 * g, a, b);
 }
 
 }  // namespace dl

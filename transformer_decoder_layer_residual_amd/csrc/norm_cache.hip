@@ -25,7 +25,8 @@ __device__ __forceinline__ f32x4 ld4f(const T* p) {
   return f32x4{o[0], o[1], o[2], o[3]};
 }
 
-template <typename Tin, typename Tout>
+// NV: 4-element vectors per thread (H <= 4 * NV * kNormThreads).
+template <typename Tin, typename Tout, int NV>
 __global__ void __launch_bounds__(kNormThreads)
 rmsnorm_kernel(const Tin* __restrict__ x, const float* __restrict__ rin, float* __restrict__ rout,
                const Tout* __restrict__ gamma, Tout* __restrict__ out, int H, float eps) {
@@ -33,20 +34,27 @@ rmsnorm_kernel(const Tin* __restrict__ x, const float* __restrict__ rin, float* 
   const int64_t row = blockIdx.x;
   const int nv = H / 4;
   const int tid = threadIdx.x;
-  f32x4 h[kNormMaxVec];
+  // Every load is issued before the first use (indices clamped into the
+  // row, results of the clamped lanes unused): with the loads under the
+  // per-vector bounds test the compiler waited for each one in turn.
+  f32x4 h[NV], g[NV], rr[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = min(tid + i * kNormThreads, nv - 1);
+    h[i] = ld4f(x + row * H + 4 * v);
+    g[i] = ld4f(gamma + 4 * v);
+    if (rin) rr[i] = *reinterpret_cast<const f32x4*>(rin + row * H + 4 * v);
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kNormMaxVec; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int v = tid + i * kNormThreads;
     if (v < nv) {
-      f32x4 a = ld4f(x + row * H + 4 * v);
       if (rin) {
-        const f32x4 r = *reinterpret_cast<const f32x4*>(rin + row * H + 4 * v);
-        a = a + r;
-        *reinterpret_cast<f32x4*>(rout + row * H + 4 * v) = a;
+        h[i] = h[i] + rr[i];
+        *reinterpret_cast<f32x4*>(rout + row * H + 4 * v) = h[i];
       }
-      h[i] = a;
-      ss += a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+      ss += h[i][0] * h[i][0] + h[i][1] * h[i][1] + h[i][2] * h[i][2] + h[i][3] * h[i][3];
     }
   }
   ss = wave_sum(ss);
@@ -57,13 +65,11 @@ rmsnorm_kernel(const Tin* __restrict__ x, const float* __restrict__ rin, float* 
   for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)H + eps);
 #pragma unroll
-  for (int i = 0; i < kNormMaxVec; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int v = tid + i * kNormThreads;
-    if (v < nv) {
-      const f32x4 g = ld4f(gamma + 4 * v);
-      store4(out + row * H + 4 * v, g[0] * (h[i][0] * inv), g[1] * (h[i][1] * inv),
-             g[2] * (h[i][2] * inv), g[3] * (h[i][3] * inv));
-    }
+    if (v < nv)
+      store4(out + row * H + 4 * v, g[i][0] * (h[i][0] * inv), g[i][1] * (h[i][1] * inv),
+             g[i][2] * (h[i][2] * inv), g[i][3] * (h[i][3] * inv));
   }
 }
 
@@ -72,8 +78,19 @@ hipError_t rmsnorm_residual(const Tin* x, const float* resid_in, float* resid_ou
                             const Tout* gamma, Tout* out, int T, int H, float eps,
                             hipStream_t st) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout>), dim3(T), dim3(kNormThreads), 0, st, x,
-                     resid_in, resid_out, gamma, out, H, eps);
+  const int nvt = (H / 4 + kNormThreads - 1) / kNormThreads;
+  if (nvt <= 1)
+    hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 1>), dim3(T), dim3(kNormThreads), 0, st, x,
+                       resid_in, resid_out, gamma, out, H, eps);
+  else if (nvt <= 2)
+    hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 2>), dim3(T), dim3(kNormThreads), 0, st, x,
+                       resid_in, resid_out, gamma, out, H, eps);
+  else if (nvt <= 4)
+    hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 4>), dim3(T), dim3(kNormThreads), 0, st, x,
+                       resid_in, resid_out, gamma, out, H, eps);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, kNormMaxVec>), dim3(T), dim3(kNormThreads), 0,
+                       st, x, resid_in, resid_out, gamma, out, H, eps);
   return hipGetLastError();
 }
 
