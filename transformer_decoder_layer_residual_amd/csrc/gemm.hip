@@ -78,11 +78,30 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
       if (big_tn >= 1 && big_tn < tn && mixed < now - 0.2) pl.mixed_tn = big_tn;
     }
   }
+  if (cfg == kCfg256 || cfg == kCfgPP128) {
+    // ping-pong tiles: split K when the tiles cover fewer than ~3/4 of the
+    // CUs (a few hundred rows against a narrow N, e.g. 64 sequences x 4
+    // verification tokens: 32 tiles for the 7B down projection), into about
+    // 256 workgroups of at least eight 64-wide k-tiles each
+    const int ktl = K / 64;
+    int sp = 1, kpt = ktl;
+    if (nt < 192 && pl.mixed_tn == 0) {
+      sp = std::min((256 + nt - 1) / nt, std::min(ktl / 8, 16));
+      if (sp >= 2) {
+        kpt = (ktl + sp - 1) / sp;
+        sp = (ktl + kpt - 1) / kpt;
+      } else {
+        sp = 1;
+        kpt = ktl;
+      }
+    }
+    pl.splits = sp;
+    pl.k_per_split = kpt * 64;
+    pl.ws_bytes = sp > 1 ? (size_t)sp * (size_t)M * (size_t)tiles_n(cfg) * 256 * sizeof(float) : 0;
+    return pl;
+  }
   int splits = 1;
-  const bool single_pass = (cfg == kCfg256 || cfg == kCfgPP128);  // no split-K variant
-  if (single_pass) {
-    splits = 1;
-  } else if (M <= 256) {
+  if (M <= 256) {
     // weight-streaming shapes: enough workgroups to keep HBM busy
     const int want = (1024 + nt - 1) / nt;
     splits = want < 1 ? 1 : want;
@@ -123,8 +142,27 @@ static hipError_t launch_cfg(const T* x, int M, int K, const Map& map, const Epi
 
 template <class Map, class Epi>
 static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
-                             hipStream_t st, int bm = 256, int bk = 64, int mixed_tn = 0) {
+                             hipStream_t st, int bm = 256, int bk = 64, int mixed_tn = 0,
+                             int splits = 1, int kps = 0, void* ws = nullptr) {
   const int tiles_n = (NL + 255) / 256;
+  if (splits > 1) {  // K % 64 == 0 (the planner splits only then)
+    const int tiles_m = (M + bm - 1) / bm, NP = tiles_n * 256, kpt = kps / 64;
+    float* partial = reinterpret_cast<float*>(ws);
+    const dim3 grid(tiles_m * tiles_n, splits);
+    if (bm == 128)
+      hipLaunchKernelGGL((gemm_pp_splitk_kernel<128, 64, Map>), grid, dim3(512), 0, st, x, M, K,
+                         map, partial, NP, tiles_m, tiles_n, kpt);
+    else
+      hipLaunchKernelGGL((gemm_pp_splitk_kernel<256, 64, Map>), grid, dim3(512), 0, st, x, M, K,
+                         map, partial, NP, tiles_m, tiles_n, kpt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t work = (int64_t)M * tiles_n * (256 / 8);
+    const int parts = splitk_parts(splits), per_block = kReduceThreads / parts;
+    hipLaunchKernelGGL((splitk_reduce<Epi>), dim3((int)((work + per_block - 1) / per_block)),
+                       dim3(kReduceThreads), 0, st, partial, splits, parts, M, NP, 256, epi);
+    return hipGetLastError();
+  }
   if (K % 64 == 0 && bm == 256 && mixed_tn > 0 && mixed_tn < tiles_n) {
     const int grid = ((M + 255) / 256) * mixed_tn + ((M + 127) / 128) * (tiles_n - mixed_tn);
     if (bk == 32)
@@ -213,8 +251,10 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
     switch (pl.cfg) {
       case kCfg256:
         return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 256, 64,
-                          pl.mixed_tn);
-      case kCfgPP128: return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 128);
+                          pl.mixed_tn, pl.splits, pl.k_per_split, ws);
+      case kCfgPP128:
+        return launch_big(x, M, K, mk_map(256, 128), mk_epi(256, 128), NL, st, 128, 64, 0,
+                          pl.splits, pl.k_per_split, ws);
       case kCfg128: return launch_cfg<T, T128>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg64: return launch_cfg<T, T64>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);
       case kCfg16: return launch_cfg<T, T16>(x, M, K, mk_map(128, 64), mk_epi(128, 64), NL, pl, ws, st);

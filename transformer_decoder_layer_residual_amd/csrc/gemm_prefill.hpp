@@ -183,11 +183,12 @@ struct PPGeom {
 };
 
 // One BM x 256 output tile: tile `bid` of a tiles_m x tiles_n grid whose
-// N-tiles start at tn0 (so a launch may cover a range of N with one shape).
+// N-tiles start at tn0 (so a launch may cover a range of N with one shape);
+// k-tiles kt0 .. kt0 + nkt - 1 are summed (the whole K unless split).
 template <int BM, int BK, class Map, class Epi>
 __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K, const Map& map,
                                         const Epi& epi, int bid, int tiles_m, int tiles_n,
-                                        int tn0, unsigned char* smem) {
+                                        int tn0, unsigned char* smem, int kt0, int nkt) {
   using Geo = PPGeom<BM, BK>;
   constexpr int BN = 256;
   constexpr int ROWB = BK * 2;                      // bytes per LDS row
@@ -232,7 +233,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
       const bf16* b = map.row(tn, row - BM);
       base = b ? b : X;                                     // missing rows: valid, never stored
     }
-    src[i] = reinterpret_cast<const unsigned char*>(base) + c * 16;
+    src[i] = reinterpret_cast<const unsigned char*>(base) + (int64_t)kt0 * BK * 2 + c * 16;
   }
   auto issue_loads = [&](int kt) {
     unsigned char* dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
@@ -297,7 +298,6 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   // one phase later.  Tile t+LA goes into tile t-1's stage in phase 2t+1 (group
   // 0 from its MEM(t), group 1 from its COMP(t-1)); tile t+1 must have landed
   // by the end of phase 2t+2.
-  const int nkt = K / BK;
   for (int i = 0; i <= LA && i < nkt; ++i) issue_loads(i);
   wait_tile(0, nkt);
   DL_PHASE_END();                                   // phase 1 begins
@@ -370,7 +370,34 @@ __global__ void __launch_bounds__(512, 1)
 gemm_pp_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
                int tiles_n) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[PPGeom<BM, BK>::SMEM];
-  pp_tile<BM, BK>(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, 0, smem);
+  pp_tile<BM, BK>(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, 0, smem, 0, K / BK);
+}
+
+// fp32 partial sums of one K split, [M][NP] row-major (NP = tiles_n * 256),
+// a tile's first 128 columns and their partners as the epilogues see them.
+struct EpiPartial {
+  float* out;
+  int NP;
+  __device__ void apply8(int m, int tn, int j, const float* a, const float* b) const {
+    float* p = out + (int64_t)m * NP + tn * 256 + j;
+    store8(p, a);
+    store8(p + 128, b);
+  }
+};
+
+// Split-K variant for shapes whose tiles do not fill the chip (a few hundred
+// rows against a narrow N): blockIdx.y is the split, which sums kps k-tiles
+// into its own partial slab; splitk_reduce adds the slabs in order and runs
+// the real epilogue.
+template <int BM, int BK, class Map>
+__global__ void __launch_bounds__(512, 1)
+gemm_pp_splitk_kernel(const bf16* __restrict__ X, int M, int K, Map map,
+                      float* __restrict__ partial, int NP, int tiles_m, int tiles_n, int kps) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[PPGeom<BM, BK>::SMEM];
+  const int split = blockIdx.y, kt0 = split * kps;
+  const int nkt = min(kps, K / BK - kt0);
+  EpiPartial epi{partial + (int64_t)split * M * NP, NP};
+  pp_tile<BM, BK>(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, 0, smem, kt0, nkt);
 }
 
 // 256-row tiles for N-tiles [0, big_tn) and 128-row tiles for the rest, in one
@@ -386,10 +413,10 @@ gemm_pp_mixed_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi,
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S256 > S128 ? S256 : S128];
   const int tm256 = (M + 255) / 256, n_big = tm256 * big_tn;
   if ((int)blockIdx.x < n_big)
-    pp_tile<256, BK>(X, M, K, map, epi, blockIdx.x, tm256, big_tn, 0, smem);
+    pp_tile<256, BK>(X, M, K, map, epi, blockIdx.x, tm256, big_tn, 0, smem, 0, K / BK);
   else
     pp_tile<128, BK>(X, M, K, map, epi, blockIdx.x - n_big, (M + 127) / 128, tiles_n - big_tn,
-                     big_tn, smem);
+                     big_tn, smem, 0, K / BK);
 }
 
 }  // namespace dl
