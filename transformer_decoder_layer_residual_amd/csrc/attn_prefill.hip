@@ -233,6 +233,14 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 // work adds up to the same total on every CU (heaviest-first alone paired
 // heavy with middle tiles: up to 1.4x the average work on one CU).
 // ---------------------------------------------------------------------------
+// Column of key `key` in a V^T tile row.  Within each 16-key group the
+// 32x32x16 score block gives a lane keys {4h..4h+3} and {8+4h..8+4h+3} (h =
+// lane / 32) of one k16 step; swapping bits 2 and 3 of the key puts those
+// eight keys side by side, so the P.V operand is one 16-byte LDS read.
+__device__ __forceinline__ int vt_col(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256, 2)
 attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -325,7 +333,7 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<bf16x2*>(&Vt[buf][(c * 8 + x) * VLS + 2 * kp]) = bf16x2{a[x], bb[x]};
+        *reinterpret_cast<bf16x2*>(&Vt[buf][(c * 8 + x) * VLS + vt_col(2 * kp)]) = bf16x2{a[x], bb[x]};
       }
     }
   };
@@ -350,26 +358,39 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           sc[kb] = mfma_32x32x16(kf, qf[ds], sc[kb]);
         }
       }
-      // mask + online softmax (log2 domain) for this lane's query
+      // mask + online softmax (log2 domain) for this lane's query; a tile whose
+      // every key is visible to every query of the wave needs no mask
       float mx = -INFINITY;
+      if (kv0 + BKV - 1 <= qw0 && kv0 + BKV <= kv_end) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-          const float val = (key <= qi && key < kv_end) ? sc[kb][e] * scale_log2 : -INFINITY;
-          sc[kb][e] = val;
-          mx = fmaxf(mx, val);
-        }
+          for (int e = 0; e < 16; ++e) {
+            sc[kb][e] *= scale_log2;
+            mx = fmaxf(mx, sc[kb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
+            const float val = (key <= qi && key < kv_end) ? sc[kb][e] * scale_log2 : -INFINITY;
+            sc[kb][e] = val;
+            mx = fmaxf(mx, val);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float m_new = fmaxf(m_i, mx);
-      const float alpha = exp2f(m_i - m_new);
+      // v_exp_f32 directly: arguments are <= 0 here, and results below the
+      // normal range (weights under 2^-126) may flush to zero
+      const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(sc[kb][e] - m_new);
+          const float p = __builtin_amdgcn_exp2f(sc[kb][e] - m_new);
           sc[kb][e] = p;
           ls += p;
         }
@@ -385,13 +406,12 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           const bf16x8 pf = {(bf16)sc[kb][8 * s2], (bf16)sc[kb][8 * s2 + 1], (bf16)sc[kb][8 * s2 + 2],
                              (bf16)sc[kb][8 * s2 + 3], (bf16)sc[kb][8 * s2 + 4], (bf16)sc[kb][8 * s2 + 5],
                              (bf16)sc[kb][8 * s2 + 6], (bf16)sc[kb][8 * s2 + 7]};
-          const int kbase = kb * 32 + 16 * s2 + 4 * fh;
+          // keys kb*32 + 16*s2 + {4fh..4fh+3, 8+4fh..8+4fh+3}: eight adjacent
+          // V^T columns after vt_col's permutation, one 16-byte read
+          const int kbase = kb * 32 + 16 * s2 + 8 * fh;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16* row = &Vt[cur][(db * 32 + fr) * VLS + kbase];
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 8);
-            const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vt[cur][(db * 32 + fr) * VLS + kbase]);
             o[db] = mfma_32x32x16(vf, pf, o[db]);
           }
         }
