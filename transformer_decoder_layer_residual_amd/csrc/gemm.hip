@@ -32,9 +32,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
     // ping-pong kernel; 256-row tiles when they fill the chip, else 128
     // (a round-count model favoured 128-row tiles for 1.5 rounds of 256-row
-    // ones, but measured no faster and with more panel traffic; 256-row
-    // tiles split in two over K for the 128 tiles of a 2048-row O or down
-    // projection measured 10-15% slower than 128-row tiles, reduce included)
+    // ones, but measured no faster and with more panel traffic)
     cfg = tiles(kCfg256) >= 256 ? kCfg256 : kCfgPP128;
   } else if (M >= 512) {
     cfg = (fits(kCfg256) && tiles(kCfg256) >= 256) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
@@ -191,8 +189,8 @@ static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const 
       hipLaunchKernelGGL((gemm_pp_kernel<256, 32, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
                          st, x, M, K, map, epi, tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_q4_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(256), 0, st, x,
-                         M, K, map, epi, tiles_m, tiles_n);
+      hipLaunchKernelGGL((gemm_pp_kernel<256, 64, Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0,
+                         st, x, M, K, map, epi, tiles_m, tiles_n);
   } else {
     hipLaunchKernelGGL((gemm_big_kernel<Map, Epi>), dim3(tiles_m * tiles_n), dim3(512), 0, st, x,
                        M, K, map, epi, tiles_m, tiles_n);

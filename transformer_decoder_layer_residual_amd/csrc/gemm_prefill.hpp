@@ -2,8 +2,6 @@
 // ping-pong kernel (K % 64 == 0) and the double-buffered 256x256 kernel.
 #pragma once
 
-#include <type_traits>
-
 #include "gemm_epi.hpp"
 
 namespace dl {
@@ -400,220 +398,6 @@ gemm_pp_splitk_kernel(const bf16* __restrict__ X, int M, int K, Map map,
   const int nkt = min(kps, K / BK - kt0);
   EpiPartial epi{partial + (int64_t)split * M * NP, NP};
   pp_tile<BM, BK>(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, 0, smem, kt0, nkt);
-}
-
-// ---------------------------------------------------------------------------
-// Four-wave prefill tile: 256 x 256 x 64, one wave per SIMD, each wave a
-// 128 x 128 block (4 x 4 blocks of 32 x 32 on v_mfma_f32_32x32x16_bf16).
-//
-// Against the ping-pong tile (eight 64 x 128 waves) every wave reads 8 KB of
-// fragments per 16 MFMAs instead of 6 KB per 8, so the tile needs a third less
-// LDS read bandwidth; the single wave on a SIMD keeps the matrix pipe fed by
-// issuing the next k16 step's fragment reads (and the global->LDS loads)
-// between its MFMAs, one per MFMA, in a fixed order (sched_barrier).
-// K-tiles live in two LDS stages.  In the last k16 step of tile t, after
-// half of its MFMAs, every wave waits for its loads of tile t+1 and meets
-// the others at a barrier: tile t+1 is then visible, and every wave is done
-// reading tile t, so the remaining MFMAs carry the step-0 fragment reads of
-// tile t+1 and the loads of tile t+2 into tile t's stage.  Same LDS row
-// layout, swizzle and tile order as the ping-pong tile; same epilogue through
-// LDS (rows [128 p, 128 p + 128) in pass p).  Requires K % 64 == 0.
-// ---------------------------------------------------------------------------
-struct Q4Geom {
-  static constexpr int BM = 256, BN = 256, BK = 64, ROWB = 128;
-  static constexpr int STAGE = (BM + BN) * ROWB;    // 64 KB
-  static constexpr int OPITCH = BN + 8;
-  static constexpr int MAIN = 2 * STAGE, OUT = 128 * OPITCH * 4;
-  static constexpr int SMEM = MAIN > OUT ? MAIN : OUT;
-};
-
-template <class Map, class Epi>
-__device__ __forceinline__ void q4_tile(const bf16* __restrict__ X, int M, int K, const Map& map,
-                                        const Epi& epi, int bid, int tiles_m, int tiles_n,
-                                        unsigned char* smem, int kt0, int nkt) {
-  constexpr int BM = Q4Geom::BM, BN = Q4Geom::BN, BK = Q4Geom::BK, ROWB = Q4Geom::ROWB;
-  constexpr int CPR = BK / 8, RPI = 64 / CPR;       // 16 B chunks per row, rows per load
-  constexpr int STAGE = Q4Geom::STAGE, OPITCH = Q4Geom::OPITCH;
-  constexpr int MS = 4, NS = 4, KS = BK / 16;
-  constexpr int RPW = (BM + BN) / 4;                // LDS rows each wave loads per stage
-  constexpr int LI = RPW / RPI;                     // 16 load instructions per wave per k-tile
-
-  const int total = tiles_m * tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int GM = 8;
-  const int gsz = GM * tiles_n;
-  const int first_m = (bid / gsz) * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int tm = first_m + (bid % gsz) % gm;
-  const int tn = (bid % gsz) / gm;
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int fr = lane & 31, fh = lane >> 5;
-
-  // waves 0-1 load the X rows of a stage, waves 2-3 the weight rows
-  const unsigned char* src[LI];
-#pragma unroll
-  for (int i = 0; i < LI; ++i) {
-    const int row = wave * RPW + i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ pp_swz<BK>(row);
-    const bf16* base;
-    if (row < BM) {
-      base = X + (int64_t)min(tm * BM + row, M - 1) * K;   // rows >= M: valid, never stored
-    } else {
-      const bf16* b = map.row(tn, row - BM);
-      base = b ? b : X;                                     // missing rows: valid, never stored
-    }
-    src[i] = reinterpret_cast<const unsigned char*>(base) + (int64_t)kt0 * BK * 2 + c * 16;
-  }
-  auto issue = [&](int kt, int i) {
-    unsigned char* dst = smem + (kt & 1) * STAGE + wave * RPW * ROWB;
-    __builtin_amdgcn_global_load_lds((const void*)(src[i] + (int64_t)kt * BK * 2),
-                                     (__attribute__((address_space(3))) void*)(dst + i * RPI * ROWB),
-                                     16, 0, 0);
-  };
-  bf16x8 fx[2][MS], fw[2][NS];
-  auto rd_x = [&](int kt, int ks, int set, int i) {
-    const unsigned char* st = smem + (kt & 1) * STAGE;
-    const int c = ks * 2 + fh, r = wm * 128 + i * 32 + fr;
-    fx[set][i] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
-  };
-  auto rd_w = [&](int kt, int ks, int set, int s) {
-    const unsigned char* st = smem + (kt & 1) * STAGE;
-    const int blk = (s < 2) ? 2 * wn + s : 4 + 2 * wn + (s - 2);  // first half, partners
-    const int c = ks * 2 + fh, r = BM + blk * 32 + fr;
-    fw[set][s] = *reinterpret_cast<const bf16x8*>(st + r * ROWB + ((c ^ pp_swz<BK>(r)) << 4));
-  };
-  f32x16 acc[MS][NS];
-#pragma unroll
-  for (int i = 0; i < MS; ++i)
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
-
-  // prologue: tile 0 landed and visible, tile 1 in flight, step-0 fragments read
-#pragma unroll
-  for (int i = 0; i < LI; ++i) issue(0, i);
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (nkt > 1) {
-#pragma unroll
-    for (int i = 0; i < LI; ++i) issue(1, i);
-  }
-#pragma unroll
-  for (int i = 0; i < MS; ++i) rd_x(0, 0, 0, i);
-#pragma unroll
-  for (int s = 0; s < NS; ++s) rd_w(0, 0, 0, s);
-
-  // One k-tile.  NXT: tile kt+1 exists; LD: tile kt+2 exists.  Both are
-  // compile-time flags (the last two tiles are peeled off the loop), so the
-  // steady-state loop has no branches and the compiler's load counting stays
-  // exact.
-  auto body = [&](int kt, auto nxt_c, auto ld_c) {
-    constexpr bool nxt = decltype(nxt_c)::value, ld = decltype(ld_c)::value;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int set = ks & 1, ns = set ^ 1;
-      if (ks < KS - 1) {
-        // 16 MFMAs of step ks; the first 8 each followed by one fragment read of step ks+1
-#pragma unroll
-        for (int i = 0; i < MS; ++i)
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            acc[i][s] = mfma_32x32x16(fw[set][s], fx[set][i], acc[i][s]);
-            const int q = i * NS + s;
-            if (q < MS) rd_x(kt, ks + 1, ns, q);
-            else if (q < MS + NS) rd_w(kt, ks + 1, ns, q - MS);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            acc[i][s] = mfma_32x32x16(fw[set][s], fx[set][i], acc[i][s]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        if constexpr (nxt) {
-          // own loads of tile kt+1 landed and own LDS reads done; then the barrier
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int i = 2; i < MS; ++i)
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            acc[i][s] = mfma_32x32x16(fw[set][s], fx[set][i], acc[i][s]);
-            const int q = (i - 2) * NS + s;
-            if constexpr (nxt) {
-              if (q < MS) rd_x(kt + 1, 0, ns, q);
-              else rd_w(kt + 1, 0, ns, q - MS);
-            }
-            if constexpr (ld) {
-              issue(kt + 2, 2 * q);
-              issue(kt + 2, 2 * q + 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-    }
-  };
-  using Yes = std::true_type;
-  using No = std::false_type;
-  int kt = 0;
-  for (; kt + 2 < nkt; ++kt) body(kt, Yes{}, Yes{});
-  if (kt + 1 < nkt) body(kt++, Yes{}, No{});
-  body(kt, No{}, No{});
-
-  // epilogue through LDS, as in the ping-pong tile: the two waves holding
-  // rows [128 p, 128 p + 128) park them in pass p, then all 256 threads take
-  // 8-column chunks in row order
-  float* stage = reinterpret_cast<float*>(smem);
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if (wm == pass) {
-#pragma unroll
-      for (int i = 0; i < MS; ++i) {
-        const int r = i * 32 + fr;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const int col = (s < 2 ? 0 : BN / 2) + (2 * wn + (s & 1)) * 32 + 4 * fh;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4*>(stage + r * OPITCH + col + 8 * q) =
-                f32x4{acc[i][s][4 * q], acc[i][s][4 * q + 1], acc[i][s][4 * q + 2],
-                      acc[i][s][4 * q + 3]};
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int CH = (BN / 2) / 8;
-#pragma unroll 4
-    for (int it = 0; it < 128 * CH / 256; ++it) {
-      const int idx = t + it * 256;
-      const int r = idx / CH, j = (idx % CH) * 8;
-      const int m = tm * BM + pass * 128 + r;
-      if (m < M) {
-        float a[8], b[8];
-        load4(stage + r * OPITCH + j, a);
-        load4(stage + r * OPITCH + j + 4, a + 4);
-        load4(stage + r * OPITCH + BN / 2 + j, b);
-        load4(stage + r * OPITCH + BN / 2 + j + 4, b + 4);
-        epi.apply8(m, tn, j, a, b);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-template <class Map, class Epi>
-__global__ void __launch_bounds__(256, 1)
-gemm_q4_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int tiles_m,
-               int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Q4Geom::SMEM];
-  q4_tile(X, M, K, map, epi, blockIdx.x, tiles_m, tiles_n, smem, 0, K / Q4Geom::BK);
 }
 
 // 256-row tiles for N-tiles [0, big_tn) and 128-row tiles for the rest, in one

@@ -40,8 +40,8 @@ WRITE_SCALE = 1.0
 # __bf16 printed as "bool _Accum"; each pattern accepts both forms of the one
 # instance the benchmark's roofline line times)
 KERNELS = {
-    "gemm_gateup_silu_prefill": (r"gemm_q4_kernelINS_9MapSwiglu"
-                                 r"|gemm_q4_kernel<dl::MapSwiglu",
+    "gemm_gateup_silu_prefill": (r"gemm_pp_kernelILi256ELi64ENS_9MapSwiglu"
+                                 r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
                                  ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
     "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16bLi128ELi1E"
                           r"|attn_decode_kernel<bool _Accum, bool _Accum, 128, 1,",
