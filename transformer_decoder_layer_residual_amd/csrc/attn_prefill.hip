@@ -346,18 +346,39 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int cur = kt & 1;
     const int kv0 = kt * BKV;
     if (kv0 <= qw0 + QW - 1) {           // otherwise every key of the tile is in this wave's future
-      // S^T = K Q^T: two 32-key blocks
+      // S^T = K Q^T: two 32-key blocks as two independent MFMA chains,
+      // interleaved, with the K fragments read two k16 steps ahead (a single
+      // chain with each read just before its MFMA waited on both latencies)
       f32x16 sc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+      auto kfrag = [&](int kb, int ds) {
+        return *reinterpret_cast<const bf16x8*>(&Ks[cur][(kb * 32 + fr) * KLS + ds * 16 + 8 * fh]);
+      };
+      bf16x8 kf[3][2];
+      kf[0][0] = kfrag(0, 0);
+      kf[0][1] = kfrag(1, 0);
+      kf[1][0] = kfrag(0, 1);
+      kf[1][1] = kfrag(1, 1);
 #pragma unroll
-        for (int ds = 0; ds < DK; ++ds) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[cur][(kb * 32 + fr) * KLS + ds * 16 + 8 * fh]);
-          sc[kb] = mfma_32x32x16(kf, qf[ds], sc[kb]);
+      for (int ds = 0; ds < DK; ++ds) {
+        if (ds + 2 < DK) {
+          kf[(ds + 2) % 3][0] = kfrag(0, ds + 2);
+          kf[(ds + 2) % 3][1] = kfrag(1, ds + 2);
         }
+        sc[0] = mfma_32x32x16(kf[ds % 3][0], qf[ds], sc[0]);
+        sc[1] = mfma_32x32x16(kf[ds % 3][1], qf[ds], sc[1]);
       }
+      // V^T fragments of the first P.V step, read while the softmax runs
+      auto vfrag = [&](int step, int db) {
+        const int kbase = (step >> 1) * 32 + 16 * (step & 1) + 8 * fh;
+        return *reinterpret_cast<const bf16x8*>(&Vt[cur][(db * 32 + fr) * VLS + kbase]);
+      };
+      bf16x8 vf[2][DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vf[0][db] = vfrag(0, db);
       // mask + online softmax (log2 domain) for this lane's query; a tile whose
       // every key is visible to every query of the wave needs no mask
       float mx = -INFINITY;
@@ -398,23 +419,23 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       m_i = m_new;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      // O^T += V^T P^T
+      // O^T += V^T P^T in four k16 steps (kb, s2); step i+1's V^T fragments
+      // are read while step i's MFMAs run.  Keys kb*32 + 16*s2 + {4fh..4fh+3,
+      // 8+4fh..8+4fh+3} are eight adjacent V^T columns after vt_col's
+      // permutation, so each fragment is one 16-byte read.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int step = 0; step < 4; ++step) {
+        const int kb = step >> 1, s2 = step & 1;
+        if (step + 1 < 4) {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 pf = {(bf16)sc[kb][8 * s2], (bf16)sc[kb][8 * s2 + 1], (bf16)sc[kb][8 * s2 + 2],
-                             (bf16)sc[kb][8 * s2 + 3], (bf16)sc[kb][8 * s2 + 4], (bf16)sc[kb][8 * s2 + 5],
-                             (bf16)sc[kb][8 * s2 + 6], (bf16)sc[kb][8 * s2 + 7]};
-          // keys kb*32 + 16*s2 + {4fh..4fh+3, 8+4fh..8+4fh+3}: eight adjacent
-          // V^T columns after vt_col's permutation, one 16-byte read
-          const int kbase = kb * 32 + 16 * s2 + 8 * fh;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vt[cur][(db * 32 + fr) * VLS + kbase]);
-            o[db] = mfma_32x32x16(vf, pf, o[db]);
-          }
+          for (int db = 0; db < DB; ++db) vf[(step + 1) & 1][db] = vfrag(step + 1, db);
         }
+        const bf16x8 pf = {(bf16)sc[kb][8 * s2], (bf16)sc[kb][8 * s2 + 1], (bf16)sc[kb][8 * s2 + 2],
+                           (bf16)sc[kb][8 * s2 + 3], (bf16)sc[kb][8 * s2 + 4], (bf16)sc[kb][8 * s2 + 5],
+                           (bf16)sc[kb][8 * s2 + 6], (bf16)sc[kb][8 * s2 + 7]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = mfma_32x32x16(vf[step & 1][db], pf, o[db]);
+      }
     }
     if (kt + 1 < nkv) sstore(cur ^ 1);
     __syncthreads();
