@@ -379,30 +379,32 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       bf16x8 vf[2][DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) vf[0][db] = vfrag(0, db);
-      // mask + online softmax (log2 domain) for this lane's query; a tile whose
-      // every key is visible to every query of the wave needs no mask
+      // mask + online softmax for this lane's query.  The running max m_i is
+      // kept in the log2 domain (scaled); the raw scores' max is scaled once
+      // (the scale is positive) and each weight is exp2(fma(s, scale, -m)).
+      // A tile whose every key is visible to every query of the wave needs
+      // no mask.  The softmax is the VALU-heavy part of the loop (a wave64
+      // VALU op takes four cycles against an MFMA's 32 per 32x32x16 block),
+      // so every op saved here is kept out of the MFMAs' way.
       float mx = -INFINITY;
       if (kv0 + BKV - 1 <= qw0 && kv0 + BKV <= kv_end) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            sc[kb][e] *= scale_log2;
-            mx = fmaxf(mx, sc[kb][e]);
-          }
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * fh + (e & 3);
-            const float val = (key <= qi && key < kv_end) ? sc[kb][e] * scale_log2 : -INFINITY;
+            const float val = (key <= qi && key < kv_end) ? sc[kb][e] : -INFINITY;
             sc[kb][e] = val;
             mx = fmaxf(mx, val);
           }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_i, mx);
+      const float m_new = fmaxf(m_i, mx * scale_log2);
       // v_exp_f32 directly: arguments are <= 0 here, and results below the
       // normal range (weights under 2^-126) may flush to zero
       const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
@@ -411,14 +413,18 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sc[kb][e] - m_new);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e], scale_log2, -m_new));
           sc[kb][e] = p;
           ls += p;
         }
       l_i = l_i * alpha + ls;
-      m_i = m_new;
+      // rescale O only when some lane's running max moved (alpha == 1 leaves
+      // O unchanged, and later tiles rarely raise the max)
+      if (__ballot(m_new != m_i)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      m_i = m_new;
       // O^T += V^T P^T in four k16 steps (kb, s2); step i+1's V^T fragments
       // are read while step i's MFMAs run.  Keys kb*32 + 16*s2 + {4fh..4fh+3,
       // 8+4fh..8+4fh+3} are eight adjacent V^T columns after vt_col's
