@@ -27,7 +27,9 @@ enum GemmCfg : int {
   kCfg32s = 4,   // BM 32,  BN 32,  2 waves (2x1), wave tile 16x32 (small/odd shapes)
   kCfgPP128 = 5, // BM 128, BN 256, 8 waves: ping-pong kernel (K % 64 == 0), bf16
   kCfgSkinny = 6,// M <= 64, BN 128, 4 waves: weight-streaming decode kernel, bf16
-  kCfgCount = 7
+  kCfgRow16 = 7, // M <= 16, BN 16: one workgroup per 16 weight rows, K split over
+                 // its waves and merged in LDS (no fp32 partials), bf16 decode
+  kCfgCount = 8
 };
 
 struct GemmPlan {

@@ -14,8 +14,8 @@ namespace dl {
 // ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
-static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32, 128, 64};
-static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32, 256, kSkBN};
+static const int kCfgBM[kCfgCount] = {256, 128, 64, 16, 32, 128, 64, 16};
+static const int kCfgBN[kCfgCount] = {256, 128, 128, 128, 32, 256, kSkBN, 16};
 
 
 GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
@@ -27,6 +27,8 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   int cfg;
   if (is_f32) {
     cfg = kCfg32s;
+  } else if (M <= 16 && K % 32 == 0 && N % 16 == 0 && N / 16 >= 256 && fits(kCfgRow16)) {
+    cfg = kCfgRow16;   // decode, a few sequences: row-block weight stream, no partials
   } else if (M <= 64 && fits(kCfgSkinny)) {
     cfg = kCfgSkinny;  // decode: weight streaming
   } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
@@ -46,6 +48,12 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   pl.BN = kCfgBN[cfg];
   const int nt = tiles(cfg);
   const int ktiles = (K + bk - 1) / bk;
+  if (cfg == kCfgRow16) {
+    pl.splits = 1;
+    pl.k_per_split = K;
+    pl.ws_bytes = 0;
+    return pl;
+  }
   if (cfg == kCfgSkinny) {
     // K slice: 2048 when that still gives every persistent workgroup at least
     // four items, else 1024 with at least two, else 512.  Measured on the
@@ -234,6 +242,23 @@ static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, con
   return hipGetLastError();
 }
 
+// Unroll depth and waves per workgroup of the row-block stream, measured on
+// the 8B- and 70B-shaped decode projections: long rows (K >= 14336, the down
+// projections) stream best as 4 waves 8 groups deep, K = 8192 as 8 waves 16
+// deep, shorter rows as 4 waves 16 deep.
+template <class Map, class Epi>
+static hipError_t launch_row16(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
+                               hipStream_t st) {
+  const dim3 grid(NL / 16);
+  if (K >= 14336)
+    hipLaunchKernelGGL((gemm_row16_kernel<8, 4, Map, Epi>), grid, dim3(256), 0, st, x, M, K, map, epi);
+  else if (K >= 8192)
+    hipLaunchKernelGGL((gemm_row16_kernel<16, 8, Map, Epi>), grid, dim3(512), 0, st, x, M, K, map, epi);
+  else
+    hipLaunchKernelGGL((gemm_row16_kernel<16, 4, Map, Epi>), grid, dim3(256), 0, st, x, M, K, map, epi);
+  return hipGetLastError();
+}
+
 typedef Tile<128, 128, 2, 2> T128;
 typedef Tile<64, 128, 1, 4> T64;
 typedef Tile<16, 128, 1, 4> T16;
@@ -261,6 +286,8 @@ static hipError_t dispatch(const T* x, int M, int K, int NL, const GemmPlan& pl,
       case kCfg32s: return launch_cfg<T, T32s>(x, M, K, mk_map(32, 16), mk_epi(32, 16), NL, pl, ws, st);
       case kCfgSkinny:
         return launch_skinny(x, M, K, mk_map(kSkBN, kSkP), mk_epi(kSkBN, kSkP), NL, pl, ws, st);
+      case kCfgRow16:
+        return launch_row16(x, M, K, mk_map(16, 8), mk_epi(16, 8), NL, st);
     }
     return hipErrorInvalidValue;
   }
