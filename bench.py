@@ -473,6 +473,34 @@ def main():
             kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv5 * D5 * 2
             a_bytes = kv_bytes + 2.0 * B5 * Hq5 * D5 * 2
             a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+            # the FFN's two projections alone (the same kernels the step runs at
+            # this batch); each streams more weight bytes than the MALL holds
+            n2 = torch.empty(B5, H5, dtype=torch.bfloat16, device="cuda:0").normal_()
+            act = torch.empty(B5, I5, dtype=torch.bfloat16, device="cuda:0")
+            res5 = torch.empty(B5, H5, dtype=torch.float32, device="cuda:0").normal_()
+            fo5 = torch.empty_like(res5)
+
+            def gu5():
+                dl.dl_gate_up_silu(n2, lay.w["wg"], lay.w["wu"], act)
+
+            def dn5():
+                dl.dl_down_residual(act, lay.w["wd"], fo5, residual=res5)
+
+            for _ in range(3):
+                gu5()
+                dn5()
+            gu_ms = time_launches(gu5, max(args.steps, 20), stream)
+            dn_ms = time_launches(dn5, max(args.steps, 20), stream)
+            gu_bytes = 2.0 * I5 * H5 * 2 + B5 * H5 * 2 + B5 * I5 * 2
+            dn_bytes = 1.0 * H5 * I5 * 2 + B5 * I5 * 2 + 2.0 * B5 * H5 * 4
+            f_gbs = (gu_bytes + dn_bytes) / ((gu_ms + dn_ms) * 1e-3) / 1e9
+            ffn = {"kernel": "gate/up + SiLU*mul and down + residual (row-block weight stream)",
+                   "achieved": round(f_gbs, 1), "unit": "GB/s",
+                   "frac": round(f_gbs / PEAK_HBM_GBS, 4),
+                   "gate_up": {"avg_launch_ms": round(gu_ms, 4), "bytes_per_launch": gu_bytes,
+                               "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                   "down": {"avg_launch_ms": round(dn_ms, 4), "bytes_per_launch": dn_bytes,
+                            "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
             outs.append({
                 "workload": "llama2-70b-layer-decode-b%d-ctx%d" % (B5, mx), "batch": B5,
                 "context": mx, "value": round(B5 / (ems * 1e-3), 1), "unit": "tokens/s",
@@ -482,11 +510,13 @@ def main():
                 "attention": {"kernel": "paged decode attention, 8-head query groups "
                               "(split-KV + combine)", "achieved": round(a_gbs, 1),
                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4),
-                              "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)}})
+                              "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
+                "ffn": ffn})
             log(f"[bench] 70B decode B{B5} x {mx}: eager {ems:.4f} ms, graph {gms:.4f} ms per "
                 f"step ({outs[-1]['graph_step_hbm_frac'] * 100:.0f}% of HBM peak); attention "
-                f"{a_ms * 1e3:.1f} us = {a_gbs:,.0f} GB/s")
-            del kc5, vc5, ws5, aws
+                f"{a_ms * 1e3:.1f} us = {a_gbs:,.0f} GB/s; FFN gate/up {gu_ms * 1e3:.1f} us + "
+                f"down {dn_ms * 1e3:.1f} us = {f_gbs:,.0f} GB/s")
+            del kc5, vc5, ws5, aws, n2, act, res5, fo5
             torch.cuda.empty_cache()
         del lay
         torch.cuda.empty_cache()
