@@ -113,6 +113,55 @@ def test_linear_random_bf16(M, N, K):
     assert_bf16_close(host(out)[rows], oracle.linear(x[rows], w, round_bf16=True), "linear")
 
 
+# Decode batches of at most 16 rows against N >= 4096 go to the row-block
+# weight stream (16 weight rows per workgroup, K split over its waves): K
+# ranges that leave each wave a ragged tail of k groups, and each row length
+# class with its own unroll/wave choice (K < 8192, 8192, >= 14336).
+ROW16_SHAPES = [(1, 4096, 4096), (13, 4096, 4128), (16, 4352, 8192), (3, 4096, 14336),
+                (9, 8192, 14368)]
+
+
+@pytest.mark.parametrize("M,N,K", ROW16_SHAPES)
+def test_linear_row_block_stream_exact(M, N, K):
+    print(f"linear row16 int {M}x{N}x{K}", flush=True)
+    x = R.integers(-3, 4, (M, K)).astype(np.float32)
+    w = R.integers(-3, 4, (N, K)).astype(np.float32)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dl.dl_linear(dev_bf16(x), dev_bf16(w), out)
+    assert np.array_equal(host(out), bf(oracle.linear(x, w)))  # |sum| < 2^24: exact
+
+
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_ffn_and_qkv_row_block_stream(T):
+    print(f"row16 ffn/qkv T={T}", flush=True)
+    H, I = 4096, 2048                      # gate/up N = 4096, down N = 4096 (K = 2048)
+    x = rnd(T, H)
+    wg, wu = (rnd(I, H, scale=0.02) for _ in range(2))
+    wd = rnd(H, I, scale=0.02)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    a = torch.empty(T, I, dtype=torch.bfloat16, device=DEV)
+    dl.dl_gate_up_silu(dev_bf16(x), dev_bf16(wg), dev_bf16(wu), a)
+    assert_bf16_close(host(a), oracle.swiglu(x, wg, wu, mode=oracle.BF16), "a")
+    y = torch.empty(T, H, device=DEV)
+    dl.dl_down_residual(a, dev_bf16(wd), y, residual=dev_f32(r))
+    assert_f32_close(host(y), oracle.down_residual(host(a), wd, r), "down+resid", max_abs=3e-2,
+                     rel=1e-2)
+    Hq, Hkv, D = 16, 8, 128                # QKV N = 32 x 128 = 4096: 256 row blocks
+    wq, wk, wv = (rnd(h * D, H, scale=0.02) for h in (Hq, Hkv, Hkv))
+    pos = R.integers(0, 4000, T).astype(np.int32)
+    cs = torch.empty(4000, D, device=DEV)
+    dl.dl_rope_table_fill(cs, 4000, D, 1e4)
+    q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=DEV)
+    k = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    dl.dl_qkv_rope(dev_bf16(x), dev_bf16(wq), dev_bf16(wk), dev_bf16(wv), dev_i32(pos), cs, q, k,
+                   v)
+    rq, rk, rv = oracle.qkv_rope(x, wq, wk, wv, pos, 1e4, Hq, Hkv, D, mode=oracle.BF16)
+    assert_bf16_close(host(q), rq, "q")
+    assert_bf16_close(host(k), rk, "k")
+    assert_bf16_close(host(v), rv, "v")
+
+
 QKV_CASES = [  # T, H, Hq, Hkv, D
     (1, 256, 4, 4, 64), (37, 512, 8, 2, 128), (64, 1024, 8, 8, 128), (300, 512, 4, 1, 64),
     (700, 1024, 8, 2, 128),
