@@ -25,11 +25,14 @@ __device__ __forceinline__ f32x4 ld4f(const T* p) {
   return f32x4{o[0], o[1], o[2], o[3]};
 }
 
-// NV: 4-element vectors per thread (H <= 4 * NV * kNormThreads).
-template <typename Tin, typename Tout, int NV>
-__global__ void __launch_bounds__(kNormThreads)
+// NV: 4-element vectors per thread (H <= 4 * NV * NT).  NT = 256 threads per
+// row for prefill-sized row counts; 1024 for a handful of decode rows, where
+// the few workgroups' load latency, not bandwidth, sets the time.
+template <typename Tin, typename Tout, int NV, int NT = kNormThreads>
+__global__ void __launch_bounds__(NT)
 rmsnorm_kernel(const Tin* __restrict__ x, const float* __restrict__ rin, float* __restrict__ rout,
                const Tout* __restrict__ gamma, Tout* __restrict__ out, int H, float eps) {
+  constexpr int kNormThreads = NT;
   __shared__ float red[kNormThreads / kWave];
   const int64_t row = blockIdx.x;
   const int nv = H / 4;
@@ -78,6 +81,16 @@ hipError_t rmsnorm_residual(const Tin* x, const float* resid_in, float* resid_ou
                             const Tout* gamma, Tout* out, int T, int H, float eps,
                             hipStream_t st) {
   if (T == 0) return hipSuccess;
+  if (T <= 64 && H / 4 > 2 * kNormThreads) {
+    // decode-sized: 1024 threads per row, at most 2 vectors each (H <= 8192)
+    if (H / 4 <= 1024)
+      hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 1, 1024>), dim3(T), dim3(1024), 0, st, x,
+                         resid_in, resid_out, gamma, out, H, eps);
+    else
+      hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 2, 1024>), dim3(T), dim3(1024), 0, st, x,
+                         resid_in, resid_out, gamma, out, H, eps);
+    return hipGetLastError();
+  }
   const int nvt = (H / 4 + kNormThreads - 1) / kNormThreads;
   if (nvt <= 1)
     hipLaunchKernelGGL((rmsnorm_kernel<Tin, Tout, 1>), dim3(T), dim3(kNormThreads), 0, st, x,
