@@ -103,9 +103,10 @@ def main():
                     help="prefix length of the CPU-oracle sample")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this layer is "
-              "built and measured on a single MI355X, see the sharding notes in DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is "
+              "built and measured on a single MI355X; across GPUs decode would shard by "
+              "sequence (no exchange) or by KV head and FFN columns with one all-reduce after "
+              "O and one after down, none of which is built here", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
