@@ -499,6 +499,7 @@ def main():
                    "achieved": round(f_gbs, 1), "unit": "GB/s",
                    "frac": round(f_gbs / PEAK_HBM_GBS, 4),
                    "gate_up": {"avg_launch_ms": round(gu_ms, 4), "bytes_per_launch": gu_bytes,
+                               "traffic": load_traffic("gemm_gateup_silu_decode_70b"),
                                "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
                    "down": {"avg_launch_ms": round(dn_ms, 4), "bytes_per_launch": dn_bytes,
                             "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}

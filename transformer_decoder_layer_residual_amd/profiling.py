@@ -43,6 +43,10 @@ KERNELS = {
     "gemm_gateup_silu_prefill": (r"gemm_pp_kernelILi256ELi64ENS_9MapSwiglu"
                                  r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
                                  ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
+    # the 70B-shaped decode gate/up (K = 8192: 16-deep, 8 waves; B4 and B1 calls)
+    "gemm_gateup_silu_decode_70b": (r"gemm_row16_kernelILi16ELi8ENS_9MapSwiglu"
+                                    r"|gemm_row16_kernel<16, 8, dl::MapSwiglu",
+                                    ("gemm_decode.hpp", "gemm_epi.hpp", "dl_common.hpp")),
     "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16bLi128ELi1E"
                           r"|attn_decode_kernel<bool _Accum, bool _Accum, 128, 1,",
                           ("attn_decode.hip", "dl_common.hpp")),
