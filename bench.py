@@ -42,6 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decoder-layer tokens/s (prefill, decode) + % of HBM/MFMA roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+SPEC_CLOCK_MHZ = 2400.0        # clock the published peaks are quoted at
 
 
 def log(*a):
@@ -64,6 +65,64 @@ def load_traffic(kernel_key: str):
     if not rec or rec.get("source_sha") != profiling.source_sha(*srcs):
         return None
     return rec.get("bytes_per_launch")
+
+
+def gfx_clock_mhz():
+    """Current graphics clock from `amd-smi metric -c --json` (a child
+    process), averaged over the GPU's XCD clock domains; with several GPUs
+    listed, the busiest (highest) one.  None when the tool is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    gpus = d.get("gpu_data", []) if isinstance(d, dict) else d
+    best = None
+    for g in gpus if isinstance(gpus, list) else []:
+        vals = []
+        for k, v in (g.get("clock") or {}).items():
+            c = v.get("clk") if isinstance(v, dict) and k.startswith("gfx") else None
+            if isinstance(c, dict) and isinstance(c.get("value"), (int, float)):
+                vals.append(float(c["value"]))
+        if vals:
+            m = sum(vals) / len(vals)
+            best = m if best is None else max(best, m)
+    return best
+
+
+def clock_under(fn, stream, samples=4, limit_s=30.0):
+    """Graphics clock sampled while fn repeats back to back on the GPU
+    (outside every timed region): mean of the samples taken, or None.  The
+    reported clock follows the load with a lag of about a second, so the
+    load runs 2 s before the first sample and samples are 0.5 s apart."""
+    import threading
+    vals, stop = [], threading.Event()
+
+    def sampler():
+        if stop.wait(2.0):
+            return
+        while not stop.is_set() and len(vals) < samples:
+            v = gfx_clock_mhz()
+            if v is None:
+                return
+            vals.append(v)
+            stop.wait(0.5)
+
+    for _ in range(5):
+        fn()
+    stream.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while th.is_alive() and time.perf_counter() - t0 < limit_s:
+        for _ in range(10):
+            fn()
+        stream.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    return round(sum(vals) / len(vals), 1) if vals else None
 
 
 def time_synced(fn, n, stream):
@@ -180,6 +239,10 @@ def main():
     gu_traffic = load_traffic("gemm_gateup_silu_prefill")
     log(f"[bench] gate/up GEMM: {gu_ms:.3f} ms, {gu_tf:.0f} TFLOP/s "
         f"({100 * gu_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+    # graphics clock under the prefill step (sampled after the timed region):
+    # the published peaks are at 2400 MHz
+    clk_prefill = clock_under(step, stream)
+    log(f"[bench] graphics clock under the prefill step: {clk_prefill} MHz")
 
     result = {
         "metric": METRIC,
@@ -200,7 +263,13 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "gemm gate/up + SiLU*mul",
                      "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": gu_traffic,
-                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4)},
+                     "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4),
+                     "frac_at_measured_clock": (round(gu_tf / (PEAK_BF16_TFLOPS * clk_prefill
+                                                               / SPEC_CLOCK_MHZ), 4)
+                                                if clk_prefill else None)},
+        "clock": {"spec_mhz": SPEC_CLOCK_MHZ, "prefill_step_mhz": clk_prefill,
+                  "source": "amd-smi metric -c, mean over the XCD clock domains, sampled while "
+                            "the step repeats after its timed region"},
         "layer": {"flops_per_step": layer_flops,
                   "achieved_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "frac_of_bf16_peak": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -287,6 +356,10 @@ def main():
                                                  else "attn_decode_paged"),
                          "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         }
+        if not int8:
+            clk = clock_under(dstep, stream)
+            result["clock"]["decode_step_mhz"] = clk
+            log(f"[bench] graphics clock under the decode step: {clk} MHz")
         log(f"[bench] decode ({kind} cache): {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} "
             f"tokens/s (graph {gms:.3f} ms); attention {a_ms:.3f} ms = {a_gbs:,.0f} GB/s")
         del caches, kc, vc, sc, dws, aws
