@@ -583,7 +583,10 @@ def main():
                 "graph_step_hbm_frac": round((w_bytes + kv_bytes) / (gms * 1e-3) / 1e9
                                              / PEAK_HBM_GBS, 4),
                 "attention": {"kernel": "paged decode attention, 8-head query groups "
-                              "(split-KV + combine)", "achieved": round(a_gbs, 1),
+                              "(split-KV + combine)",
+                              # back-to-back launches over less than the 256 MB MALL
+                              "cache_state": "warm" if a_bytes < 256e6 else "cold",
+                              "achieved": round(a_gbs, 1),
                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4),
                               "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
                 "ffn": ffn})
