@@ -99,6 +99,21 @@ def test_layer_workspace_queries(L):
     assert L.dl_layer_workspace_size(ctypes.byref(bad), 64, 64, 64, 64, dl.DL_FUSED) == 0
 
 
+def test_decode_projection_workspaces(L):
+    """Up to 16 rows against N >= 4096 stream 16-row weight blocks with K
+    split inside the workgroup: no fp32 partials, so no workspace.  64 rows
+    take the 128-row stream with split-K partials; a narrow N (< 4096) keeps
+    the 128-row stream at any decode size."""
+    bf = dl.DL_BF16
+    for M in (1, 4, 16):
+        assert L.dl_linear_workspace_size(M, 8192, 28672, bf) == 0          # 70B-shaped down
+        assert L.dl_gate_up_silu_workspace_size(M, 8192, 28672, bf) == 0    # 70B gate/up
+        assert L.dl_down_residual_workspace_size(M, 4096, 14336, bf) == 0   # 8B down
+    assert L.dl_linear_workspace_size(64, 4096, 11008, bf) > 0              # 7B down, B64
+    assert L.dl_linear_workspace_size(17, 8192, 28672, bf) > 0
+    assert L.dl_linear_workspace_size(4, 2048, 8192, bf) > 0                 # N / 16 < 256
+
+
 def test_product_code_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "transformer_decoder_layer_residual_amd")
     for dirpath, _, files in os.walk(pkg):
