@@ -487,7 +487,48 @@ def main():
                                             / PEAK_HBM_GBS, 4)}
         log(f"[bench] 8B decode B{B4}: eager {ems:.4f} ms, graph {gms:.4f} ms per step; with a "
             f"host sync per step: eager {ems_sync:.4f} ms, graph {gms_sync:.4f} ms")
-        del kc4, vc4, ws4, lay
+        del kc4, vc4, ws4
+
+        # The workload as a sequence: 128 decode steps on the cache its prefill
+        # left, contexts S_b+1 .. S_b+128 (each step writes its token's K/V into
+        # the paged cache before attending); HIP events around every step,
+        # median over the 128 steps.
+        lens = gen.prefill_batch(c4).lens.astype(np.int32)
+        btS = gen.block_table(c4, lens + 128)
+        kb, vb = gen.synthetic_cache(c4, btS, lens + 1)       # positions < S_b
+        kcS, vcS = cache_dev(kb), cache_dev(vb)
+        del kb, vb
+        btSd = i32(btS.table)
+        mxS = int(lens.max()) + 128
+        wsS = torch.empty(dl.dl_layer_workspace_size(lay.dims, B4, B4, 0, mxS, mode),
+                          dtype=torch.uint8, device="cuda:0")
+        posS = [i32(lens + i) for i in range(128)]
+        ctxS = [i32(lens + i + 1) for i in range(128)]
+
+        def run_seq(evs=None):
+            for i in range(128):
+                if evs:
+                    evs[i][0].record(stream)
+                dl.dl_layer_decode(lay.dims, lay.w, lay.cs, x4, y4, posS[i], ctxS[i], mxS, kcS,
+                                   vcS, btSd, ws=wsS)
+                if evs:
+                    evs[i][1].record(stream)
+
+        run_seq()                      # warm-up pass: writes the K/V the timed pass rewrites
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(128)]
+        run_seq(evs)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        med, p10, p90 = ts[64], ts[12], ts[115]
+        out["steps128"] = {"context": "S_b+1 .. S_b+128, S_b ~ U{256..1024}",
+                           "median_ms_per_step": round(med, 4), "p10_ms": round(p10, 4),
+                           "p90_ms": round(p90, 4),
+                           "median_tokens_per_s": round(B4 / (med * 1e-3), 1)}
+        log(f"[bench] 8B decode B{B4}, 128 steps from the prefill lengths: median {med:.4f} ms "
+            f"(p10 {p10:.4f}, p90 {p90:.4f})")
+        del kcS, vcS, wsS, lay
         torch.cuda.empty_cache()
         return out
 
