@@ -665,6 +665,30 @@ def main():
             "value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of the {T} prefill tokens, same weights, exact fp32/fp64 "
                       f"mode, {dt:.1f} s"}
+        # the decode step too: the oracle's layer step for the first sequences
+        # of the 7B decode workload, over their own cache blocks (the bf16
+        # cache's values in fp32), same weights
+        if not args.no_decode:
+            dcfg = gen.CONFIGS[3]
+            nb = 16
+            dctx = gen.decode_context_lens(dcfg)[:nb]
+            dbt = gen.block_table(dcfg, dctx)
+            kb, vb = gen.synthetic_cache(dcfg, dbt, dctx)
+            kf, vf = gen.bits_to_f32(kb), gen.bits_to_f32(vb)
+            del kb, vb
+            xdh = gen.hidden(dcfg, nb)
+            log(f"[bench] CPU oracle decode step for {nb} sequences")
+            t0 = time.time()
+            oracle.layer_decode(dcfg.dims(), w_host, xdh, dctx, kf, vf, dbt.table,
+                                mode=oracle.EXACT)
+            ddt = time.time() - t0
+            result["cpu_baseline_decode"] = {
+                "value": round(nb / ddt, 2), "unit": "tokens/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"first {nb} of the 64 sequences of the 7B decode step (contexts "
+                          f"{', '.join(str(int(c)) for c in dctx)}), same weights, exact "
+                          f"fp32/fp64 mode, {ddt:.2f} s"}
+            del kf, vf
     print(json.dumps(result), flush=True)
 
 
