@@ -213,6 +213,17 @@ def main():
     torch.cuda.synchronize()
     ms = time_launches(step, args.steps, stream)
     tok_s = T / (ms * 1e-3)
+    # per-step spread (a second pass with an event pair around every step)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(args.steps, 20))]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    st_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    pct = {q: round(st_ms[min(len(st_ms) - 1, int(q / 100 * len(st_ms)))], 4)
+           for q in (10, 50, 90)}
     H, Hq, D, I = cfg.hidden, cfg.n_q_heads, cfg.head_dim, cfg.intermediate
     Hkv = cfg.n_kv_heads
     gemm_flops = 2.0 * T * H * ((Hq + 2 * Hkv) * D + Hq * D + 2 * I + I)
@@ -270,6 +281,8 @@ def main():
         "clock": {"spec_mhz": SPEC_CLOCK_MHZ, "prefill_step_mhz": clk_prefill,
                   "source": "amd-smi metric -c, mean over the XCD clock domains, sampled while "
                             "the step repeats after its timed region"},
+        "step_ms_percentiles": {"p10": pct[10], "p50": pct[50], "p90": pct[90],
+                                "steps": len(st_ms)},
         "layer": {"flops_per_step": layer_flops,
                   "achieved_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "frac_of_bf16_peak": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
