@@ -23,10 +23,17 @@ Beside it the JSON line carries:
                 the step replayed as one HIP graph, back to back and with a
                 host synchronisation after every step (decode lines above also
                 carry their graph timing);
-  cpu_baseline  the CPU oracle on a bounded prefix of the same prefill.
+  prefill_gqa_8b  the Llama-3-8B-shaped GQA layer prefilling 8 ragged
+                sequences U{256..1024} (tokens/s, its gate/up GEMM roofline);
+  cpu_baseline  the CPU oracle on a bounded prefix of the same prefill (all
+                host threads; the decode and tiny-layer samples also on one).
 
 Inputs are resident in HBM before the timed region; weights and activations
-are seeded synthetic data.
+are seeded synthetic data.  Timed steps are cold: before every step, outside
+its HIP event pair, a 1 GiB buffer is written, which evicts the L2s and the
+256 MB MALL, and the step's time is the median over the steps; back-to-back
+(warm) means are reported beside them.  Every timed line names its
+cache_state.
 """
 from __future__ import annotations
 
@@ -136,6 +143,54 @@ def time_synced(fn, n, stream):
     return (time.perf_counter() - t0) * 1e3 / n
 
 
+FLUSH_BYTES = 1 << 30
+
+
+class Flusher:
+    """Writes a 1 GiB device buffer (a fill kernel on the timing stream), which
+    evicts every L2 and the MALL between timed steps."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+        self.k = 0
+
+    def __call__(self):
+        self.k += 1
+        self.buf.fill_(self.k)
+
+
+def time_cold(fn, n, stream, flush):
+    """n steps, each preceded by a cache flush outside its event pair: (median,
+    p10, p90) in ms."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    q = lambda f: t[min(len(t) - 1, int(f * len(t)))]
+    return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2]), \
+        q(0.1), q(0.9)
+
+
+def warm_up(fn, n, stream, min_s=1.0):
+    """At least n steps and at least min_s seconds of them (the clocks settle
+    under sustained load)."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < min_s:
+        fn()
+        i += 1
+        if i % 8 == 0:
+            stream.synchronize()
+    stream.synchronize()
+
+
 def time_launches(fn, n, stream):
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -146,6 +201,82 @@ def time_launches(fn, n, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / n   # ms per launch
+
+
+def host_cpu():
+    """CPU model, sockets and logical CPUs of the host (lscpu)."""
+    import subprocess
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return info
+    for line in out.splitlines():
+        k, _, v = line.partition(":")
+        k, v = k.strip(), v.strip()
+        if k == "Model name":
+            info["model"] = v
+        elif k == "Socket(s)":
+            info["sockets"] = int(v) if v.isdigit() else v
+        elif k == "Core(s) per socket":
+            info["cores_per_socket"] = int(v) if v.isdigit() else v
+    return info
+
+
+def cpu_sample(kind: str) -> dict:
+    """A bounded CPU-oracle sample (no GPU): 'tiny' = the tiny fp32 layer's
+    32-token prefill then 8 decode steps on its own cache; 'decode' = the 7B
+    decode layer step for the first 4 sequences of the 7B decode workload."""
+    import numpy as np
+
+    import oracle
+    from transformer_decoder_layer_residual_amd import inputs as gen
+    if kind == "tiny":
+        cfg = gen.CONFIGS[1]
+        w = gen.weights(cfg)
+        pb = gen.prefill_batch(cfg)
+        bt = gen.block_table(cfg, pb.lens + cfg.decode_steps)
+        kb, vb = gen.empty_cache(cfg, bt.num_blocks)
+        kf, vf = gen.cache_to_f32(kb).copy(), gen.cache_to_f32(vb).copy()
+        x = gen.hidden(cfg, pb.T)
+        xs = [gen.hidden(cfg, 1, step=1 + s) for s in range(cfg.decode_steps)]
+        t0 = time.perf_counter()
+        oracle.layer_prefill(cfg.dims(), w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens, kf,
+                             vf, bt.table, mode=oracle.EXACT)
+        t1 = time.perf_counter()
+        for s in range(cfg.decode_steps):
+            ctx = np.array([pb.T + s + 1], np.int32)
+            oracle.layer_decode(cfg.dims(), w, xs[s], ctx, kf, vf, bt.table, mode=oracle.EXACT)
+        t2 = time.perf_counter()
+        return {"prefill_tokens_per_s": round(pb.T / (t1 - t0), 1),
+                "decode_tokens_per_s": round(cfg.decode_steps / (t2 - t1), 1),
+                "seconds": round(t2 - t0, 4)}
+    cfg = gen.CONFIGS[3]
+    nb = 4
+    w = gen.weights(cfg)
+    ctx = gen.decode_context_lens(cfg)[:nb]
+    bt = gen.block_table(cfg, ctx)
+    kb, vb = gen.synthetic_cache(cfg, bt, ctx)
+    kf, vf = gen.bits_to_f32(kb), gen.bits_to_f32(vb)
+    x = gen.hidden(cfg, nb)
+    t0 = time.perf_counter()
+    oracle.layer_decode(cfg.dims(), w, x, ctx, kf, vf, bt.table, mode=oracle.EXACT)
+    dt = time.perf_counter() - t0
+    return {"value": round(nb / dt, 3), "unit": "tokens/s", "cores": 1,
+            "sample": f"first {nb} sequences of the 7B decode step (contexts "
+                      f"{', '.join(str(int(c)) for c in ctx)}), exact mode, {dt:.2f} s"}
+
+
+def cpu_child(kind: str) -> dict:
+    """cpu_sample in a child process pinned to one OpenMP thread (the child
+    never touches the GPU)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-sample", kind],
+                       capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        return {"error": (r.stderr or "")[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -160,7 +291,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="prefix length of the CPU-oracle sample")
+    ap.add_argument("--cpu-sample", choices=["tiny", "decode"], default=None,
+                    help=argparse.SUPPRESS)   # the one-thread CPU child (no GPU use)
     args = ap.parse_args()
+    if args.cpu_sample:
+        print(json.dumps(cpu_sample(args.cpu_sample)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is "
               "built and measured on a single MI355X; across GPUs decode would shard by "
@@ -208,28 +344,18 @@ def main():
         dl.dl_layer_prefill(layer.dims, layer.w, layer.cs, x, y, pos, seq, cu, pb.max_seqlen, kc,
                             vc, btd, mode=mode, ws=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ms = time_launches(step, args.steps, stream)
+    flush = Flusher()
+    warm_up(step, args.warmup, stream)
+    ms, p10, p90 = time_cold(step, args.steps, stream, flush)
     tok_s = T / (ms * 1e-3)
-    # per-step spread (a second pass with an event pair around every step)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(max(args.steps, 20))]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    st_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    pct = {q: round(st_ms[min(len(st_ms) - 1, int(q / 100 * len(st_ms)))], 4)
-           for q in (10, 50, 90)}
+    warm_ms = time_launches(step, args.steps, stream)
     H, Hq, D, I = cfg.hidden, cfg.n_q_heads, cfg.head_dim, cfg.intermediate
     Hkv = cfg.n_kv_heads
     gemm_flops = 2.0 * T * H * ((Hq + 2 * Hkv) * D + Hq * D + 2 * I + I)
     attn_flops = 4.0 * Hq * D * float((pb.lens.astype(np.int64) * (pb.lens + 1) // 2).sum())
     layer_flops = gemm_flops + attn_flops
-    log(f"[bench] prefill: {ms:.3f} ms/step, {tok_s:,.0f} tokens/s, "
+    log(f"[bench] prefill: {ms:.3f} ms/step (median, cold; p10 {p10:.3f}, p90 {p90:.3f}; "
+        f"back-to-back {warm_ms:.3f}), {tok_s:,.0f} tokens/s, "
         f"{layer_flops / (ms * 1e-3) / 1e12:.0f} TFLOP/s")
 
     # dominant kernel: gate/up GEMM with the SiLU*mul epilogue, timed with HIP
@@ -271,7 +397,11 @@ def main():
         "config": {"workload": "llama2-7b-layer-prefill", "batch": 1, "seq_len": T,
                    "hidden": H, "heads": f"{Hq}/{Hkv}x{D}", "intermediate": I,
                    "mode": args.mode},
+        "cache_state": "cold: 1 GiB written before every step, outside its events; "
+                       "ms_per_step is the median over the steps",
+        "warm_back_to_back_ms_per_step": round(warm_ms, 4),
         "roofline": {"bound": "mfma", "kernel": "gemm gate/up + SiLU*mul",
+                     "cache_state": "inside back-to-back step-by-step layer chains",
                      "achieved": round(gu_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": gu_traffic,
                      "flops_per_launch": gu_flops, "avg_launch_ms": round(gu_ms, 4),
@@ -281,8 +411,8 @@ def main():
         "clock": {"spec_mhz": SPEC_CLOCK_MHZ, "prefill_step_mhz": clk_prefill,
                   "source": "amd-smi metric -c, mean over the XCD clock domains, sampled while "
                             "the step repeats after its timed region"},
-        "step_ms_percentiles": {"p10": pct[10], "p50": pct[50], "p90": pct[90],
-                                "steps": len(st_ms)},
+        "step_ms_percentiles": {"p10": round(p10, 4), "p50": round(ms, 4), "p90": round(p90, 4),
+                                "steps": args.steps},
         "layer": {"flops_per_step": layer_flops,
                   "achieved_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 1),
                   "frac_of_bf16_peak": round(layer_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -290,6 +420,73 @@ def main():
     }
     del ws, kc, vc
     torch.cuda.empty_cache()
+
+    # ------------------------------------------- 8B-GQA ragged prefill batch
+    def run_prefill_gqa():
+        """Llama-3-8B-shaped GQA layer (32/8 heads x 128, I 14336, theta 5e5):
+        one prefill call over 8 packed sequences of U{256..1024} tokens."""
+        c4 = gen.CONFIGS[4]
+        pb4 = gen.prefill_batch(c4)
+        T4 = pb4.T
+        log(f"[bench] generating {c4.name} prefill inputs (T={T4}, lens {pb4.lens.tolist()})")
+        lay = DeviceLayer.build(c4, max_pos=int(pb4.lens.max()) + 1)
+        x4 = to_dev(gen.hidden(c4, T4), torch.float32)
+        y4 = torch.empty_like(x4)
+        bt4 = gen.block_table(c4, pb4.lens)
+        kb, vb = gen.empty_cache(c4, bt4.num_blocks)
+        kc4, vc4 = cache_dev(kb), cache_dev(vb)
+        bt4d = i32(bt4.table)
+        p4, s4, cu4 = i32(pb4.positions), i32(pb4.seq_of_token), i32(pb4.cu_seqlens)
+        ws4 = torch.empty(dl.dl_layer_workspace_size(lay.dims, T4, pb4.B, pb4.max_seqlen, 0, mode),
+                          dtype=torch.uint8, device="cuda:0")
+
+        def step4():
+            dl.dl_layer_prefill(lay.dims, lay.w, lay.cs, x4, y4, p4, s4, cu4, pb4.max_seqlen, kc4,
+                                vc4, bt4d, mode=mode, ws=ws4)
+
+        warm_up(step4, args.warmup, stream)
+        ms4, q10, q90 = time_cold(step4, args.steps, stream, flush)
+        warm4 = time_launches(step4, args.steps, stream)
+        kc5, vc5 = cache_dev(kb), cache_dev(vb)
+        pairs4 = []
+        for i in range(max(args.steps // 2, 10) + 2):
+            ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            lay.steps_prefill(x4, pb4, kc5, vc5, bt4d, gu_events=ev)
+            if i >= 2:
+                pairs4.append(ev)
+        torch.cuda.synchronize()
+        gu4_ms = sum(a.elapsed_time(b) for a, b in pairs4) / len(pairs4)
+        H4, Hq4, Hkv4, D4, I4 = c4.hidden, c4.n_q_heads, c4.n_kv_heads, c4.head_dim, \
+            c4.intermediate
+        g_fl = 2.0 * T4 * H4 * ((Hq4 + 2 * Hkv4) * D4 + Hq4 * D4 + 3 * I4)
+        a_fl = 4.0 * Hq4 * D4 * float((pb4.lens.astype(np.int64) * (pb4.lens + 1) // 2).sum())
+        gu4_fl = 2.0 * T4 * (2 * I4) * H4
+        gu4_tf = gu4_fl / (gu4_ms * 1e-3) / 1e12
+        out = {"workload": "llama3-8b-gqa-layer-prefill-b8-ragged", "batch": pb4.B,
+               "tokens": T4, "lens": pb4.lens.tolist(),
+               "value": round(T4 / (ms4 * 1e-3), 1), "unit": "tokens/s",
+               "ms_per_step": round(ms4, 4),
+               "cache_state": "cold (1 GiB written before every step; median)",
+               "step_ms_p10_p90": [round(q10, 4), round(q90, 4)],
+               "warm_back_to_back_ms_per_step": round(warm4, 4),
+               "layer": {"flops_per_step": g_fl + a_fl,
+                         "achieved_tflops": round((g_fl + a_fl) / (ms4 * 1e-3) / 1e12, 1),
+                         "frac_of_bf16_peak": round((g_fl + a_fl) / (ms4 * 1e-3) / 1e12
+                                                    / PEAK_BF16_TFLOPS, 4)},
+               "roofline": {"bound": "mfma", "kernel": "gemm gate/up + SiLU*mul",
+                            "cache_state": "inside back-to-back step-by-step layer chains",
+                            "achieved": round(gu4_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(gu4_tf / PEAK_BF16_TFLOPS, 4),
+                            "traffic": None, "flops_per_launch": gu4_fl,
+                            "avg_launch_ms": round(gu4_ms, 4)}}
+        log(f"[bench] 8B GQA prefill B8 ragged (T={T4}): {ms4:.3f} ms/step (cold median; "
+            f"back-to-back {warm4:.3f}), {T4 / (ms4 * 1e-3):,.0f} tokens/s; gate/up "
+            f"{gu4_ms:.3f} ms = {gu4_tf:.0f} TFLOP/s")
+        del kc4, vc4, kc5, vc5, ws4, lay
+        torch.cuda.empty_cache()
+        return out
+
+    result["prefill_gqa_8b"] = run_prefill_gqa()
 
     # ------------------------------------------------------------------ decode
     def run_decode(int8: bool):
@@ -317,10 +514,9 @@ def main():
             dl.dl_layer_decode(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, kc,
                                vc, dbtd, mode=mode, ws=dws, **sc)
 
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        dms = time_launches(dstep, args.steps, stream)
+        warm_up(dstep, args.warmup, stream)
+        dms, dp10, dp90 = time_cold(dstep, args.steps, stream, flush)
+        dwarm = time_launches(dstep, args.steps, stream)
         # the same step replayed as one HIP graph (dl_layer_decode_graph_create)
         side = torch.cuda.Stream()
         graph = dl.DecodeGraph(layer.dims, layer.w, layer.cs, xd, yd, dpos, dctx, max_ctx, kc, vc,
@@ -343,7 +539,8 @@ def main():
 
         for _ in range(3):
             dattn()
-        a_ms = time_launches(dattn, max(args.steps, 20), stream)
+        a_ms, _, _ = time_cold(dattn, max(args.steps, 20), stream, flush)
+        a_warm = time_launches(dattn, max(args.steps, 20), stream)
         # per cached token and kv head: K and V rows of D elements (+ a 4-byte
         # scale each for INT8)
         row_bytes = 2.0 * ((D + 4) if int8 else D * 2)
@@ -358,7 +555,11 @@ def main():
             "kv_cache": "int8 codes + fp32 per-token scales" if int8 else "bf16",
             "value": round(B / (dms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(dms, 4),
+            "cache_state": "cold (1 GiB written before every step; median)",
+            "step_ms_p10_p90": [round(dp10, 4), round(dp90, 4)],
+            "warm_back_to_back_ms_per_step": round(dwarm, 4),
             "graph_ms_per_step": round(gms, 4),
+            "graph_cache_state": "warm (back-to-back replays)",
             "graph_tokens_per_s": round(B / (gms * 1e-3), 1),
             "step_hbm_frac": round(step_bytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm", "kernel": "paged decode attention (split-KV + combine)"
@@ -367,7 +568,9 @@ def main():
                          "frac": round(a_gbs / PEAK_HBM_GBS, 4),
                          "traffic": load_traffic("attn_decode_paged_int8" if int8
                                                  else "attn_decode_paged"),
-                         "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
+                         "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4),
+                         "cache_state": "cold (median of flushed launches)",
+                         "warm_back_to_back_ms": round(a_warm, 4)},
         }
         if not int8:
             clk = clock_under(dstep, stream)
@@ -410,10 +613,8 @@ def main():
             dl.dl_layer_decode_qlens(layer.dims, layer.w, layer.cs, xq, yq, vpos, vseq, vcu, vctx,
                                      qb.max_seqlen, int(ctx.max()), kc, vc, dbtd, ws=vws)
 
-        for _ in range(args.warmup):
-            vstep()
-        torch.cuda.synchronize()
-        vms = time_launches(vstep, args.steps, stream)
+        warm_up(vstep, args.warmup, stream)
+        vms, _, _ = time_cold(vstep, args.steps, stream, flush)
         q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device="cuda:0").normal_()
         ao = torch.empty_like(q)
         cu, dctx = i32(qb.cu_seqlens), i32(ctx)
@@ -426,7 +627,7 @@ def main():
 
         for _ in range(3):
             vattn()
-        a_ms = time_launches(vattn, max(args.steps, 20), stream)
+        a_ms, _, _ = time_cold(vattn, max(args.steps, 20), stream, flush)
         kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv * D * 2
         a_bytes = kv_bytes + 2.0 * T * Hq * D * 2
         a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
@@ -435,8 +636,10 @@ def main():
             "context": "uniform 128..4096 (mean %.0f) after the step" % ctx.mean(),
             "value": round(T / (vms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(vms, 4),
+            "cache_state": "cold (1 GiB written before every step; median)",
             "roofline": {"bound": "hbm", "kernel": "paged attention, q_len %d (split-KV + combine)"
-                         % qlen, "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         % qlen, "cache_state": "cold (median of flushed launches)",
+                         "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                          "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
         }
@@ -489,7 +692,10 @@ def main():
             c4.intermediate
         w_bytes = 2.0 * (H4 * (Hq4 + 2 * Hkv4) * D4 + Hq4 * D4 * H4 + 3 * H4 * I4)
         kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv4 * D4 * 2
+        ecold, _, _ = time_cold(step4, max(args.steps, 50), stream, flush)
         out = {"workload": "llama3-8b-layer-decode-b8", "batch": B4,
+               "cache_state": "warm (back-to-back) unless named cold",
+               "cold_eager_ms_per_step": round(ecold, 4),
                "context": "prefill lengths U{256..1024} + 64 (mean %.0f)" % ctx.mean(),
                "eager_ms_per_step": round(ems, 4), "graph_ms_per_step": round(gms, 4),
                "synced_eager_ms_per_step": round(ems_sync, 4),
@@ -574,10 +780,9 @@ def main():
                 dl.dl_layer_decode(lay.dims, lay.w, lay.cs, x5, y5, p5, c5d, mx, kc5, vc5, bt5d,
                                    ws=ws5)
 
-            for _ in range(args.warmup):
-                step5()
-            torch.cuda.synchronize()
-            ems = time_launches(step5, max(args.steps, 20), stream)
+            warm_up(step5, args.warmup, stream)
+            ems, _, _ = time_cold(step5, max(args.steps, 20), stream, flush)
+            ewarm = time_launches(step5, max(args.steps, 20), stream)
             side = torch.cuda.Stream()
             g5 = dl.DecodeGraph(lay.dims, lay.w, lay.cs, x5, y5, p5, c5d, mx, kc5, vc5, bt5d,
                                 side, ws=ws5)
@@ -597,7 +802,8 @@ def main():
 
             for _ in range(3):
                 attn5()
-            a_ms = time_launches(attn5, max(args.steps, 20), stream)
+            a_ms, _, _ = time_cold(attn5, max(args.steps, 20), stream, flush)
+            a_warm = time_launches(attn5, max(args.steps, 20), stream)
             kv_bytes = 2.0 * float(ctx.astype(np.int64).sum()) * Hkv5 * D5 * 2
             a_bytes = kv_bytes + 2.0 * B5 * Hq5 * D5 * 2
             a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
@@ -617,12 +823,13 @@ def main():
             for _ in range(3):
                 gu5()
                 dn5()
-            gu_ms = time_launches(gu5, max(args.steps, 20), stream)
-            dn_ms = time_launches(dn5, max(args.steps, 20), stream)
+            gu_ms, _, _ = time_cold(gu5, max(args.steps, 20), stream, flush)
+            dn_ms, _, _ = time_cold(dn5, max(args.steps, 20), stream, flush)
             gu_bytes = 2.0 * I5 * H5 * 2 + B5 * H5 * 2 + B5 * I5 * 2
             dn_bytes = 1.0 * H5 * I5 * 2 + B5 * I5 * 2 + 2.0 * B5 * H5 * 4
             f_gbs = (gu_bytes + dn_bytes) / ((gu_ms + dn_ms) * 1e-3) / 1e9
             ffn = {"kernel": "gate/up + SiLU*mul and down + residual (row-block weight stream)",
+                   "cache_state": "cold (median of flushed launches)",
                    "achieved": round(f_gbs, 1), "unit": "GB/s",
                    "frac": round(f_gbs / PEAK_HBM_GBS, 4),
                    "gate_up": {"avg_launch_ms": round(gu_ms, 4), "bytes_per_launch": gu_bytes,
@@ -633,13 +840,17 @@ def main():
             outs.append({
                 "workload": "llama2-70b-layer-decode-b%d-ctx%d" % (B5, mx), "batch": B5,
                 "context": mx, "value": round(B5 / (ems * 1e-3), 1), "unit": "tokens/s",
-                "ms_per_step": round(ems, 4), "graph_ms_per_step": round(gms, 4),
+                "ms_per_step": round(ems, 4),
+                "cache_state": "cold (1 GiB written before every step; median)",
+                "warm_back_to_back_ms_per_step": round(ewarm, 4),
+                "graph_ms_per_step": round(gms, 4),
                 "graph_step_hbm_frac": round((w_bytes + kv_bytes) / (gms * 1e-3) / 1e9
                                              / PEAK_HBM_GBS, 4),
                 "attention": {"kernel": "paged decode attention, 8-head query groups "
                               "(split-KV + combine)",
-                              # back-to-back launches over less than the 256 MB MALL
-                              "cache_state": "warm" if a_bytes < 256e6 else "cold",
+                              "cache_state": "cold (median of flushed launches)",
+                              "warm_back_to_back_ms": round(a_warm, 4),
+                              "warm_back_to_back_gbs": round(a_bytes / (a_warm * 1e-3) / 1e9, 1),
                               "achieved": round(a_gbs, 1),
                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4),
                               "bytes_per_launch": a_bytes, "avg_launch_ms": round(a_ms, 4)},
@@ -677,7 +888,16 @@ def main():
         result["cpu_baseline"] = {
             "value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of the {T} prefill tokens, same weights, exact fp32/fp64 "
-                      f"mode, {dt:.1f} s"}
+                      f"mode, {dt:.1f} s", "host": host_cpu()}
+        # the tiny fp32 layer (prefill of 32 tokens + 8 decode steps) on all
+        # threads here and on one thread in a child process; the 7B decode
+        # step for 4 sequences on one thread
+        tiny = cpu_sample("tiny")
+        tiny1 = cpu_child("tiny")
+        result["cpu_baseline_tiny"] = {
+            "unit": "tokens/s", "kind": "oracle",
+            "sample": "tiny fp32 layer: prefill of 32 tokens, then 8 decode steps",
+            "all_threads": {"cores": cores, **tiny}, "one_thread": {"cores": 1, **tiny1}}
         # the decode step too: the oracle's layer step for the first sequences
         # of the 7B decode workload, over their own cache blocks (the bf16
         # cache's values in fp32), same weights
@@ -700,7 +920,8 @@ def main():
                 "kind": "oracle",
                 "sample": f"first {nb} of the 64 sequences of the 7B decode step (contexts "
                           f"{', '.join(str(int(c)) for c in dctx)}), same weights, exact "
-                          f"fp32/fp64 mode, {ddt:.2f} s"}
+                          f"fp32/fp64 mode, {ddt:.2f} s",
+                "one_thread": cpu_child("decode")}
             del kf, vf
     print(json.dumps(result), flush=True)
 

@@ -34,11 +34,18 @@
  *   - Return value: DL_OK, or an error code, in which case NOTHING was
  *     enqueued; dl_last_error() then describes the failure (thread-local).
  *     DL_ERR_HIP reports a failed launch.
- *   - Device-side preconditions (not checked, never fault): block_table
- *     entries that are used lie in [0, num_blocks); 0 <= positions <
- *     max_blocks_per_seq * BS; 1 <= context_lens[b] <= max_context_len.  An
- *     out-of-range table entry makes the cache write drop the token and the
- *     attention read block 0 instead (wrong numbers, no memory fault).
+ *   - Device-side preconditions (not checked by the compute calls; a bad
+ *     entry gives wrong numbers, never a memory fault, and dl_check_indices
+ *     reports it):
+ *       block_table entries that are used lie in [0, num_blocks);
+ *       0 <= positions[t] < max_blocks_per_seq * BS;
+ *       0 <= seq_of_token[t] < number of block_table rows (B);
+ *       1 <= context_lens[b] <= max_context_len;
+ *       cu_seqlens / cu_q_lens start at 0, never decrease, end at T (Tq), and
+ *       no length exceeds max_seqlen (max_q_len).
+ *     An out-of-range table entry makes the cache write drop the token and
+ *     the attention read block 0 instead; query rows named by a cumulative
+ *     length outside [0, T) are not computed.
  *   - Supported shapes: head_dim D in {64, 128}; Hq % Hkv == 0 with
  *     Hq / Hkv in {1, 2, 4, 8}; BS in {16, 32, 64, 128}; hidden H a multiple
  *     of 32 and <= 8192; intermediate I a multiple of 16; reduction sizes a
@@ -216,7 +223,9 @@ dl_status dl_reshape_and_cache(const void* k, const void* v, const int32_t* seq_
  * cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens [B+1] int32, device, with
  * cu_seqlens[B] == T and every length <= max_seqlen).  Row i of a sequence
  * attends to rows 0..i of the same sequence; kv head = h / (Hq/Hkv).
- * q, out [T][Hq][D]; k, v [T][Hkv][D].  scale is normally 1/sqrt(D).
+ * q, out [T][Hq][D]; k, v [T][Hkv][D].  scale multiplies q.k before the
+ * softmax; scale <= 0 selects 1/sqrt(D), the scaled dot-product of the
+ * pages (ATB decoder-layer page, "operator fusion graph of a decoder layer").
  */
 dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
                           const int32_t* cu_seqlens, int32_t B, int32_t T, int32_t max_seqlen,
@@ -230,7 +239,8 @@ dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
  * Sequence b attends over cached positions 0 .. context_lens[b]-1 (the new
  * token must already be in the cache).  q, out [B][Hq][D].  The result does
  * not depend on which physical blocks hold the data.  A DL_KV_INT8 cache is
- * dequantised (code x row scale) as its blocks are read.
+ * dequantised (code x row scale) as its blocks are read.  scale <= 0 selects
+ * 1/sqrt(D), as for dl_attn_prefill.
  */
 size_t dl_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                      int32_t max_context_len, int32_t BS);
@@ -254,7 +264,7 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
  * q_len = context_lens is a prefill that reads its keys from the cache; a
  * q_len of 0 is allowed.  Preconditions as for dl_attn_decode_paged, plus
  * q_len_b <= context_lens[b] <= max_context_len.  Layer-dtype caches only
- * (an INT8 cache returns DL_ERR_UNSUPPORTED).
+ * (an INT8 cache returns DL_ERR_UNSUPPORTED).  scale <= 0 selects 1/sqrt(D).
  */
 size_t dl_attn_paged_qlens_workspace_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
                                           int32_t D, int32_t max_q_len,
@@ -391,6 +401,78 @@ dl_status dl_layer_decode_qlens(const dl_layer_dims* d, const dl_layer_weights* 
  * Errors: those of dl_layer_decode (nothing recorded, *graph untouched), or
  * DL_ERR_HIP if capture or instantiation fails.
  */
+/*
+ * Validation of the index inputs of the paged-cache calls (the ReshapeAndCache
+ * and PagedAttention inputs of the ATB KV-cache page, section "KV cache memory
+ * bottleneck": block_table, positions, the token's sequence, contextLens; and
+ * the packed-sequence offsets of prefill).  Enqueues one small kernel that
+ * reads the given arrays and stores into *error_word (device int32, 4-byte
+ * aligned; overwritten, no clearing needed) the OR of one bit per violated
+ * device-side precondition listed at the top of this header:
+ *   DL_CHECK_BIT_SEQ       seq_of_token[t] outside [0, B)
+ *   DL_CHECK_BIT_POSITION  positions[t] outside [0, max_blocks_per_seq * BS)
+ *   DL_CHECK_BIT_BLOCK     a table entry some token writes, or some context
+ *                          position reads, outside [0, num_blocks)
+ *   DL_CHECK_BIT_CONTEXT   context_lens[b] outside [1, max_context_len] or
+ *                          beyond max_blocks_per_seq * BS
+ *   DL_CHECK_BIT_CU        cu_seqlens not 0 .. T nondecreasing, or a length
+ *                          above max_seqlen
+ * 0 means every given array is valid.  Any array may be NULL to skip its
+ * checks (seq_of_token NULL means seq_of_token[t] = t, the decode case).
+ * block_table [B][max_blocks_per_seq]; positions, seq_of_token [T];
+ * context_lens [B]; cu_seqlens [B+1].  It is a debug aid: the compute calls
+ * keep their own clamps, so nothing here is needed for memory safety.
+ */
+enum {
+  DL_CHECK_BIT_SEQ = 1,
+  DL_CHECK_BIT_POSITION = 2,
+  DL_CHECK_BIT_BLOCK = 4,
+  DL_CHECK_BIT_CONTEXT = 8,
+  DL_CHECK_BIT_CU = 16
+};
+dl_status dl_check_indices(const int32_t* block_table, int32_t B, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t BS, const int32_t* positions,
+                           const int32_t* seq_of_token, int32_t T, const int32_t* context_lens,
+                           int32_t max_context_len, const int32_t* cu_seqlens,
+                           int32_t max_seqlen, int32_t* error_word, void* stream);
+
+/*
+ * Named regions of a layer workspace, for inspecting a call's intermediates
+ * after it ran: the debugging method of the ATB fusion-strategy page (section
+ * "debugging"), which runs the chain step by step and compares each
+ * intermediate tensor with the fused result.  After dl_layer_prefill (or
+ * dl_layer_decode) returns and its stream has finished, the workspace holds
+ * that call's intermediates until the next call that uses it:
+ *   DL_WS_N1, DL_WS_N2    normalised activations [T][H] (dtype)
+ *   DL_WS_Q, DL_WS_K, DL_WS_V   q [T][Hq][D], k, v [T][Hkv][D] after RoPE
+ *                         (the fused decode step writes k/v to the cache
+ *                         only, so there they are not filled)
+ *   DL_WS_ATTN            attention output [T][Hq*D]
+ *   DL_WS_O               output projection [T][H]
+ *   DL_WS_H               residual stream after attention [T][H] fp32
+ *   DL_WS_A               silu(gate) * up [T][I]
+ *   DL_UNFUSED only:      DL_WS_SCORES fp32 [B][Hq][S][S] (prefill, S =
+ *                         max_seqlen, -inf above the diagonal) or [B][Hq][S]
+ *                         (decode, S = max_context_len); DL_WS_PROBS the
+ *                         softmax of each row (dtype), same shape;
+ *                         DL_WS_GATE, DL_WS_UP, DL_WS_SILU [T][I] (dtype);
+ *                         DL_WS_DOWN the down projection [T][H] fp32
+ *   DL_WS_PARTIAL, DL_WS_DECODE   GEMM and attention split partials (opaque)
+ * offsets[r] and sizes[r] (host arrays of DL_WS_COUNT) receive each region's
+ * byte offset into the workspace and its byte size (0 when the call does not
+ * use it).  is_decode 0: the prefill layout for (T, B, max_seqlen); 1: the
+ * decode layout for (B, max_context_len), with T == B.  The dims and sizes
+ * are checked as the layer calls check them.
+ */
+typedef enum {
+  DL_WS_N1 = 0, DL_WS_Q, DL_WS_K, DL_WS_V, DL_WS_ATTN, DL_WS_O, DL_WS_H, DL_WS_N2, DL_WS_A,
+  DL_WS_PARTIAL, DL_WS_DECODE, DL_WS_SCORES, DL_WS_PROBS, DL_WS_GATE, DL_WS_UP, DL_WS_SILU,
+  DL_WS_DOWN, DL_WS_COUNT
+} dl_ws_region;
+dl_status dl_layer_workspace_regions(const dl_layer_dims* d, int32_t T, int32_t B,
+                                     int32_t max_seqlen_or_context, int32_t is_decode, dl_mode m,
+                                     size_t* offsets, size_t* sizes);
+
 typedef struct dl_graph_s* dl_graph;
 dl_status dl_layer_decode_graph_create(const dl_layer_dims* d, const dl_layer_weights* w,
                                        const float* cos_sin, int32_t max_pos,

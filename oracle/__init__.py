@@ -90,6 +90,9 @@ def _declare(L):
     L.orc_attn_decode_contig.argtypes = [_f32p, _f32p, _f32p, _i, _i32p, _i, _i,
                                          _i, _i, _d, _f32p, _i]
     L.orc_swiglu.argtypes = [_f32p, _f32p, _f32p, _f32p, _i, _i, _i, _i]
+    L.orc_swiglu_parts.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _i, _i,
+                                   _i, _i]
+    L.orc_attn_row.argtypes = [_f32p, _f32p, _f32p, _i, _i, _d, _i, _f32p, _f32p, _f32p]
     L.orc_down_residual.argtypes = [_f32p, _f32p, _f32p, _f32p, _i, _i, _i]
     L.orc_ffn.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _i, _i, _i, _i]
     L.orc_layer_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Weights),
@@ -325,6 +328,32 @@ def swiglu(x, wg, wu, mode=EXACT):
     a = np.empty((M, I), np.float32)
     lib().orc_swiglu(_p(x), _p(_f(wg)), _p(_f(wu)), _p(a), M, H, I, mode)
     return a
+
+
+def swiglu_parts(x, wg, wu, mode=EXACT):
+    """(g, u, silu(g), a), each [M, I], as stored in the given mode."""
+    x = _f(x)
+    M, H = x.shape
+    I = wg.shape[0]
+    g, u, sg, a = (np.empty((M, I), np.float32) for _ in range(4))
+    lib().orc_swiglu_parts(_p(x), _p(_f(wg)), _p(_f(wu)), _p(g), _p(u), _p(sg), _p(a), M, H,
+                           I, mode)
+    return g, u, sg, a
+
+
+def attn_row(q, k, v, scale=None, mode=EXACT):
+    """One query row q [D] over keys k [n, D] and values v [n, D]:
+    (scores [n], probabilities [n], output [D]) as stored in the given mode."""
+    q, k, v = _f(q), _f(k), _f(v)
+    D = q.shape[-1]
+    n = k.shape[0]
+    assert k.shape == (n, D) and v.shape == (n, D) and q.size == D
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    s = np.empty(n, np.float32)
+    p = np.empty(n, np.float32)
+    o = np.empty(D, np.float32)
+    lib().orc_attn_row(_p(q), _p(k), _p(v), n, D, scale, mode, _p(s), _p(p), _p(o))
+    return s, p, o
 
 
 def down_residual(a, wd, resid=None):

@@ -251,10 +251,11 @@ void orc_reshape_and_cache(const float* k, const float* v,
  * the element used is the dequantised code x scale (an exact product in
  * fp64).  scratch holds n doubles.
  */
-static void attend(const float* q, const float* const* keys,
-                   const float* const* vals, const double* kmul,
-                   const double* vmul, int n, int D, double scale, float* out,
-                   int mode, double* s) {
+static void attend_keep(const float* q, const float* const* keys,
+                        const float* const* vals, const double* kmul,
+                        const double* vmul, int n, int D, double scale,
+                        float* out, int mode, double* s, float* s_keep,
+                        float* p_keep) {
   double mx = -INFINITY;
   for (int j = 0; j < n; ++j) {
     const double km = kmul ? kmul[j] : 1.0;
@@ -262,6 +263,7 @@ static void attend(const float* q, const float* const* keys,
     for (int d = 0; d < D; ++d) acc += (double)q[d] * ((double)keys[j][d] * km);
     s[j] = acc * scale;
     if (mode == ORC_BF16_UNFUSED) s[j] = (double)(float)s[j];
+    if (s_keep) s_keep[j] = (float)s[j];
     if (s[j] > mx) mx = s[j];
   }
   double l = 0.0;
@@ -272,6 +274,7 @@ static void attend(const float* q, const float* const* keys,
   for (int j = 0; j < n; ++j) {
     s[j] /= l;
     if (mode == ORC_BF16_UNFUSED) s[j] = (double)orc_bf16_round((float)s[j]);
+    if (p_keep) p_keep[j] = (float)s[j];
   }
   for (int d = 0; d < D; ++d) {
     double acc = 0.0;
@@ -279,6 +282,36 @@ static void attend(const float* q, const float* const* keys,
       acc += s[j] * ((double)vals[j][d] * (vmul ? vmul[j] : 1.0));
     out[d] = store(acc, mode != ORC_EXACT);
   }
+}
+
+static void attend(const float* q, const float* const* keys,
+                   const float* const* vals, const double* kmul,
+                   const double* vmul, int n, int D, double scale, float* out,
+                   int mode, double* s) {
+  attend_keep(q, keys, vals, kmul, vmul, n, D, scale, out, mode, s, NULL, NULL);
+}
+
+/*
+ * One query row over n contiguous keys k [n][D] and values v [n][D]: the
+ * same computation as every attention function here, with its scores and
+ * probabilities also returned as the kernel-per-op chain stores them
+ * (s_out: fp32 scores after the scale; p_out: probabilities, bf16 in
+ * ORC_BF16_UNFUSED).  o [D] is the row's output.             [chain]
+ */
+void orc_attn_row(const float* q, const float* k, const float* v, int n, int D,
+                  double scale, int mode, float* s_out, float* p_out,
+                  float* o) {
+  const float** keys = (const float**)malloc(sizeof(float*) * (size_t)(n > 0 ? n : 1));
+  const float** vals = (const float**)malloc(sizeof(float*) * (size_t)(n > 0 ? n : 1));
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  for (int j = 0; j < n; ++j) {
+    keys[j] = k + (int64_t)j * D;
+    vals[j] = v + (int64_t)j * D;
+  }
+  attend_keep(q, keys, vals, NULL, NULL, n, D, scale, o, mode, sc, s_out, p_out);
+  free(keys);
+  free(vals);
+  free(sc);
 }
 
 /*
@@ -419,22 +452,34 @@ void orc_attn_decode_contig(const float* q, const float* k_cache,
 /* SwiGLU feed-forward                                    [chain], [ffn]    */
 /* ------------------------------------------------------------------------ */
 
-/* a = silu(x Wg^T) * (x Wu^T), silu(z) = z / (1 + e^-z).  a [M][I]. */
-void orc_swiglu(const float* x, const float* wg, const float* wu, float* a,
-                int M, int H, int I, int mode) {
+/*
+ * a = silu(x Wg^T) * (x Wu^T), silu(z) = z / (1 + e^-z).  a [M][I].
+ * g_out, u_out, sg_out (each [M][I], NULL to skip) receive the gate and up
+ * projections and silu(gate) as they are stored (bf16 in ORC_BF16_UNFUSED,
+ * the kernel-per-op chain's storage points).
+ */
+void orc_swiglu_parts(const float* x, const float* wg, const float* wu,
+                      float* g_out, float* u_out, float* sg_out, float* a,
+                      int M, int H, int I, int mode) {
   const int unf = (mode == ORC_BF16_UNFUSED);
-  float* g = (float*)malloc(sizeof(float) * (size_t)M * (size_t)I);
-  float* u = (float*)malloc(sizeof(float) * (size_t)M * (size_t)I);
+  float* g = g_out ? g_out : (float*)malloc(sizeof(float) * (size_t)M * (size_t)I);
+  float* u = u_out ? u_out : (float*)malloc(sizeof(float) * (size_t)M * (size_t)I);
   orc_linear(x, wg, g, M, I, H, unf);
   orc_linear(x, wu, u, M, I, H, unf);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < (int64_t)M * I; ++i) {
     double z = g[i];
     float sl = store(z / (1.0 + exp(-z)), unf);
+    if (sg_out) sg_out[i] = sl;
     a[i] = store((double)sl * (double)u[i], mode != ORC_EXACT);
   }
-  free(g);
-  free(u);
+  if (!g_out) free(g);
+  if (!u_out) free(u);
+}
+
+void orc_swiglu(const float* x, const float* wg, const float* wu, float* a,
+                int M, int H, int I, int mode) {
+  orc_swiglu_parts(x, wg, wu, NULL, NULL, NULL, a, M, H, I, mode);
 }
 
 /* y = resid + a Wd^T (the product is stored in fp32, then one fp32 add). */

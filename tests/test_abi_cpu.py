@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from transformer_decoder_layer_residual_amd import binding as dl
 
@@ -38,7 +39,7 @@ def test_every_declared_symbol_is_exported(L):
 def test_status_strings_and_version(L):
     assert L.dl_status_string(0) == b"DL_OK"
     assert L.dl_status_string(4) == b"DL_ERR_WORKSPACE"
-    assert L.dl_abi_version() == 2
+    assert L.dl_abi_version() == 3 == dl.ABI_VERSION
 
 
 def test_null_and_unsupported_arguments_fail_on_host(L):
@@ -122,3 +123,45 @@ def test_product_code_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "liborc" not in text, f
                 assert "orc_" not in text, f
+
+
+def test_workspace_regions_match_the_layer_workspace(L):
+    """The region table describes the workspace the layer calls carve: every
+    region lies inside dl_layer_workspace_size, regions do not overlap, the
+    activations have their [T][...] sizes, and the score / probability
+    regions exist only in the kernel-per-op mode."""
+    T, B, S = 2048, 1, 2048
+    H, Hq, Hkv, D, I = 4096, 32, 32, 128, 11008
+    dims = dl.make_dims(H, Hq, Hkv, D, I, 128, 1e-5, torch.bfloat16)
+    for mode in (dl.DL_FUSED, dl.DL_UNFUSED):
+        r = dl.dl_layer_workspace_regions(dims, T, B, S, False, mode)
+        total = L.dl_layer_workspace_size(ctypes.byref(dims), T, B, S, 0, mode)
+        spans = sorted((o, o + n) for o, n in r.values() if n)
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[-1][1] <= total
+        assert all(o % 256 == 0 for o, _ in r.values())
+        assert r["n1"][1] == T * H * 2 and r["q"][1] == T * Hq * D * 2
+        assert r["k"][1] == T * Hkv * D * 2 and r["h"][1] == T * H * 4
+        assert r["a"][1] == T * I * 2
+        if mode == dl.DL_UNFUSED:
+            assert r["scores"][1] == B * Hq * S * S * 4
+            assert r["probs"][1] == B * Hq * S * S * 2
+            assert r["gate"][1] == r["up"][1] == r["silu"][1] == T * I * 2
+            assert r["down"][1] == T * H * 4
+        else:
+            assert r["scores"][1] == r["probs"][1] == r["gate"][1] == r["down"][1] == 0
+    with pytest.raises(dl.DLError, match="T == B"):
+        dl.dl_layer_workspace_regions(dims, 8, 4, 64, True, dl.DL_FUSED)
+    with pytest.raises(dl.DLError, match="max_seqlen"):
+        dl.dl_layer_workspace_regions(dims, 8, 1, 9, False, dl.DL_FUSED)
+
+
+def test_check_indices_host_errors(L):
+    s = L.dl_check_indices(None, 1, 1, 1, 16, None, None, 0, None, 0, None, 0, None, None)
+    assert s == 1 and b"error_word" in L.dl_last_error()
+    s = L.dl_check_indices(None, 1, 1, 1, 16, None, None, 0, None, 0, None, 0, 6, None)
+    assert s == 3
+    s = L.dl_check_indices(64, 1, 2, 4, 24, None, None, 0, None, 0, None, 0, 8, None)
+    assert s == 2 and b"block_size" in L.dl_last_error()
+    s = L.dl_check_indices(None, 2, 0, 0, 0, None, None, 0, 64, 0, None, 0, 8, None)
+    assert s == 1 and b"max_context_len" in L.dl_last_error()

@@ -27,7 +27,7 @@ from transformer_decoder_layer_residual_amd import binding as dl
 from transformer_decoder_layer_residual_amd import inputs as gen
 from transformer_decoder_layer_residual_amd.harness import DeviceLayer, cache_dev, i32, to_dev
 
-from _util import assert_bf16_close, assert_f32_close, host, host_bits, rel_l2
+from _util import assert_bf16_close, assert_f32_close, bf16_ulp, host, host_bits, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -146,19 +146,110 @@ def run_full_prefill(cfg, decode_capacity=0):
     return layer, pb, bt, (kc1, vc1), btd, xd, y
 
 
+def assert_probs_close(gpu, ref, what):
+    """Softmax probabilities stored in bf16 by both sides: each within one
+    bf16 ulp of the oracle's (the scores they come from differ only by fp32
+    summation order, so at most one rounding boundary flips)."""
+    gpu = np.asarray(gpu, np.float32)
+    ref = np.asarray(ref, np.float32)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite probabilities"
+    bound = np.maximum(bf16_ulp(ref), np.float32(1e-30))
+    bad = np.abs(gpu - ref) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} probabilities beyond one bf16 ulp"
+    assert rel_l2(gpu, ref) <= 1e-2, what
+
+
+def check_unfused_chain(layer, pb, bt, btd, xd, x_host, y_fused, rows, what):
+    """The kernel-per-op chain at full size, every stored intermediate read
+    back from the layer workspace (dl_layer_workspace_regions) and compared
+    element by element on the sampled rows with the oracle's BF16_UNFUSED
+    steps, each fed the GPU's own inputs to that step: n1; q, k (rounded
+    before and after RoPE) and v; the fp32 score rows and the bf16
+    probability rows of every head (masked keys -inf / 0); the attention
+    output; o; h; n2; gate, up, silu(gate) and a; the fp32 down projection;
+    y.  The cache it writes is the oracle's reshape-and-cache of its own k/v
+    bit for bit."""
+    c, w = layer.cfg, layer.w_host
+    T, B, S = pb.T, pb.B, pb.max_seqlen
+    H, Hq, Hkv, D, I = c.hidden, c.n_q_heads, c.n_kv_heads, c.head_dim, c.intermediate
+    dt = torch.bfloat16
+    n = dl.dl_layer_workspace_size(layer.dims, T, B, S, 0, dl.DL_UNFUSED)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    kb, vb = gen.empty_cache(c, bt.num_blocks)
+    kc, vc = cache_dev(kb), cache_dev(vb)
+    yu = layer.prefill(xd, pb, kc, vc, btd, mode=dl.DL_UNFUSED, ws=ws)
+    torch.cuda.synchronize()
+    reg = dl.dl_layer_workspace_regions(layer.dims, T, B, S, False, dl.DL_UNFUSED)
+
+    def region(name, dtype, shape):
+        off, size = reg[name]
+        assert size == int(np.prod(shape)) * torch.empty(0, dtype=dtype).element_size(), name
+        return ws[off:off + size].view(dtype).view(*shape)
+
+    n1 = host(region("n1", dt, (T, H)))[rows]
+    assert_bf16_close(n1, oracle.rmsnorm(x_host[rows], w["ln1"], c.rms_eps, mode=oracle.BF16),
+                      f"{what} unfused n1")
+    q_all = host(region("q", dt, (T, Hq, D)))
+    k_all = host(region("k", dt, (T, Hkv, D)))
+    v_all = host(region("v", dt, (T, Hkv, D)))
+    rq, rk, rv = oracle.qkv_rope(n1, w["wq"], w["wk"], w["wv"], pb.positions[rows], c.rope_theta,
+                                 Hq, Hkv, D, mode=oracle.BF16_UNFUSED)
+    assert_bf16_close(q_all[rows], rq, f"{what} unfused q")
+    assert_bf16_close(k_all[rows], rk, f"{what} unfused k")
+    assert_bf16_close(v_all[rows], rv, f"{what} unfused v")
+    check_cache_write((kc, vc), (kb, vb), k_all, v_all, pb.seq_of_token, pb.positions, bt.table,
+                      f"{what} unfused cache")
+    scores = region("scores", torch.float32, (B, Hq, S, S))
+    probs = region("probs", dt, (B, Hq, S, S))
+    attn = host(region("attn", dt, (T, Hq * D)))[rows].reshape(-1, Hq, D)
+    G = Hq // Hkv
+    for r_i, t in enumerate(rows):
+        b = int(pb.seq_of_token[t])
+        t0 = int(pb.cu_seqlens[b])
+        Sb = int(pb.cu_seqlens[b + 1]) - t0
+        i = int(t) - t0
+        s_row = host(scores[b, :, i, :Sb])
+        p_row = host(probs[b, :, i, :Sb])
+        assert np.all(np.isneginf(s_row[:, i + 1:])), f"{what} row {t}: unmasked scores"
+        assert np.all(p_row[:, i + 1:] == 0), f"{what} row {t}: probabilities past the diagonal"
+        o_ref = np.empty((Hq, D), np.float32)
+        for h in range(Hq):
+            g = h // G
+            s_ref, p_ref, o_ref[h] = oracle.attn_row(q_all[t, h], k_all[t0:t0 + i + 1, g],
+                                                     v_all[t0:t0 + i + 1, g],
+                                                     mode=oracle.BF16_UNFUSED)
+            assert_f32_close(s_row[h, :i + 1], s_ref, f"{what} row {t} head {h} scores",
+                             max_abs=1e-3, rel=1e-5)
+            assert_probs_close(p_row[h, :i + 1], p_ref, f"{what} row {t} head {h} probs")
+        assert_bf16_close(attn[r_i], o_ref, f"{what} row {t} unfused attn")
+    attn = attn.reshape(len(rows), Hq * D)
+    o = host(region("o", dt, (T, H)))[rows]
+    assert_bf16_close(o, oracle.linear(attn, w["wo"], round_bf16=True), f"{what} unfused o")
+    h = host(region("h", torch.float32, (T, H)))[rows]
+    n2_ref, h_ref = oracle.rmsnorm(o, w["ln2"], c.rms_eps, resid=x_host[rows], mode=oracle.BF16)
+    assert np.array_equal(h, h_ref), f"{what} unfused h: the fp32 residual add is exact"
+    n2 = host(region("n2", dt, (T, H)))[rows]
+    assert_bf16_close(n2, n2_ref, f"{what} unfused n2")
+    g_ref, u_ref, sg_ref, a_ref = oracle.swiglu_parts(n2, w["wg"], w["wu"],
+                                                      mode=oracle.BF16_UNFUSED)
+    for name, ref in (("gate", g_ref), ("up", u_ref), ("silu", sg_ref), ("a", a_ref)):
+        assert_bf16_close(host(region(name, dt, (T, I)))[rows], ref, f"{what} unfused {name}")
+    a = host(region("a", dt, (T, I)))[rows]
+    dd = host(region("down", torch.float32, (T, H)))[rows]
+    assert_f32_close(dd, oracle.down_residual(a, w["wd"]), f"{what} unfused down")
+    yr = host(yu)[rows]
+    assert np.array_equal(yr, (h + dd).astype(np.float32)), f"{what} unfused y = h + down"
+    assert_f32_close(yr, oracle.down_residual(a, w["wd"], h), f"{what} unfused y")
+    # the two modes round at different places; reported, not gated
+    r = rel_l2(host(yu), host(y_fused))
+    say(f"{what}: fused vs unfused rel-L2 {r:.2e}, max-abs {float((yu - y_fused).abs().max()):.3e}")
+
+
 def test_llama2_7b_prefill_full_size():
     cfg = gen.CONFIGS[2]
     layer, pb, bt, caches, btd, xd, y = run_full_prefill(cfg)
-    # The unfused kernel-per-op chain stores more intermediates in bf16 (pre-RoPE
-    # q/k, gate, up, silu(gate), P), so at this size it drifts from the fused
-    # path by more than one output half-ulp in places (|y| reaches ~14, where a
-    # bf16 half-ulp is 0.03); the two agree in relative L2.
-    kb, vb = gen.empty_cache(cfg, bt.num_blocks)
-    yu = layer.prefill(xd, pb, cache_dev(kb), cache_dev(vb), btd, mode=dl.DL_UNFUSED)
-    torch.cuda.synchronize()
-    r = rel_l2(host(yu), host(y))
-    say(f"fused vs unfused: rel-L2 {r:.2e}, max-abs {float((yu - y).abs().max()):.3e}")
-    assert np.isfinite(host(yu)).all() and r <= 1e-2
+    rows = sample_rows(pb.T, 10, 21, must=[0, 1, 127, 128, pb.T - 1])
+    check_unfused_chain(layer, pb, bt, btd, xd, gen.hidden(cfg, pb.T), y, rows, cfg.name)
 
 
 def decode_step_checked(layer, x_host, ctx, caches, bt, btd, what, rows=None):
@@ -193,7 +284,10 @@ def decode_step_checked(layer, x_host, ctx, caches, bt, btd, what, rows=None):
 
 def test_llama3_8b_gqa_prefill_then_128_decode_steps():
     cfg = gen.CONFIGS[4]
-    layer, pb, bt, caches, btd, _, _ = run_full_prefill(cfg, decode_capacity=cfg.decode_steps)
+    layer, pb, bt, caches, btd, xd, y = run_full_prefill(cfg, decode_capacity=cfg.decode_steps)
+    starts = pb.cu_seqlens[:-1]
+    rows = sample_rows(pb.T, 6, 41, must=[0, pb.T - 1, *starts[1:3], *(starts[1:3] - 1)])
+    check_unfused_chain(layer, pb, bt, btd, xd, gen.hidden(cfg, pb.T), y, rows, cfg.name)
     checked = {0, cfg.decode_steps // 2, cfg.decode_steps - 1}
     for step in range(cfg.decode_steps):
         ctx = (pb.lens + step + 1).astype(np.int32)

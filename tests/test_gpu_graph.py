@@ -1,17 +1,23 @@
 """The decode step recorded as a HIP graph: every replay, with its inputs
 rewritten in place and eager work and synchronisations in between, gives
 the same output and cache bits as the eager dl_layer_decode call with the
-same arguments."""
+same arguments, and matches the oracle's decode step: the output within the
+layer tolerance, the cache slots the replay wrote within the storage
+tolerance (float caches; every other slot keeps its bits) or bit for bit as
+the oracle's quantising write of the k/v the replay produced (INT8)."""
 import dataclasses
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from transformer_decoder_layer_residual_amd import binding as dl
 from transformer_decoder_layer_residual_amd import inputs as gen
 from transformer_decoder_layer_residual_amd.harness import (DeviceLayer, cache_dev, i32,
                                                             prefill_inputs, to_dev)
+
+from _util import assert_bf16_close, assert_f32_close, host, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -50,12 +56,34 @@ def test_decode_graph_replays_equal_eager(cfg_name, int8):
     ctx = torch.zeros(B, dtype=torch.int32, device="cuda:0")
     side = torch.cuda.Stream()
     scales = {"k_scale": a[2], "v_scale": a[3]} if int8 else {}
+    n = dl.dl_layer_workspace_size(layer.dims, B, B, 0, max_ctx, dl.DL_FUSED)
+    gws = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     graph = dl.DecodeGraph(layer.dims, layer.w, layer.cs, xin, yout, pos, ctx, max_ctx, a[0], a[1],
-                           btd, side, **scales)
+                           btd, side, ws=gws, **scales)
+    # the oracle's own chain, from the same prefill input
+    d = cfg.dims()
+    omode = oracle.EXACT if cfg.dtype == "f32" else oracle.BF16
+    oc = [c.copy() for c in host_cache]
+    if int8:
+        oracle.layer_prefill_q8(d, layer.w_host, host(x0), pb.positions, pb.seq_of_token,
+                                pb.cu_seqlens, *oc, bt.table, mode=omode)
+        mirror = [t.cpu().numpy() for t in a]       # GPU cache after its prefill
+    else:
+        oc = [gen.cache_to_f32(c).copy() for c in oc]
+        oracle.layer_prefill(d, layer.w_host, host(x0), pb.positions, pb.seq_of_token,
+                             pb.cu_seqlens, oc[0], oc[1], bt.table, mode=omode)
+    if cfg.dtype == "f32":
+        y_close = lambda g, r, w: assert_f32_close(g, r, w, max_abs=1e-3, rel=1e-5)
+        c_close = lambda g, r, w: assert_f32_close(g, r, w, max_abs=1e-3, rel=1e-5)
+    else:
+        y_close = lambda g, r, w: assert_f32_close(g, r, w)
+        c_close = assert_bf16_close
     try:
         for s in range(steps):
             c = (pb.lens + s + 1).astype(np.int32)
-            xs = to_dev(gen.hidden(cfg, B, step=50 + s), torch.float32)
+            xh = gen.hidden(cfg, B, step=50 + s)
+            xs = to_dev(xh, torch.float32)
+            before = [t.clone() for t in a]
             xin.copy_(xs)
             pos.copy_(i32(c - 1))
             ctx.copy_(i32(c))
@@ -77,6 +105,38 @@ def test_decode_graph_replays_equal_eager(cfg_name, int8):
                     assert torch.equal(ta.view(torch.int16), tb.view(torch.int16)), f"replay {s}"
                 else:
                     assert torch.equal(ta, tb), f"replay {s}: cache differs"
+            # against the oracle's decode step
+            if int8:
+                y_orc, _ = oracle.layer_decode_q8(d, layer.w_host, xh, c, *oc, bt.table,
+                                                  mode=omode)
+                reg = dl.dl_layer_workspace_regions(layer.dims, B, B, max_ctx, True, dl.DL_FUSED)
+                kv = []
+                for name in ("k", "v"):
+                    off, size = reg[name]
+                    ldt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+                    kv.append(host(gws[off:off + size].view(ldt)
+                                   .view(B, cfg.n_kv_heads, cfg.head_dim)))
+                oracle.reshape_and_cache_q8(kv[0], kv[1], np.arange(B, dtype=np.int32), c - 1,
+                                            bt.table, *mirror)
+                got = [t.cpu().numpy() for t in a]
+                for g_, w_, name in zip(got, mirror, ("k codes", "v codes", "k scales",
+                                                      "v scales")):
+                    same = (g_.view(np.uint32) == w_.view(np.uint32)) if g_.dtype == np.float32 \
+                        else (g_ == w_)
+                    assert same.all(), f"replay {s}: {int((~same).sum())} {name} differ"
+            else:
+                y_orc, _ = oracle.layer_decode(d, layer.w_host, xh, c, oc[0], oc[1], bt.table,
+                                               mode=omode)
+                blk = bt.table[np.arange(B), (c - 1) // cfg.block_size]
+                slot = (c - 1) % cfg.block_size
+                for cache_now, cache_before, ocache, name in zip(a[:2], before[:2], oc, "kv"):
+                    c_close(host(cache_now)[blk, :, slot], ocache[blk, :, slot],
+                            f"replay {s} {name} new slots")
+                    gb, g0b = host_bits(cache_now), host_bits(cache_before)
+                    gb[blk, :, slot] = g0b[blk, :, slot]
+                    assert np.array_equal(gb, g0b), \
+                        f"replay {s}: {name} cache changed outside the new slots"
+            y_close(host(y_graph), y_orc, f"replay {s} vs oracle")
     finally:
         graph.close()
 

@@ -570,6 +570,80 @@ def test_swiglu_special_values():
     assert np.all(oracle.swiglu(x, wg, np.zeros_like(wu)) == 0)
 
 
+def test_swiglu_parts_exact_projections_and_silu_identities():
+    """The stored parts of the kernel-per-op FFN: gate and up are exact on
+    small integers (any summation order), silu satisfies silu(-z) = silu(z) - z
+    and silu(ln 3) = 0.75 ln 3 (sigmoid(ln 3) = 3/4), and a is the product of
+    the parts, rounded where the mode stores it."""
+    M, H, I = 5, 24, 40
+    x = R.integers(-3, 4, (M, H)).astype(np.float32)
+    wg = R.integers(-3, 4, (I, H)).astype(np.float32)
+    wu = R.integers(-3, 4, (I, H)).astype(np.float32)
+    for mode in (oracle.EXACT, oracle.BF16, oracle.BF16_UNFUSED):
+        g, u, sg, a = oracle.swiglu_parts(x, wg, wu, mode=mode)
+        want_g = (x.astype(np.int64) @ wg.T.astype(np.int64)).astype(np.float32)
+        want_u = (x.astype(np.int64) @ wu.T.astype(np.int64)).astype(np.float32)
+        # |g| <= 216: every value is bf16-representable up to 256 only when even;
+        # the exact integers survive fp32 and are rounded to bf16 in the unfused mode
+        if mode == oracle.BF16_UNFUSED:
+            want_g, want_u = bf(want_g), bf(want_u)
+        assert np.array_equal(g, want_g) and np.array_equal(u, want_u)
+        assert np.array_equal(a, oracle.swiglu(x, wg, wu, mode=mode))
+        prod = sg.astype(np.float64) * u.astype(np.float64)
+        want_a = prod.astype(np.float32)
+        if mode != oracle.EXACT:
+            want_a = bf(want_a)
+        assert np.array_equal(a, want_a)
+    # silu identities through a one-hot input selecting gate weights z
+    z = np.array([np.log(3.0), -np.log(3.0), 0.0, 2.5, -2.5, 7.0, -7.0], np.float64)
+    xh = np.zeros((1, 8), np.float32)
+    xh[0, 0] = 1.0
+    wz = np.zeros((z.size, 8), np.float32)
+    wz[:, 0] = z.astype(np.float32)
+    _, _, sgz, _ = oracle.swiglu_parts(xh, wz, np.ones_like(wz), mode=oracle.EXACT)
+    zf = wz[:, 0].astype(np.float64)
+    s = sgz[0].astype(np.float64)
+    assert s[0] == pytest.approx(0.75 * zf[0], rel=1e-6)
+    for i in (0, 3, 5):
+        assert s[i + 1] == pytest.approx(s[i] - zf[i], rel=1e-6, abs=1e-6)
+    assert s[2] == 0.0
+
+
+def test_attn_row_scores_probs_exact_cases():
+    """Scores of small-integer rows at scale 1 are exact integers; the
+    probabilities are in the ratio exp(s_j - s_k), sum to one, and round to
+    bf16 in the unfused mode; the output equals the contiguous attention
+    of the same row."""
+    D, n = 16, 9
+    q = R.integers(-2, 3, D).astype(np.float32)
+    k = R.integers(-2, 3, (n, D)).astype(np.float32)
+    v = R.standard_normal((n, D)).astype(np.float32)
+    s, p, o = oracle.attn_row(q, k, v, scale=1.0, mode=oracle.EXACT)
+    assert np.array_equal(s, (k.astype(np.int64) @ q.astype(np.int64)).astype(np.float32))
+    e = np.exp(s.astype(np.float64) - s.max())
+    np.testing.assert_allclose(p, e / e.sum(), rtol=1e-6)
+    assert abs(float(p.astype(np.float64).sum()) - 1.0) < 1e-6
+    # the scale multiplies the scores (two keys: p0 = logistic(s0 - s1))
+    s2, p2, _ = oracle.attn_row(q, k[:2], v[:2], scale=0.25, mode=oracle.EXACT)
+    np.testing.assert_allclose(s2, 0.25 * s[:2], rtol=1e-7)
+    assert p2[0] == pytest.approx(1.0 / (1.0 + np.exp(-(s2[0] - s2[1]))), rel=1e-6)
+    # unfused storage: fp32 scores, bf16 probabilities
+    qf = R.standard_normal(D).astype(np.float32)
+    kf = R.standard_normal((n, D)).astype(np.float32)
+    su, pu, _ = oracle.attn_row(qf, kf, v, mode=oracle.BF16_UNFUSED)
+    assert np.array_equal(pu, bf(pu))
+    assert abs(float(pu.astype(np.float64).sum()) - 1.0) < n * 2.0 ** -8
+    se, pe, _ = oracle.attn_row(qf, kf, v, mode=oracle.EXACT)
+    np.testing.assert_allclose(su, se, rtol=1e-6, atol=1e-6)
+    assert np.all(np.abs(pu - pe) <= 2.0 ** -8 * np.maximum(pe, 2.0 ** -126) + 1e-12)
+    # the output is the attention of the row over a contiguous cache
+    for mode in (oracle.EXACT, oracle.BF16, oracle.BF16_UNFUSED):
+        _, _, om = oracle.attn_row(qf, kf, v, mode=mode)
+        ref = oracle.attn_decode_contig(qf[None, None], kf[None, None], v[None, None],
+                                        np.array([n], np.int32), mode=mode)[0, 0]
+        assert np.array_equal(om, ref)
+
+
 def test_ffn_composition_and_residual():
     M, H, I = 3, 32, 48
     x = R.standard_normal((M, H)).astype(np.float32)

@@ -22,7 +22,7 @@ DL_OK = 0
 DL_F32, DL_BF16 = 0, 1
 DL_FUSED, DL_UNFUSED = 0, 1
 DL_KV_LAYER, DL_KV_INT8 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -110,6 +110,11 @@ _SIGS = [
       ctypes.POINTER(_vp)]),
     ("dl_graph_launch", ctypes.c_int, [_vp, _vp]),
     ("dl_graph_destroy", ctypes.c_int, [_vp]),
+    ("dl_check_indices", ctypes.c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_int,
+                                        _vp, _c_int, _vp, _c_int, _vp, _vp]),
+    ("dl_layer_workspace_regions", ctypes.c_int, [ctypes.POINTER(LayerDims), _c_int, _c_int,
+                                                  _c_int, _c_int, ctypes.c_int,
+                                                  ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     ("dl_layer_decode_qlens_workspace_size", _sz, [ctypes.POINTER(LayerDims), _c_int, _c_int,
                                                    _c_int, _c_int]),
     ("dl_layer_decode_qlens", ctypes.c_int, [ctypes.POINTER(LayerDims),
@@ -198,6 +203,40 @@ def _cache(k_cache, v_cache, k_scale=None, v_scale=None) -> KVCache:
 # step entry points
 # ---------------------------------------------------------------------------
 
+DL_CHECK_BIT_SEQ, DL_CHECK_BIT_POSITION, DL_CHECK_BIT_BLOCK = 1, 2, 4
+DL_CHECK_BIT_CONTEXT, DL_CHECK_BIT_CU = 8, 16
+WS_REGIONS = ("n1", "q", "k", "v", "attn", "o", "h", "n2", "a", "partial", "decode", "scores",
+              "probs", "gate", "up", "silu", "down")
+
+
+def dl_check_indices(error_word, block_table=None, num_blocks=0, block_size=0, positions=None,
+                     seq_of_token=None, context_lens=None, max_context_len=0, cu_seqlens=None,
+                     max_seqlen=0, B=None, T=None):
+    """Enqueue the index validation; error_word is a 1-element int32 device
+    tensor that receives the OR of the violated DL_CHECK_BIT_* bits."""
+    if B is None:
+        B = (block_table.shape[0] if block_table is not None else
+             context_lens.shape[0] if context_lens is not None else
+             cu_seqlens.shape[0] - 1 if cu_seqlens is not None else 0)
+    if T is None:
+        T = (positions.shape[0] if positions is not None else
+             seq_of_token.shape[0] if seq_of_token is not None else 0)
+    mb = block_table.shape[1] if block_table is not None else 0
+    _check(lib().dl_check_indices(_p(block_table), B, mb, num_blocks, block_size, _p(positions),
+                                  _p(seq_of_token), T, _p(context_lens), max_context_len,
+                                  _p(cu_seqlens), max_seqlen, _p(error_word), _stream()))
+
+
+def dl_layer_workspace_regions(dims, T: int, B: int, max_seqlen_or_context: int, is_decode: bool,
+                               mode=DL_FUSED):
+    """{region name: (byte offset, byte size)} of the layer workspace."""
+    off = (_sz * len(WS_REGIONS))()
+    size = (_sz * len(WS_REGIONS))()
+    _check(lib().dl_layer_workspace_regions(ctypes.byref(dims), T, B, max_seqlen_or_context,
+                                            int(bool(is_decode)), mode, off, size))
+    return {n: (int(off[i]), int(size[i])) for i, n in enumerate(WS_REGIONS)}
+
+
 def dl_rope_table_fill(cos_sin, max_pos: int, head_dim: int, theta: float):
     _check(lib().dl_rope_table_fill(_p(cos_sin), max_pos, head_dim, theta, _stream()))
 
@@ -251,7 +290,7 @@ def dl_attn_prefill(q, k, v, cu_seqlens, max_seqlen: int, out, scale=None):
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     B = cu_seqlens.shape[0] - 1
-    scale = D ** -0.5 if scale is None else scale
+    scale = 0.0 if scale is None else scale       # <= 0: the library's 1/sqrt(D)
     _check(lib().dl_attn_prefill(_p(q), _p(k), _p(v), _p(cu_seqlens), B, T, max_seqlen, Hq, Hkv,
                                  D, scale, _p(out), dtype_code(q.dtype), _stream()))
 
@@ -260,7 +299,7 @@ def dl_attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_con
                          out, scale=None, ws=None, k_scale=None, v_scale=None):
     B, Hq, D = q.shape
     Hkv, BS = k_cache.shape[1], k_cache.shape[2]
-    scale = D ** -0.5 if scale is None else scale
+    scale = 0.0 if scale is None else scale       # <= 0: the library's 1/sqrt(D)
     L = lib()
     ws, nb = _ws(L.dl_attn_decode_workspace_size(B, Hq, Hkv, D, max_context_len, BS), ws,
                  q.device)
@@ -277,7 +316,7 @@ def dl_attn_paged_qlens(q, k_cache, v_cache, block_table, cu_q_lens, context_len
     Tq, Hq, D = q.shape
     Hkv, BS = k_cache.shape[1], k_cache.shape[2]
     B = cu_q_lens.shape[0] - 1
-    scale = D ** -0.5 if scale is None else scale
+    scale = 0.0 if scale is None else scale       # <= 0: the library's 1/sqrt(D)
     L = lib()
     ws, nb = _ws(L.dl_attn_paged_qlens_workspace_size(B, Tq, Hq, Hkv, D, max_q_len,
                                                       max_context_len, BS), ws, q.device)

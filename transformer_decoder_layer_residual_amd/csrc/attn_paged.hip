@@ -59,14 +59,15 @@ __device__ __forceinline__ void load_split_frag(Frag<float>& f, const float* p0,
 }
 
 // Per-sequence geometry shared by both kernels; every count is clamped to
-// what the host sized the grid and the workspace for.  cu_q == nullptr: one
-// new token per sequence (the decode step).
+// what the host sized the grid and the workspace for: the sequence's query
+// rows to [0, Tq), its context to the table and to max_ctx.  cu_q ==
+// nullptr: one new token per sequence (the decode step).
 struct PgSeq {
   int q0, ql, ctx, first;  // first = position of new token 0
-  __device__ PgSeq(const int32_t* cu_q, const int32_t* ctx_lens, int b, int max_blocks, int BS,
-                   int max_ctx) {
-    q0 = cu_q ? cu_q[b] : b;
-    ql = cu_q ? max(cu_q[b + 1] - q0, 0) : 1;
+  __device__ PgSeq(const int32_t* cu_q, const int32_t* ctx_lens, int b, int Tq, int max_blocks,
+                   int BS, int max_ctx) {
+    q0 = cu_q ? min(max(cu_q[b], 0), Tq) : b;
+    ql = cu_q ? max(min(cu_q[b + 1], Tq) - q0, 0) : 1;
     ctx = min(min(ctx_lens[b], max_blocks * BS), max_ctx);
     first = ctx - ql;
   }
@@ -135,7 +136,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256, 2)
 attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
                   const int32_t* __restrict__ bt, int max_blocks, const int32_t* __restrict__ cu_q,
-                  const int32_t* __restrict__ ctx_lens, int B, int Hq, int Hkv, int BS,
+                  const int32_t* __restrict__ ctx_lens, int B, int Tq, int Hq, int Hkv, int BS,
                   float scale_log2, int ck, int max_qt, int max_sp, int max_ctx,
                   float* __restrict__ ws, int num_blocks, T* __restrict__ out) {
   constexpr int NT = 256, BKV = kPgBKV, VE = 16 / sizeof(T);
@@ -154,7 +155,7 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
 
   // ---- item -> (sequence, query tile, split)
   auto counts = [&](int bb, int& nqt, int& nsp) {
-    const PgSeq s(cu_q, ctx_lens, bb, max_blocks, BS, max_ctx);
+    const PgSeq s(cu_q, ctx_lens, bb, Tq, max_blocks, BS, max_ctx);
     nqt = s.ql > 0 ? min((s.ql + QB - 1) / QB, max_qt) : 0;
     nsp = s.ctx > 0 ? min((s.ctx + ck - 1) / ck, max_sp) : 0;
   };
@@ -180,7 +181,7 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
     base += total;
   }
   if (b < 0) return;
-  const PgSeq sq(cu_q, ctx_lens, b, max_blocks, BS, max_ctx);
+  const PgSeq sq(cu_q, ctx_lens, b, Tq, max_blocks, BS, max_ctx);
   int nqt, nsp;
   counts(b, nqt, nsp);
   const int qt = local / nsp, sp = local % nsp;
@@ -406,7 +407,8 @@ __global__ void __launch_bounds__(256, 1)
 attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
                          const T* __restrict__ vc, const int32_t* __restrict__ bt, int max_blocks,
                          const int32_t* __restrict__ cu_q, const int32_t* __restrict__ ctx_lens,
-                         int B, int Hq, int Hkv, int BS, float scale_log2, int ck, int max_qt,
+                         int B, int Tq, int Hq, int Hkv, int BS, float scale_log2, int ck,
+                         int max_qt,
                          int max_sp, int max_ctx, float* __restrict__ ws, int num_blocks,
                          T* __restrict__ out) {
   constexpr int VE = 16 / sizeof(T);
@@ -426,7 +428,7 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 
   // ---- item -> (sequence, query tile, split), as in the wide kernel
   auto counts = [&](int bb, int& nqt, int& nsp) {
-    const PgSeq s(cu_q, ctx_lens, bb, max_blocks, BS, max_ctx);
+    const PgSeq s(cu_q, ctx_lens, bb, Tq, max_blocks, BS, max_ctx);
     nqt = s.ql > 0 ? min((s.ql + QB - 1) / QB, max_qt) : 0;
     nsp = s.ctx > 0 ? min((s.ctx + ck - 1) / ck, max_sp) : 0;
   };
@@ -452,7 +454,7 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
     base += total;
   }
   if (b < 0) return;
-  const PgSeq sq(cu_q, ctx_lens, b, max_blocks, BS, max_ctx);
+  const PgSeq sq(cu_q, ctx_lens, b, Tq, max_blocks, BS, max_ctx);
   int nqt, nsp;
   counts(b, nqt, nsp);
   const int qt = local / nsp, sp = local % nsp;
@@ -679,8 +681,8 @@ attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
 template <typename T, int D>
 __global__ void __launch_bounds__(kCombineThreads)
 attn_paged_combine(const float* __restrict__ ws, const int32_t* __restrict__ cu_q,
-                   const int32_t* __restrict__ ctx_lens, int B, int Hq, int BS, int max_blocks,
-                   int ck, int max_sp, int max_ctx, T* __restrict__ out) {
+                   const int32_t* __restrict__ ctx_lens, int B, int Tq, int Hq, int BS,
+                   int max_blocks, int ck, int max_sp, int max_ctx, T* __restrict__ out) {
   const int h = blockIdx.x, t = blockIdx.y;
   int lo = cu_q ? 0 : t, hi = B;  // largest b with cu_q[b] <= t
   while (cu_q && hi - lo > 1) {
@@ -688,7 +690,7 @@ attn_paged_combine(const float* __restrict__ ws, const int32_t* __restrict__ cu_
     if (cu_q[mid] <= t) lo = mid;
     else hi = mid;
   }
-  const PgSeq sq(cu_q, ctx_lens, lo, max_blocks, BS, max_ctx);
+  const PgSeq sq(cu_q, ctx_lens, lo, Tq, max_blocks, BS, max_ctx);
   const int ns = row_splits(sq.first + (t - sq.q0), ck, max_sp);
   if (ns == 1) return;  // written by the attention kernel
   combine_row<T, D>(ws + ((int64_t)t * Hq + h) * max_sp * (D + 2), ns,
@@ -705,16 +707,16 @@ static hipError_t launch_paged(const T* q, const T* kc, const T* vc, const int32
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
   if (pl.narrow)
     hipLaunchKernelGGL((attn_paged_narrow_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q,
-                       kc, vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
+                       kc, vc, bt, max_blocks, cu_q, ctx, B, Tq, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
                        pl.max_sp, max_ctx, ws, num_blocks, out);
   else
     hipLaunchKernelGGL((attn_paged_kernel<T, D>), dim3((unsigned)wgs), dim3(256), 0, st, q, kc,
-                       vc, bt, max_blocks, cu_q, ctx, B, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
+                       vc, bt, max_blocks, cu_q, ctx, B, Tq, Hq, Hkv, BS, sl2, pl.ck, pl.max_qt,
                        pl.max_sp, max_ctx, ws, num_blocks, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_paged_combine<T, D>), dim3(Hq, Tq), dim3(kCombineThreads), 0, st, ws, cu_q, ctx, B,
-                     Hq, BS, max_blocks, pl.ck, pl.max_sp, max_ctx, out);
+                     Tq, Hq, BS, max_blocks, pl.ck, pl.max_sp, max_ctx, out);
   return hipGetLastError();
 }
 
@@ -752,20 +754,20 @@ hipError_t attn_decode_narrow(const T* q, const T* k_cache, const T* v_cache,
   if (wgs > 0x7fffffffL) return hipErrorInvalidValue;
   if (D == 128) {
     hipLaunchKernelGGL((attn_paged_narrow_kernel<T, 128>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, Hq,
-                       Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
+                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, B,
+                       Hq, Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_paged_combine<T, 128>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w, nullptr,
-                       context_lens, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
+                       context_lens, B, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
   } else if (D == 64) {
     hipLaunchKernelGGL((attn_paged_narrow_kernel<T, 64>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, Hq,
-                       Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
+                       q, k_cache, v_cache, block_table, max_blocks, nullptr, context_lens, B, B,
+                       Hq, Hkv, BS, sl2, ck, 1, max_sp, max_context_len, w, num_blocks, out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_paged_combine<T, 64>), dim3(Hq, B), dim3(kCombineThreads), 0, st, w, nullptr,
-                       context_lens, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
+                       context_lens, B, B, Hq, BS, max_blocks, ck, max_sp, max_context_len, out);
   } else {
     return hipErrorInvalidValue;
   }

@@ -41,6 +41,10 @@ dl_status hip_fail(hipError_t e, const char* where) {
     if (e_ != hipSuccess) return hip_fail(e_, where); \
   } while (0)
 
+// The scaled dot-product's default scale, 1/sqrt(D) (ATB decoder-layer page,
+// "operator fusion graph of a decoder layer").
+float default_scale(int D) { return 1.0f / sqrtf((float)D); }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t esize(dl_dtype dt) { return dt == DL_BF16 ? 2 : 4; }
@@ -112,6 +116,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---- layer workspace layout -------------------------------------------------
 enum Buf { kN1, kQ, kK, kV, kAttn, kO, kH, kN2, kA, kPart, kDec, kS, kP, kG, kU, kSG, kDd, kNBuf };
+static_assert(kN1 == DL_WS_N1 && kQ == DL_WS_Q && kK == DL_WS_K && kV == DL_WS_V &&
+                  kAttn == DL_WS_ATTN && kO == DL_WS_O && kH == DL_WS_H && kN2 == DL_WS_N2 &&
+                  kA == DL_WS_A && kPart == DL_WS_PARTIAL && kDec == DL_WS_DECODE &&
+                  kS == DL_WS_SCORES && kP == DL_WS_PROBS && kG == DL_WS_GATE && kU == DL_WS_UP &&
+                  kSG == DL_WS_SILU && kDd == DL_WS_DOWN && kNBuf == DL_WS_COUNT,
+              "workspace regions follow the public enum");
 
 struct Layout {
   size_t off[kNBuf];
@@ -240,7 +250,7 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
   const int H = d->hidden, Hq = d->n_q_heads, Hkv = d->n_kv_heads, D = d->head_dim,
             I = d->intermediate, BS = d->block_size;
   const dl_dtype dt = d->dtype;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float scale = default_scale(D);
   T* n1 = at<T>(ws, L, kN1);
   T* q = at<T>(ws, L, kQ);
   T* k = at<T>(ws, L, kK);
@@ -382,7 +392,7 @@ const char* dl_status_string(dl_status s) {
 
 const char* dl_last_error(void) { return g_last_error.c_str(); }
 
-int32_t dl_abi_version(void) { return 2; }
+int32_t dl_abi_version(void) { return 3; }
 
 dl_status dl_rope_table_fill(float* cos_sin, int32_t max_pos, int32_t head_dim, double theta,
                              void* stream) {
@@ -558,6 +568,7 @@ dl_status dl_attn_prefill(const void* q, const void* k, const void* v,
   CHECK_PTR(v);
   CHECK_PTR(out);
   CHECK_IDX(cu_seqlens);
+  if (!(scale > 0.f)) scale = default_scale(D);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dt == DL_BF16
       ? attn_prefill<bf16>((const bf16*)q, (const bf16*)k, (const bf16*)v, cu_seqlens, B, max_seqlen, Hq, Hkv, D, scale, (bf16*)out, st)
@@ -594,6 +605,7 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
   if (!ws || ws_bytes < pl.ws_bytes)
     return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
   CHECK_PTR(ws);
+  if (!(scale > 0.f)) scale = default_scale(D);
   hipStream_t st = (hipStream_t)stream;
   if (is_q8(cache)) {
     const int8_t* kq = static_cast<const int8_t*>(cache->k_cache);
@@ -648,6 +660,7 @@ dl_status dl_attn_paged_qlens(const void* q, const dl_kv_cache* cache, const int
   if (!ws || ws_bytes < pl.ws_bytes)
     return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
   CHECK_PTR(ws);
+  if (!(scale > 0.f)) scale = default_scale(D);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dt == DL_BF16
       ? attn_paged_qlens<bf16>((const bf16*)q, (const bf16*)cache->k_cache, (const bf16*)cache->v_cache, block_table, max_blocks_per_seq, cu_q_lens, context_lens, B, Tq, Hq, Hkv, D, BS, max_context_len, scale, (bf16*)out, pl, ws, cache->num_blocks, st)
@@ -948,6 +961,57 @@ dl_status dl_layer_decode(const dl_layer_dims* d, const dl_layer_weights* w,
   return layer_body<float>(d, w, cos_sin, max_pos, hidden_in, hidden_out, positions, nullptr, nullptr,
                            context_lens, B, B, max_context_len, true, cache, block_table,
                            max_blocks_per_seq, m, ws, L, st);
+}
+
+dl_status dl_check_indices(const int32_t* block_table, int32_t B, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t BS, const int32_t* positions,
+                           const int32_t* seq_of_token, int32_t T, const int32_t* context_lens,
+                           int32_t max_context_len, const int32_t* cu_seqlens,
+                           int32_t max_seqlen, int32_t* error_word, void* stream) {
+  if (!error_word) return fail(DL_ERR_INVALID_ARG, "error_word must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(error_word) & 3u) != 0)
+    return fail(DL_ERR_ALIGNMENT, "error_word is not 4-byte aligned");
+  if (B < 0 || T < 0) return fail(DL_ERR_INVALID_ARG, "negative size");
+  if (block_table || positions) {
+    TRY(check_bs(BS));
+    if (max_blocks_per_seq <= 0) return fail(DL_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  }
+  if (block_table && num_blocks <= 0) return fail(DL_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (context_lens && max_context_len <= 0)
+    return fail(DL_ERR_INVALID_ARG, "max_context_len must be positive");
+  if (cu_seqlens && max_seqlen < 0) return fail(DL_ERR_INVALID_ARG, "max_seqlen must be >= 0");
+  if (block_table) CHECK_IDX(block_table);
+  if (positions) CHECK_IDX(positions);
+  if (seq_of_token) CHECK_IDX(seq_of_token);
+  if (context_lens) CHECK_IDX(context_lens);
+  if (cu_seqlens) CHECK_IDX(cu_seqlens);
+  // without positions there are no per-token checks except the sequence map
+  const int Tt = (positions || seq_of_token) ? T : 0;
+  DL_HIP(check_indices(block_table, B, max_blocks_per_seq, num_blocks, BS, positions,
+                       seq_of_token, Tt, context_lens, max_context_len, cu_seqlens, max_seqlen,
+                       error_word, (hipStream_t)stream),
+         "check_indices");
+  return ok();
+}
+
+dl_status dl_layer_workspace_regions(const dl_layer_dims* d, int32_t T, int32_t B,
+                                     int32_t max_seqlen_or_context, int32_t is_decode, dl_mode m,
+                                     size_t* offsets, size_t* sizes) {
+  TRY(check_dims(d));
+  if (m != DL_FUSED && m != DL_UNFUSED) return fail(DL_ERR_INVALID_ARG, "unknown mode %d", (int)m);
+  if (!offsets || !sizes) return fail(DL_ERR_INVALID_ARG, "offsets and sizes must not be NULL");
+  if (T <= 0 || B <= 0 || max_seqlen_or_context <= 0)
+    return fail(DL_ERR_INVALID_ARG, "T, B and the length bound must be positive");
+  if (is_decode && T != B) return fail(DL_ERR_INVALID_ARG, "a decode layout has T == B");
+  if (!is_decode && max_seqlen_or_context > T)
+    return fail(DL_ERR_INVALID_ARG, "max_seqlen must be in [1, T]");
+  const Layout L = layout(d, T, B, max_seqlen_or_context, is_decode != 0, m,
+                          part_bytes(d, T, m));
+  for (int i = 0; i < kNBuf; ++i) {
+    offsets[i] = L.off[i];
+    sizes[i] = L.size[i];
+  }
+  return ok();
 }
 
 struct dl_graph_s {

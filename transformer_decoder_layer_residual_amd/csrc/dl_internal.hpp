@@ -174,4 +174,11 @@ hipError_t unf_silu(const T* g, T* out, int64_t n, hipStream_t st);
 template <typename T>
 hipError_t unf_mul(const T* a, const T* b, T* out, int64_t n, hipStream_t st);
 
+// Validation of the paged-cache index inputs (check.hip): one workgroup,
+// writes the OR of the violated DL_CHECK_BIT_* conditions to *word.
+hipError_t check_indices(const int32_t* bt, int B, int max_blocks, int num_blocks, int BS,
+                         const int32_t* pos, const int32_t* seq, int T, const int32_t* ctx,
+                         int max_ctx, const int32_t* cu, int max_seqlen, int32_t* word,
+                         hipStream_t st);
+
 }  // namespace dl

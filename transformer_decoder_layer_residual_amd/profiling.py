@@ -165,16 +165,17 @@ def stats_md(csv_path: str, out: str, cmd: str, title: str):
         f.write("\n".join(lines) + "\n")
 
 
-def run_layer(mode: str, calls: int):
-    """One 7B-shaped prefill layer (B1 x 2048), `calls` times, for counters."""
+def run_layer(mode: str, calls: int, config: int = 2):
+    """One prefill layer call of workload `config` (2: the 7B-shaped B1 x 2048;
+    4: the 8B-GQA-shaped 8 ragged sequences), `calls` times, for counters."""
     import torch
 
     from . import binding as dl
     from . import inputs as gen
     from .harness import DeviceLayer, cache_dev, i32, to_dev
-    cfg = gen.CONFIGS[2]
+    cfg = gen.CONFIGS[config]
     pb = gen.prefill_batch(cfg)
-    layer = DeviceLayer.build(cfg, max_pos=pb.T, w_host=gen.weights(cfg))
+    layer = DeviceLayer.build(cfg, max_pos=int(pb.lens.max()), w_host=gen.weights(cfg))
     x = to_dev(gen.hidden(cfg, pb.T), torch.float32)
     bt = gen.block_table(cfg, pb.lens)
     kb, vb = gen.empty_cache(cfg, bt.num_blocks)
@@ -207,10 +208,12 @@ def main(argv=None):
     c = sub.add_parser("layer-bytes")
     c.add_argument("--mode", choices=["fused", "unfused"], required=True)
     c.add_argument("--calls", type=int, default=3)
+    c.add_argument("--config", type=int, choices=[2, 4], default=2)
     d = sub.add_parser("bytes-summary")
     for k in ("fused-fetch", "fused-write", "unfused-fetch", "unfused-write"):
         d.add_argument("--" + k, required=True)
     d.add_argument("--calls", type=int, default=3)
+    d.add_argument("--config", type=int, choices=[2, 4], default=2)
     d.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     if args.sub == "stats":
@@ -222,22 +225,26 @@ def main(argv=None):
         traffic_md(t, os.path.splitext(args.out)[0] + ".md")
         print(json.dumps(t, indent=1))
     elif args.sub == "layer-bytes":
-        run_layer(args.mode, args.calls)
+        run_layer(args.mode, args.calls, args.config)
     else:
         fu = layer_bytes(args.fused_fetch, args.fused_write, args.calls)
         un = layer_bytes(args.unfused_fetch, args.unfused_write, args.calls)
-        lines = ["# HBM bytes per Llama-2-7B-shaped prefill layer (B1 x 2048), fused vs unfused", "",
+        title = {2: "Llama-2-7B-shaped prefill layer (B1 x 2048)",
+                 4: "Llama-3-8B-GQA-shaped prefill layer (8 ragged sequences U{256..1024})"}
+        lines = [f"# HBM bytes per {title[args.config]}, fused vs unfused", "",
                  "FETCH_SIZE x 2 + WRITE_SIZE x 1 (copy-kernel calibration), summed over the "
                  "layer's kernels, per layer call.", "",
                  "Commands (repository root on the MI355X box; one counter per run, MODE = fused "
                  "or unfused, COUNTER = FETCH_SIZE or WRITE_SIZE):", "", "```",
                  "cd /tmp && export TMPDIR=/tmp && export PYTHONPATH=$REPO",
                  "rocprofv3 --pmc COUNTER -f csv -d gpurun_out/lb_MODE_COUNTER -o lb -- python -u -m "
-                 "transformer_decoder_layer_residual_amd.profiling layer-bytes --mode MODE --calls 3",
+                 "transformer_decoder_layer_residual_amd.profiling layer-bytes --mode MODE --calls 3 "
+                 f"--config {args.config}",
                  "python -m transformer_decoder_layer_residual_amd.profiling bytes-summary "
                  "--fused-fetch gpurun_out/lb_fused_FETCH_SIZE --fused-write gpurun_out/lb_fused_WRITE_SIZE "
                  "--unfused-fetch gpurun_out/lb_unfused_FETCH_SIZE --unfused-write "
-                 "gpurun_out/lb_unfused_WRITE_SIZE --calls 3 --out profiles/NAME.md", "```", "",
+                 f"gpurun_out/lb_unfused_WRITE_SIZE --calls 3 --config {args.config} "
+                 "--out profiles/NAME.md", "```", "",
                  "| path | read GB | write GB | total GB |", "|---|---:|---:|---:|",
                  f"| fused | {fu['fetch'] / 1e9:.3f} | {fu['write'] / 1e9:.3f} | {fu['total'] / 1e9:.3f} |",
                  f"| unfused (kernel per op) | {un['fetch'] / 1e9:.3f} | {un['write'] / 1e9:.3f} | "
