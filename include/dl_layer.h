@@ -251,6 +251,28 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
                                void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dl_attn_decode_paged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, with the split
+ * partials kept in a fixed device scratch array of the library instead of a
+ * caller workspace.  Nothing is allocated per call (no hipMalloc, hipFree or
+ * allocating library routine).  The scratch holds
+ * dl_attn_decode_noalloc_max_scratch() = 32 MiB on every GPU the library
+ * runs on, from load until the process ends; a call whose
+ * dl_attn_decode_workspace_size exceeds it returns DL_ERR_WORKSPACE and
+ * enqueues nothing.  Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (different streams, or host threads
+ * enqueueing concurrently) race; calls on one stream are ordered and safe.
+ * The scratch needs no clearing: every partial a call reads it wrote first.
+ */
+dl_status dl_attn_decode_paged_noalloc(const void* q, const dl_kv_cache* cache,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                                       float scale, void* out, dl_dtype dt, void* stream);
+size_t dl_attn_decode_noalloc_max_scratch(void);
+
+/*
  * Paged attention for several new tokens per sequence (ATB KV-cache page,
  * section "speculative decoding": the paged attention verifies every
  * sequence's candidate tokens in one pass, with per-sequence query lengths

@@ -77,6 +77,11 @@ _SIGS = [
     ("dl_attn_decode_paged", ctypes.c_int, [_vp, ctypes.POINTER(KVCache), _vp, _c_int, _vp,
                                             _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                             ctypes.c_float, _vp, ctypes.c_int, _vp, _sz, _vp]),
+    ("dl_attn_decode_paged_noalloc", ctypes.c_int, [_vp, ctypes.POINTER(KVCache), _vp, _c_int,
+                                                    _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                                    _c_int, ctypes.c_float, _vp, ctypes.c_int,
+                                                    _vp]),
+    ("dl_attn_decode_noalloc_max_scratch", _sz, []),
     ("dl_attn_paged_qlens_workspace_size", _sz, [_c_int] * 8),
     ("dl_attn_paged_qlens", ctypes.c_int, [_vp, ctypes.POINTER(KVCache), _vp, _c_int, _vp, _vp,
                                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -307,6 +312,21 @@ def dl_attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_con
     _check(L.dl_attn_decode_paged(_p(q), ctypes.byref(c), _p(block_table), block_table.shape[1],
                                   _p(context_lens), max_context_len, B, Hq, Hkv, D, BS, scale,
                                   _p(out), dtype_code(q.dtype), _p(ws), nb, _stream()))
+
+
+def dl_attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, context_lens,
+                                 max_context_len: int, out, scale=None, k_scale=None,
+                                 v_scale=None):
+    """dl_attn_decode_paged with the library's fixed device scratch: no
+    workspace is passed and nothing is allocated."""
+    B, Hq, D = q.shape
+    Hkv, BS = k_cache.shape[1], k_cache.shape[2]
+    scale = 0.0 if scale is None else scale       # <= 0: the library's 1/sqrt(D)
+    c = _cache(k_cache, v_cache, k_scale, v_scale)
+    _check(lib().dl_attn_decode_paged_noalloc(_p(q), ctypes.byref(c), _p(block_table),
+                                              block_table.shape[1], _p(context_lens),
+                                              max_context_len, B, Hq, Hkv, D, BS, scale, _p(out),
+                                              dtype_code(q.dtype), _stream()))
 
 
 def dl_attn_paged_qlens(q, k_cache, v_cache, block_table, cu_q_lens, context_lens,

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/dl_layer.h"
@@ -583,11 +584,42 @@ size_t dl_attn_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t
   return plan_decode(B, Hq, Hkv, D, max_context_len, BS).ws_bytes;
 }
 
-dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
-                               const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, int32_t max_context_len, int32_t B,
-                               int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, float scale,
-                               void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- fixed device scratch for the entry points that allocate nothing -------
+// One array per GPU (each device holds its own copy from the time the library
+// is loaded until the process ends).  Host code never uses the array's name as
+// an address: the per-device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dl_status scratch_address(void** out) {
+  int dev = -1;
+  DL_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DL_ERR_UNSUPPORTED, "device id %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DL_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DL_OK;
+}
+
+dl_status attn_decode_paged_impl(const void* q, const dl_kv_cache* cache,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, float scale,
+                                 void* out, dl_dtype dt, void* ws, size_t ws_bytes, bool no_alloc,
+                                 void* stream) {
   TRY(check_dtype(dt));
   TRY(check_heads(Hq, Hkv, D));
   TRY(check_bs(BS));
@@ -602,6 +634,15 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
   CHECK_IDX(block_table);
   CHECK_IDX(context_lens);
   const DecodePlan pl = plan_decode(B, Hq, Hkv, D, max_context_len, BS);
+  if (no_alloc) {
+    if (pl.ws_bytes > kScratchBytes)
+      return fail(DL_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch, beyond the fixed %zu-byte device "
+                  "scratch of dl_attn_decode_paged_noalloc (use dl_attn_decode_paged with a "
+                  "workspace)", pl.ws_bytes, kScratchBytes);
+    TRY(scratch_address(&ws));
+    ws_bytes = kScratchBytes;
+  }
   if (!ws || ws_bytes < pl.ws_bytes)
     return fail(DL_ERR_WORKSPACE, "workspace %zu < required %zu", ws_bytes, pl.ws_bytes);
   CHECK_PTR(ws);
@@ -622,6 +663,32 @@ dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
   DL_HIP(e, "attn_decode_paged");
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
+
+dl_status dl_attn_decode_paged(const void* q, const dl_kv_cache* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                               int32_t Hq, int32_t Hkv, int32_t D, int32_t BS, float scale,
+                               void* out, dl_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  return attn_decode_paged_impl(q, cache, block_table, max_blocks_per_seq, context_lens,
+                                max_context_len, B, Hq, Hkv, D, BS, scale, out, dt, ws, ws_bytes,
+                                false, stream);
+}
+
+dl_status dl_attn_decode_paged_noalloc(const void* q, const dl_kv_cache* cache,
+                                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t max_context_len,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t BS,
+                                       float scale, void* out, dl_dtype dt, void* stream) {
+  return attn_decode_paged_impl(q, cache, block_table, max_blocks_per_seq, context_lens,
+                                max_context_len, B, Hq, Hkv, D, BS, scale, out, dt, nullptr, 0,
+                                true, stream);
+}
+
+size_t dl_attn_decode_noalloc_max_scratch(void) { return kScratchBytes; }
 
 size_t dl_attn_paged_qlens_workspace_size(int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
                                           int32_t D, int32_t max_q_len,
