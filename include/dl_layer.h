@@ -467,8 +467,9 @@ dl_status dl_check_indices(const int32_t* block_table, int32_t B, int32_t max_bl
  * that call's intermediates until the next call that uses it:
  *   DL_WS_N1, DL_WS_N2    normalised activations [T][H] (dtype)
  *   DL_WS_Q, DL_WS_K, DL_WS_V   q [T][Hq][D], k, v [T][Hkv][D] after RoPE
- *                         (the fused decode step writes k/v to the cache
- *                         only, so there they are not filled)
+ *                         (the fused decode step with a layer-dtype cache
+ *                         writes k/v to the cache only, so there they are
+ *                         not filled)
  *   DL_WS_ATTN            attention output [T][Hq*D]
  *   DL_WS_O               output projection [T][H]
  *   DL_WS_H               residual stream after attention [T][H] fp32

@@ -286,9 +286,15 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
     DL_HIP(reshape_and_cache_q8<T>(k, v, seq, pos, bt, maxblk, kq, vq, cache->k_scale,
                                    cache->v_scale, Tn, Hkv, D, BS, cache->num_blocks, st),
            "reshape_and_cache_q8");
-  } else if (m == DL_FUSED && is_decode) {
-    // decode: the projection's epilogue writes rotated k and v straight into
-    // the paged cache (attention reads them only from there)
+  } else if (m == DL_FUSED) {
+    // the projection's epilogue writes rotated k and v straight into the
+    // paged cache (the reshape-and-cache write folded into the QKV step).
+    // Decode attention reads them only from there, so k/v are not stored
+    // elsewhere (nor for a step with several new tokens per sequence, whose
+    // attention also reads the cache); prefill attention reads the
+    // contiguous k/v the same epilogue also stores.  The epilogue hands out each output row from LDS
+    // in 8-column chunks, so a (token, kv head) cache row leaves as whole
+    // 128-byte segments.
     KVSink kv;
     kv.k_cache = kc;
     kv.v_cache = vc;
@@ -297,18 +303,11 @@ dl_status layer_body(const dl_layer_dims* d, const dl_layer_weights* w, const fl
     kv.max_blocks = maxblk;
     kv.block_size = BS;
     kv.num_blocks = cache->num_blocks;
-    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, nullptr, nullptr, Tn, H, Hq,
-                            Hkv, D, plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st, kv),
+    const bool kv_bufs = !is_decode && max_q_len == 0;   // only prefill attention reads them
+    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, kv_bufs ? k : nullptr,
+                            kv_bufs ? v : nullptr, Tn, H, Hq, Hkv, D,
+                            plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st, kv),
            "qkv_rope_cache");
-  } else if (m == DL_FUSED) {
-    // prefill: attention reads k/v from the projection's output, and a
-    // separate copy kernel fills the cache (writing the cache from the GEMM
-    // epilogue as well measured 2.5x more write traffic for the projection,
-    // from partial-line stores, than the 67 MB the copy kernel moves)
-    DL_HIP(gemm_qkv_rope<T>(n1, wq, wk, wv, pos, cs, max_pos, q, k, v, Tn, H, Hq, Hkv, D,
-                            plan_qkv(Tn, H, Hq, Hkv, D, dt), part, st), "qkv_rope");
-    DL_HIP(reshape_and_cache<T>(k, v, seq, pos, bt, maxblk, kc, vc, Tn, Hkv, D, BS,
-                                cache->num_blocks, st), "reshape_and_cache");
   } else {
     DL_HIP((gemm_linear<T, T>(n1, wq, q, Tn, Hq * D, H, plan_lin(Tn, Hq * D, H, dt), part, st)), "q");
     DL_HIP((gemm_linear<T, T>(n1, wk, k, Tn, Hkv * D, H, plan_lin(Tn, Hkv * D, H, dt), part, st)), "k");
