@@ -100,37 +100,61 @@ def gfx_clock_mhz():
     return best
 
 
-def clock_under(fn, stream, samples=4, limit_s=30.0):
-    """Graphics clock sampled while fn repeats back to back on the GPU
-    (outside every timed region): mean of the samples taken, or None.  The
-    reported clock follows the load with a lag of about a second, so the
-    load runs 2 s before the first sample and samples are 0.5 s apart."""
-    import threading
-    vals, stop = [], threading.Event()
+class ClockSampler:
+    """Graphics-clock readings from a child process started before this
+    process touches the GPU (the child runs amd-smi every half second and
+    prints time-stamped readings; nothing is started from the GPU process).
+    under(fn) keeps fn repeating on the GPU for a few seconds and averages the
+    readings taken in that window, skipping its first 2 s (the reported
+    clock lags the load by about a second)."""
 
-    def sampler():
-        if stop.wait(2.0):
+    def __init__(self):
+        import subprocess
+        import threading
+        self.samples = []
+        self.proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler"],
+                                     stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+
+        def reader():
+            for line in self.proc.stdout:
+                t, _, v = line.strip().partition(" ")
+                try:
+                    self.samples.append((float(t), float(v)))
+                except ValueError:
+                    pass
+
+        self.th = threading.Thread(target=reader, daemon=True)
+        self.th.start()
+
+    def under(self, fn, stream, seconds=4.5):
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            for _ in range(10):
+                fn()
+            stream.synchronize()
+        t1 = time.time()
+        time.sleep(0.6)                       # the reading of the window's last moments
+        vals = [v for t, v in self.samples if t0 + 2.0 <= t <= t1]
+        return round(sum(vals) / len(vals), 1) if vals else None
+
+    def close(self):
+        if self.proc.poll() is None:
+            self.proc.terminate()
+            try:
+                self.proc.wait(timeout=10)
+            except Exception:
+                self.proc.kill()
+
+
+def clock_sampler_child(limit_s=1200.0):
+    """The sampler child's loop (never initialises the GPU)."""
+    t0 = time.time()
+    while time.time() - t0 < limit_s:
+        v = gfx_clock_mhz()
+        print(f"{time.time():.3f} {v if v is not None else 'none'}", flush=True)
+        if v is None:
             return
-        while not stop.is_set() and len(vals) < samples:
-            v = gfx_clock_mhz()
-            if v is None:
-                return
-            vals.append(v)
-            stop.wait(0.5)
-
-    for _ in range(5):
-        fn()
-    stream.synchronize()
-    th = threading.Thread(target=sampler, daemon=True)
-    th.start()
-    t0 = time.perf_counter()
-    while th.is_alive() and time.perf_counter() - t0 < limit_s:
-        for _ in range(10):
-            fn()
-        stream.synchronize()
-    stop.set()
-    th.join(timeout=60)
-    return round(sum(vals) / len(vals), 1) if vals else None
+        time.sleep(0.5)
 
 
 def time_synced(fn, n, stream):
@@ -274,16 +298,25 @@ def cpu_sample(kind: str) -> dict:
                       f"{', '.join(str(int(c)) for c in ctx)}), exact mode, {dt:.2f} s"}
 
 
-def cpu_child(kind: str) -> dict:
-    """cpu_sample in a child process pinned to one OpenMP thread (the child
-    never touches the GPU)."""
+def cpu_child(kind: str):
+    """Start cpu_sample in a child process pinned to one OpenMP thread; the
+    caller starts it before touching the GPU and collects it with
+    cpu_child_result (the child never touches the GPU)."""
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-sample", kind],
-                       capture_output=True, text=True, env=env, timeout=600)
-    if r.returncode != 0:
-        return {"error": (r.stderr or "")[-300:]}
-    return json.loads(r.stdout.strip().splitlines()[-1])
+    return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-sample", kind],
+                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env)
+
+
+def cpu_child_result(proc) -> dict:
+    try:
+        out, err = proc.communicate(timeout=600)
+    except Exception as e:   # noqa: BLE001
+        proc.kill()
+        return {"error": str(e)}
+    if proc.returncode != 0:
+        return {"error": (err or "")[-300:]}
+    return json.loads(out.strip().splitlines()[-1])
 
 
 def main():
@@ -300,9 +333,14 @@ def main():
                     help="prefix length of the CPU-oracle sample")
     ap.add_argument("--cpu-sample", choices=["tiny", "decode"], default=None,
                     help=argparse.SUPPRESS)   # the one-thread CPU child (no GPU use)
+    ap.add_argument("--clock-sampler", action="store_true",
+                    help=argparse.SUPPRESS)   # the clock-reading child (no GPU use)
     args = ap.parse_args()
     if args.cpu_sample:
         print(json.dumps(cpu_sample(args.cpu_sample)), flush=True)
+        return
+    if args.clock_sampler:
+        clock_sampler_child()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer is "
@@ -310,6 +348,16 @@ def main():
               "sequence (no exchange) or by KV head and FFN columns with one all-reduce after "
               "O and one after down, none of which is built here", file=sys.stderr)
         sys.exit(2)
+
+    # children first: nothing is started from this process once it has
+    # touched the GPU
+    clocks = ClockSampler()
+    host = host_cpu()
+    children = {}
+    if not args.no_cpu_baseline:
+        children["tiny"] = cpu_child("tiny")
+        if not args.no_decode:
+            children["decode"] = cpu_child("decode")
 
     import numpy as np
     import torch
@@ -385,7 +433,7 @@ def main():
         f"({100 * gu_tf / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
     # graphics clock under the prefill step (sampled after the timed region):
     # the published peaks are at 2400 MHz
-    clk_prefill = clock_under(step, stream)
+    clk_prefill = clocks.under(step, stream)
     log(f"[bench] graphics clock under the prefill step: {clk_prefill} MHz")
 
     result = {
@@ -416,8 +464,9 @@ def main():
                                                                / SPEC_CLOCK_MHZ), 4)
                                                 if clk_prefill else None)},
         "clock": {"spec_mhz": SPEC_CLOCK_MHZ, "prefill_step_mhz": clk_prefill,
-                  "source": "amd-smi metric -c, mean over the XCD clock domains, sampled while "
-                            "the step repeats after its timed region"},
+                  "source": "amd-smi metric -c (run by a child process started before the GPU "
+                            "is touched), mean over the XCD clock domains, sampled while the step "
+                            "repeats after its timed region"},
         "step_ms_percentiles": {"p10": round(p10, 4), "p50": round(ms, 4), "p90": round(p90, 4),
                                 "steps": args.steps},
         "layer": {"flops_per_step": layer_flops,
@@ -484,7 +533,8 @@ def main():
                             "cache_state": "inside back-to-back step-by-step layer chains",
                             "achieved": round(gu4_tf, 1), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(gu4_tf / PEAK_BF16_TFLOPS, 4),
-                            "traffic": None, "flops_per_launch": gu4_fl,
+                            "traffic": load_traffic("gemm_gateup_silu_prefill_8b"),
+                            "flops_per_launch": gu4_fl,
                             "avg_launch_ms": round(gu4_ms, 4)}}
         log(f"[bench] 8B GQA prefill B8 ragged (T={T4}): {ms4:.3f} ms/step (cold median; "
             f"back-to-back {warm4:.3f}), {T4 / (ms4 * 1e-3):,.0f} tokens/s; gate/up "
@@ -580,7 +630,7 @@ def main():
                          "warm_back_to_back_ms": round(a_warm, 4)},
         }
         if not int8:
-            clk = clock_under(dstep, stream)
+            clk = clocks.under(dstep, stream)
             result["clock"]["decode_step_mhz"] = clk
             log(f"[bench] graphics clock under the decode step: {clk} MHz")
         log(f"[bench] decode ({kind} cache): {dms:.3f} ms/step, {B / (dms * 1e-3):,.0f} "
@@ -895,12 +945,12 @@ def main():
         result["cpu_baseline"] = {
             "value": round(n / dt, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n} of the {T} prefill tokens, same weights, exact fp32/fp64 "
-                      f"mode, {dt:.1f} s", "host": host_cpu()}
+                      f"mode, {dt:.1f} s", "host": host}
         # the tiny fp32 layer (prefill of 32 tokens + 8 decode steps) on all
         # threads here and on one thread in a child process; the 7B decode
         # step for 4 sequences on one thread
         tiny = cpu_sample("tiny")
-        tiny1 = cpu_child("tiny")
+        tiny1 = cpu_child_result(children["tiny"])
         result["cpu_baseline_tiny"] = {
             "unit": "tokens/s", "kind": "oracle",
             "sample": "tiny fp32 layer: prefill of 32 tokens, then 8 decode steps",
@@ -928,8 +978,12 @@ def main():
                 "sample": f"first {nb} of the 64 sequences of the 7B decode step (contexts "
                           f"{', '.join(str(int(c)) for c in dctx)}), same weights, exact "
                           f"fp32/fp64 mode, {ddt:.2f} s",
-                "one_thread": cpu_child("decode")}
+                "one_thread": cpu_child_result(children["decode"])}
             del kf, vf
+    clocks.close()
+    for proc in children.values():
+        if proc.poll() is None:
+            proc.kill()
     print(json.dumps(result), flush=True)
 
 

@@ -46,7 +46,9 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
                    int n_items, float* __restrict__ partial, int NP) {
   static_assert(NST % 2 == 0 && NST >= 2, "stage pairs");
   constexpr int NI = MB / 16, G = kSkKS / 32, STAGE_B = MB * kSkKS * 2;
-  constexpr int XI = MB / 8;  // activation vectors (16 B) per thread per stage
+  constexpr int RB = kSkKS * 2, CPX = kSkKS / 8;  // bytes and 16-byte chunks of an LDS row
+  constexpr int XI = MB * CPX / kSkNT;            // activation vectors (16 B) per thread per stage
+  static_assert(XI * kSkNT == MB * CPX, "activation vectors split evenly over the threads");
   constexpr int kc = NST * kSkKS;
   __shared__ __attribute__((aligned(1024))) unsigned char xs[2][STAGE_B];
 
@@ -85,7 +87,7 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
   auto load_x = [&](const Item& x, int st) {
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
-      const int v = t + kSkNT * u, m = v >> 5, c = v & 31;
+      const int v = t + kSkNT * u, m = v / CPX, c = v % CPX;
       const int k = min(st * kSkKS + 8 * c, x.klen - 8);
       xr[u] = ld16(X + (int64_t)min(m, M - 1) * K + x.k0 + k);
     }
@@ -94,8 +96,8 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
     const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
-      const int v = t + kSkNT * u, m = v >> 5, c = v & 31;
-      st16(&xs[buf][m * 512 + ((c ^ (m & 15)) << 4)],
+      const int v = t + kSkNT * u, m = v / CPX, c = v % CPX;
+      st16(&xs[buf][m * RB + ((c ^ (m & 15)) << 4)],
            st * kSkKS + 8 * c < x.klen ? xr[u] : zero);
     }
   };
@@ -129,7 +131,7 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
     load_x(xa, sx);
     // bare barrier: __syncthreads() would also drain the weight loads in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const unsigned char* xst = &xs[st & 1][(lane & 15) * 512];
+    const unsigned char* xst = &xs[st & 1][(lane & 15) * RB];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int off = ((4 * g + (lane >> 4)) ^ sw) * 16;
@@ -137,7 +139,7 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, w[1][g]);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xst + i * 16 * 512 + off);
+        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xst + i * 16 * RB + off);
         acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xf, acc[0][i], 0, 0, 0);
         acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xf, acc[1][i], 0, 0, 0);
       }

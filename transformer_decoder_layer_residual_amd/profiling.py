@@ -40,9 +40,15 @@ WRITE_SCALE = 1.0
 # __bf16 printed as "bool _Accum"; each pattern accepts both forms of the one
 # instance the benchmark's roofline line times)
 KERNELS = {
+    # the 7B prefill gate/up (2048 x 22016 x 4096: 8 x 86 tiles of 512 threads)
     "gemm_gateup_silu_prefill": (r"gemm_pp_kernelILi256ELi64ENS_9MapSwiglu"
                                  r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
-                                 ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp")),
+                                 ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp"), 688 * 512),
+    # the same kernel at the 8B-GQA ragged prefill (6235 x 28672 x 4096: 25 x 112 tiles)
+    "gemm_gateup_silu_prefill_8b": (r"gemm_pp_kernelILi256ELi64ENS_9MapSwiglu"
+                                    r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
+                                    ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp"),
+                                    2800 * 512),
     # the 70B-shaped decode gate/up (K = 8192: 16-deep, 8 waves; B4 and B1 calls)
     "gemm_gateup_silu_decode_70b": (r"gemm_row16_kernelILi16ELi8ENS_9MapSwiglu"
                                     r"|gemm_row16_kernel<16, 8, dl::MapSwiglu",
@@ -75,12 +81,13 @@ def _rows(d: str):
 
 
 def _per_kernel(d: str, counter: str):
-    """kernel name -> list of per-dispatch counter values (KiB)."""
+    """(kernel name, grid size in threads) -> list of per-dispatch counter
+    values (KiB)."""
     res = {}
     for r in _rows(d):
         if r["Counter_Name"] != counter:
             continue
-        res.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        res.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
     return res
 
 
@@ -88,15 +95,18 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     f = _per_kernel(fetch_dir, "FETCH_SIZE")
     w = _per_kernel(write_dir, "WRITE_SIZE")
     out = {"fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE}
-    for key, (rx, srcs) in KERNELS.items():
-        names = [n for n in f if re.search(rx, n)]
+    for key, spec in KERNELS.items():
+        rx, srcs = spec[0], spec[1]
+        grid = spec[2] if len(spec) > 2 else None   # launch grid of the one workload meant
+        names = [n for n in f if re.search(rx, n[0]) and (grid is None or n[1] == grid)]
         if not names:
             continue
         fv = [v for n in names for v in f[n]]
         wv = [v for n in names for v in w.get(n, [])]
         fetch = sum(fv) / len(fv) * 1024 * FETCH_SCALE
         write = (sum(wv) / len(wv) * 1024 * WRITE_SCALE) if wv else 0.0
-        out[key] = {"kernel": names[0][:160], "dispatches": len(fv),
+        out[key] = {"kernel": names[0][0][:160], "grid_threads": names[0][1],
+                    "dispatches": len(fv),
                     "fetch_bytes": round(fetch), "write_bytes": round(write),
                     "bytes_per_launch": round(fetch + write),
                     "source_sha": source_sha(*srcs)}
@@ -124,6 +134,29 @@ def layer_bytes(fetch_dir: str, write_dir: str, calls: int) -> dict:
     wb, wper = total(write_dir, "WRITE_SIZE", WRITE_SCALE)
     return {"fetch": fb, "write": wb, "total": fb + wb, "fetch_per_kernel": fper,
             "write_per_kernel": wper}
+
+
+def counters_md(dirs, out: str, cmd: str, title: str):
+    """Per-kernel mean of every counter found under the given rocprofv3 --pmc
+    output directories (one directory per pass), as a markdown table; the
+    MfmaUtil column is rocprofv3's derived metric (SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE x SIMDs, in %)."""
+    per = {}
+    for d in dirs:
+        for r in _rows(d):
+            n = re.sub(r"^_ZN2dl\d+", "", r["Kernel_Name"])[:72]
+            per.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = [f"# {title}", "", "Commands (repository root on the MI355X box; one counter set per run):",
+             "", "```", "cd /tmp && export TMPDIR=/tmp && export PYTHONPATH=$REPO", cmd, "```", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |",
+             "|---|---:|" + "---:|" * len(names)]
+    for n, c in sorted(per.items(), key=lambda kv: -max(len(v) for v in kv[1].values())):
+        disp = max(len(v) for v in c.values())
+        vals = [f"{sum(c[k]) / len(c[k]):.4g}" if k in c else "" for k in names]
+        lines.append(f"| `{n}` | {disp} | " + " | ".join(vals) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def traffic_md(t: dict, out: str):
@@ -209,6 +242,11 @@ def main(argv=None):
     c.add_argument("--mode", choices=["fused", "unfused"], required=True)
     c.add_argument("--calls", type=int, default=3)
     c.add_argument("--config", type=int, choices=[2, 4], default=2)
+    e = sub.add_parser("counters")
+    e.add_argument("--dirs", nargs="+", required=True)
+    e.add_argument("--out", required=True)
+    e.add_argument("--cmd", required=True)
+    e.add_argument("--title", default="Counters per kernel")
     d = sub.add_parser("bytes-summary")
     for k in ("fused-fetch", "fused-write", "unfused-fetch", "unfused-write"):
         d.add_argument("--" + k, required=True)
@@ -224,6 +262,8 @@ def main(argv=None):
             json.dump(t, f, indent=1)
         traffic_md(t, os.path.splitext(args.out)[0] + ".md")
         print(json.dumps(t, indent=1))
+    elif args.sub == "counters":
+        counters_md(args.dirs, args.out, args.cmd, args.title)
     elif args.sub == "layer-bytes":
         run_layer(args.mode, args.calls, args.config)
     else:
