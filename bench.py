@@ -254,10 +254,12 @@ def host_cpu():
     return info
 
 
-def cpu_sample(kind: str) -> dict:
+def cpu_sample(kind: str, ready=None) -> dict:
     """A bounded CPU-oracle sample (no GPU): 'tiny' = the tiny fp32 layer's
     32-token prefill then 8 decode steps on its own cache; 'decode' = the 7B
-    decode layer step for the first 4 sequences of the 7B decode workload."""
+    decode layer step for the first 4 sequences of the 7B decode workload.
+    `ready`, if given, is called once the inputs are built and returns when
+    the timed part may start."""
     import numpy as np
 
     import oracle
@@ -271,6 +273,8 @@ def cpu_sample(kind: str) -> dict:
         kf, vf = gen.cache_to_f32(kb).copy(), gen.cache_to_f32(vb).copy()
         x = gen.hidden(cfg, pb.T)
         xs = [gen.hidden(cfg, 1, step=1 + s) for s in range(cfg.decode_steps)]
+        if ready:
+            ready()
         t0 = time.perf_counter()
         oracle.layer_prefill(cfg.dims(), w, x, pb.positions, pb.seq_of_token, pb.cu_seqlens, kf,
                              vf, bt.table, mode=oracle.EXACT)
@@ -290,6 +294,8 @@ def cpu_sample(kind: str) -> dict:
     kb, vb = gen.synthetic_cache(cfg, bt, ctx)
     kf, vf = gen.bits_to_f32(kb), gen.bits_to_f32(vb)
     x = gen.hidden(cfg, nb)
+    if ready:
+        ready()
     t0 = time.perf_counter()
     oracle.layer_decode(cfg.dims(), w, x, ctx, kf, vf, bt.table, mode=oracle.EXACT)
     dt = time.perf_counter() - t0
@@ -301,16 +307,21 @@ def cpu_sample(kind: str) -> dict:
 def cpu_child(kind: str):
     """Start cpu_sample in a child process pinned to one OpenMP thread; the
     caller starts it before touching the GPU and collects it with
-    cpu_child_result (the child never touches the GPU)."""
+    cpu_child_result (the child never touches the GPU).  The child builds its
+    inputs, then waits for a line on its stdin before its timed part, so the
+    caller releases it only while its own process is idle."""
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1")
     return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-sample", kind],
-                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env)
+                            stdin=subprocess.PIPE, stdout=subprocess.PIPE,
+                            stderr=subprocess.PIPE, text=True, env=env)
 
 
 def cpu_child_result(proc) -> dict:
+    """Release the child's timed part and wait for its JSON line (the caller
+    does nothing else meanwhile)."""
     try:
-        out, err = proc.communicate(timeout=600)
+        out, err = proc.communicate(input="go\n", timeout=600)
     except Exception as e:   # noqa: BLE001
         proc.kill()
         return {"error": str(e)}
@@ -337,7 +348,7 @@ def main():
                     help=argparse.SUPPRESS)   # the clock-reading child (no GPU use)
     args = ap.parse_args()
     if args.cpu_sample:
-        print(json.dumps(cpu_sample(args.cpu_sample)), flush=True)
+        print(json.dumps(cpu_sample(args.cpu_sample, ready=sys.stdin.readline)), flush=True)
         return
     if args.clock_sampler:
         clock_sampler_child()

@@ -21,9 +21,13 @@ namespace dl {
 //     start or drain idles the memory pipe;
 //   * each wave streams its 2 x 16 weight rows straight from HBM into
 //     registers in the 16x16x32 MFMA operand layout (lane l holds row l % 16
-//     at k = 8 * (l / 16) of each 32-wide k group); two stages are in flight,
-//     and each k group's registers are reloaded for two stages ahead as soon
-//     as its MFMAs are issued;
+//     at k = 8 * (l / 16) of each 32-wide k group); each k group's registers
+//     are reloaded for the next stage as soon as its MFMAs are issued, so one
+//     stage (16 loads of 16 B per lane) is in flight.  Two stages in flight
+//     (two register sets) streamed 4-11% slower on every 64-row decode
+//     projection of the 7B layer: a plain one-workgroup-per-CU stream, too,
+//     runs at 5.8-5.9 TB/s with 8 or 16 loads in flight per lane and at about
+//     3.8 TB/s with 32;
 //   * the activation rows of a stage are loaded into registers one stage
 //     ahead and written to a double-buffered LDS tile (2 x MB x 256 bf16, at
 //     most 64 KB); chunk c of row m sits at c ^ (m % 16), so a fragment's 16
@@ -101,8 +105,8 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
            st * kSkKS + 8 * c < x.klen ? xr[u] : zero);
     }
   };
-  u32x4 wa[2][G], wb[2][G];
-  auto load_group = [&](u32x4 (&w)[2][G], const Item& x, int g, int st) {
+  u32x4 w[2][G];
+  auto load_group = [&](const Item& x, int g, int st) {
     const int e = x.k0 + min(st * kSkKS + 32 * g + kl, x.klen - 8);
     w[0][g] = ld16(x.w0 + e);
     w[1][g] = ld16(x.w1 + e);
@@ -117,17 +121,17 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
   };
   const int sw = lane & 15;  // chunk swizzle of this lane's fragment rows
 
-  // One stage st of item cur: next activations' first half load, barrier
-  // (this stage's activations visible; the other buffer free), MFMAs with
-  // the weight reloads for two stages ahead (which may fall in item nxt),
-  // the next activations into the other buffer.  Past the last item, loads
-  // repeat the current item's last stage (cached) and feed nothing.
-  auto stage = [&](u32x4 (&w)[2][G], auto stc, const Item& cur, const Item& nxt, bool last) {
+  // One stage st of item cur: next activations' load, barrier (this stage's
+  // activations visible; the other buffer free), MFMAs with the weight
+  // reloads for the next stage (which may fall in item nxt), the next
+  // activations into the other buffer.  Past the last item, loads repeat the
+  // current item's last stage (cached) and feed nothing.
+  auto stage = [&](auto stc, const Item& cur, const Item& nxt, bool last) {
     constexpr int st = decltype(stc)::value;
     const Item& xa = st + 1 < NST ? cur : (last ? cur : nxt);
     const int sx = st + 1 < NST ? st + 1 : (last ? NST - 1 : 0);
-    const Item& wi = st + 2 < NST ? cur : (last ? cur : nxt);
-    const int swt = st + 2 < NST ? st + 2 : (last ? NST - 1 : st + 2 - NST);
+    const Item& wi = st + 1 < NST ? cur : (last ? cur : nxt);
+    const int swt = st + 1 < NST ? st + 1 : (last ? NST - 1 : 0);
     load_x(xa, sx);
     // bare barrier: __syncthreads() would also drain the weight loads in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -143,9 +147,9 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
         acc[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xf, acc[0][i], 0, 0, 0);
         acc[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xf, acc[1][i], 0, 0, 0);
       }
-      load_group(w, wi, g, swt);
+      load_group(wi, g, swt);
       // keep the reload here: the scheduler would otherwise sink it to its
-      // use two stages later and serialise the stream
+      // use in the next stage and serialise the stream
       __builtin_amdgcn_sched_barrier(0);
     }
     store_x(xa, sx, (st + 1) & 1);
@@ -154,9 +158,7 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
   Item cur = make(i0);
   Item nxt = make(min(i0 + 1, i1 - 1));
 #pragma unroll
-  for (int g = 0; g < G; ++g) load_group(wa, cur, g, 0);
-#pragma unroll
-  for (int g = 0; g < G; ++g) load_group(wb, cur, g, 1);
+  for (int g = 0; g < G; ++g) load_group(cur, g, 0);
   load_x(cur, 0);
   store_x(cur, 0, 0);
 
@@ -165,17 +167,17 @@ gemm_skinny_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, i
     const bool last = it + 1 >= i1;
     zero_acc();
     using std::integral_constant;
-    stage(wa, integral_constant<int, 0>{}, cur, nxt, last);
-    stage(wb, integral_constant<int, 1>{}, cur, nxt, last);
+    stage(integral_constant<int, 0>{}, cur, nxt, last);
+    stage(integral_constant<int, 1>{}, cur, nxt, last);
     if constexpr (NST > 2) {
-      stage(wa, integral_constant<int, 2>{}, cur, nxt, last);
-      stage(wb, integral_constant<int, 3>{}, cur, nxt, last);
+      stage(integral_constant<int, 2>{}, cur, nxt, last);
+      stage(integral_constant<int, 3>{}, cur, nxt, last);
     }
     if constexpr (NST > 4) {
-      stage(wa, integral_constant<int, 4>{}, cur, nxt, last);
-      stage(wb, integral_constant<int, 5>{}, cur, nxt, last);
-      stage(wa, integral_constant<int, 6>{}, cur, nxt, last);
-      stage(wb, integral_constant<int, 7>{}, cur, nxt, last);
+      stage(integral_constant<int, 4>{}, cur, nxt, last);
+      stage(integral_constant<int, 5>{}, cur, nxt, last);
+      stage(integral_constant<int, 6>{}, cur, nxt, last);
+      stage(integral_constant<int, 7>{}, cur, nxt, last);
     }
     static_assert(NST == 2 || NST == 4 || NST == 8, "stage sequence above");
     // lane holds C[n = 4 * (lane / 16) + e][m = 16 * i + lane % 16] of each block
