@@ -340,6 +340,9 @@ def test_qkv_rope_cache_equals_separate_calls(cfg_id, decode):
 
 PREFILL_CASES = [  # lens, Hq, Hkv, D
     ([32], 4, 4, 64), ([1, 7, 130, 64], 4, 2, 128), ([300, 129], 8, 1, 128), ([257], 2, 2, 64),
+    # even and odd q-tile counts (128-query tiles paired first with last), a
+    # tile split between the two wave groups of a workgroup, an empty sequence
+    ([1024], 4, 2, 128), ([640, 385, 2, 0, 129], 4, 4, 64), ([896, 65], 2, 1, 128),
 ]
 
 

@@ -55,20 +55,13 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
     return pl;
   }
   if (cfg == kCfgSkinny) {
-    // K slice: 2048 when that still gives every persistent workgroup at least
-    // four items, else 1024 with at least two, else 512.  Measured on the
-    // decode shapes of the 7B (M 64), 8B (M 8) and 70B (M 4) layers, this
-    // picks the fastest slice or one within 8% of it on all twelve
-    // projections; a round model (workgroups streaming at a fixed rate) had
-    // picked 2048 for the 70B down and O projections (112 and 38 us against
-    // 99 and 32 us at 1024).
-    auto items_at = [&](int kc) { return (long)((K + kc - 1) / kc) * nt; };
-    int best_kc = 2 * kSkKS;
-    if (items_at(8 * kSkKS) >= 4L * kSkGrid) best_kc = 8 * kSkKS;
-    else if (items_at(4 * kSkKS) >= 2L * kSkGrid) best_kc = 4 * kSkKS;
-    pl.splits = (K + best_kc - 1) / best_kc;
-    pl.k_per_split = best_kc;
-    pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)tiles_n(cfg) * kSkBN *
+    // stream-K over (tile, 256-k stage) units: splits = the partial slabs
+    // per tile (1: none), k_per_split = the stages of a tile
+    const int S = (K + kSkKS - 1) / kSkKS, tn = tiles_n(cfg);
+    const int W = (int)std::min<int64_t>(kSkGrid, (int64_t)tn * S);
+    pl.k_per_split = S;
+    pl.splits = sk_max_contributors(tn, S, W);
+    pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)tn * kSkBN *
                                       sizeof(float) : 0;
     return pl;
   }
@@ -206,39 +199,30 @@ static hipError_t launch_big(const bf16* x, int M, int K, const Map& map, const 
   return hipGetLastError();
 }
 
-template <int MB, class Map, class Epi>
-static void launch_skinny_mb(const bf16* x, int M, int K, const Map& map, const Epi& epi, int kc,
-                             int tiles_n, int n_items, float* partial, int NP, hipStream_t st) {
-  const dim3 grid(std::min(n_items, kSkGrid));
-  if (kc == 2 * kSkKS)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 2, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, tiles_n, n_items, partial, NP);
-  else if (kc == 4 * kSkKS)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 4, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, tiles_n, n_items, partial, NP);
-  else
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, 8, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K,
-                       map, epi, tiles_n, n_items, partial, NP);
-}
-
 template <class Map, class Epi>
 static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, const Epi& epi,
                                 int NL, const GemmPlan& pl, void* ws, hipStream_t st) {
-  const int kc = pl.k_per_split;
-  if (M > 64 || (kc != 2 * kSkKS && kc != 4 * kSkKS && kc != 8 * kSkKS)) return hipErrorInvalidValue;
+  const int S = pl.k_per_split;
   const int tiles_n = (NL + kSkBN - 1) / kSkBN;
+  if (M > 64 || S != (K + kSkKS - 1) / kSkKS) return hipErrorInvalidValue;
   const int NP = tiles_n * kSkBN;
-  const int n_items = tiles_n * pl.splits;
+  const int W = (int)std::min<int64_t>(kSkGrid, (int64_t)tiles_n * S);
   float* partial = pl.splits > 1 ? reinterpret_cast<float*>(ws) : nullptr;
-  if (M <= 16) launch_skinny_mb<16>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
-  else if (M <= 32) launch_skinny_mb<32>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
-  else launch_skinny_mb<64>(x, M, K, map, epi, kc, tiles_n, n_items, partial, NP, st);
+  const dim3 grid(W);
+  if (M <= 16)
+    hipLaunchKernelGGL((gemm_skinny_kernel<16, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K, map,
+                       epi, tiles_n, S, partial, NP);
+  else if (M <= 32)
+    hipLaunchKernelGGL((gemm_skinny_kernel<32, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K, map,
+                       epi, tiles_n, S, partial, NP);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<64, Map, Epi>), grid, dim3(kSkNT), 0, st, x, M, K, map,
+                       epi, tiles_n, S, partial, NP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   const int64_t work = (int64_t)M * tiles_n * (kSkBN / 8);
-  const int parts = splitk_parts(pl.splits), per_block = kReduceThreads / parts;
-  hipLaunchKernelGGL((splitk_reduce<Epi>), dim3((int)((work + per_block - 1) / per_block)),
-                     dim3(kReduceThreads), 0, st, partial, pl.splits, parts, M, NP, kSkBN, epi);
+  hipLaunchKernelGGL((streamk_reduce<Epi>), dim3((int)((work + 255) / 256)), dim3(256), 0, st,
+                     partial, M, NP, tiles_n, S, W, epi);
   return hipGetLastError();
 }
 
