@@ -78,7 +78,8 @@ GEMM_SHAPES = [
     (200, 1024, 4096), (600, 2048, 256), (2048, 16384, 320), (100, 96, 688),
     (700, 22000, 200),   # 256x256 prefill tile: M tail, ragged N, K tail
     (40, 1008, 264),     # decode weight-streaming kernel: ragged last tile, K tail
-    (64, 4096, 11008),   # decode down-projection shape: 16 K slices
+    (64, 4096, 11008),   # decode down-projection shape: tiles shared by several workgroups
+    (40, 38400, 512),    # decode stream with runs of 2-3 stages: whole tiles and shared ones
     (2048, 12288, 128),  # 384 tiles of 256: 256-row tiles then 128-row tiles in one launch
     (2000, 12288, 192),  # the same with a ragged last row tile
 ]
