@@ -168,9 +168,9 @@ def traffic_md(t: dict, out: str):
              "Commands (repository root on the MI355X box):", "", "```",
              "cd /tmp && export TMPDIR=/tmp",
              "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_f -o bench -- python -u "
-             "bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-clock",
              "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_w -o bench -- python -u "
-             "bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-clock",
              "python -m transformer_decoder_layer_residual_amd.profiling traffic --fetch "
              "gpurun_out/pmc_f --write gpurun_out/pmc_w --out profiles/traffic.json", "```", "",
              "| key | kernel | dispatches | fetch MB | write MB | bytes/launch MB | source_sha |",
