@@ -227,12 +227,18 @@ attn_prefill_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 // the score registers with the key order of its k-slots matched by the V^T
 // reads.  Waves skip tiles entirely above their causal diagonal.  Blocks are
 // ordered so that every q-tile of a head runs on the same XCD (K/V of a head
-// stay in that XCD's L2): the heavier half of the q-tiles first, heaviest
-// first, then the lighter half lightest first.  With two workgroups per CU
-// filled in dispatch order, a CU then holds tiles t and n-1-t, whose causal
-// work adds up to the same total on every CU (heaviest-first alone paired
-// heavy with middle tiles: up to 1.4x the average work on one CU).
+// stay in that XCD's L2).  When the whole grid is resident at once (two
+// workgroups per CU), the heavier half of the q-tiles goes first, heaviest
+// first, then the lighter half lightest first: a CU then holds tiles t and
+// n-1-t, whose causal work adds up to the same total on every CU
+// (heaviest-first alone paired heavy with middle tiles: up to 1.4x the
+// average work on one CU; 4% slower at 7B B1 x 2048).  A larger grid is
+// dispatched as slots free up, and there heaviest-first throughout balances
+// better (the 8B batch of 8 ragged sequences: 106 against 114 us).
 // ---------------------------------------------------------------------------
+// workgroups of the bf16 kernel resident at once: two per CU on 256 CUs
+constexpr long kPfResidentBlocks = 2 * 256;
+
 // Column of key `key` in a V^T tile row.  Within each 16-key group the
 // 32x32x16 score block gives a lane keys {4h..4h+3} and {8+4h..8+4h+3} (h =
 // lane / 32) of one k16 step; swapping bits 2 and 3 of the key puts those
@@ -246,7 +252,7 @@ __global__ void __launch_bounds__(256, 2)
 attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, const int32_t* __restrict__ cu, int Hq,
                          int Hkv, float scale_log2, bf16* __restrict__ out, int n_qtiles,
-                         int n_heads_total) {
+                         int n_heads_total, int pair_order) {
   constexpr int BQ = 128, BKV = 64, QW = 32;
   constexpr int KLS = D + 8;          // padded K row (elements)
   constexpr int VLS = BKV + 8;        // padded V^T row
@@ -270,7 +276,7 @@ attn_prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     hh = L % n_heads_total;
   }
   const int heavy = (n_qtiles + 1) / 2;
-  const int qt = u < heavy ? n_qtiles - 1 - u : u - heavy;
+  const int qt = !pair_order || u < heavy ? n_qtiles - 1 - u : u - heavy;
   const int b = hh / Hq, h = hh % Hq;
   const int t0 = cu[b], S = cu[b + 1] - t0;
   const int q_begin = qt * BQ;
@@ -473,12 +479,13 @@ hipError_t attn_prefill(const T* q, const T* k, const T* v, const int32_t* cu_se
   if constexpr (sizeof(T) == 2) {
     const int nh = B * Hq;
     dim3 grid(n_qtiles * nh), block(256);
+    const int pair = (long)n_qtiles * nh <= kPfResidentBlocks ? 1 : 0;
     if (D == 128)
       hipLaunchKernelGGL((attn_prefill_bf16_kernel<128>), grid, block, 0, st, q, k, v, cu_seqlens,
-                         Hq, Hkv, sl2, out, n_qtiles, nh);
+                         Hq, Hkv, sl2, out, n_qtiles, nh, pair);
     else if (D == 64)
       hipLaunchKernelGGL((attn_prefill_bf16_kernel<64>), grid, block, 0, st, q, k, v, cu_seqlens,
-                         Hq, Hkv, sl2, out, n_qtiles, nh);
+                         Hq, Hkv, sl2, out, n_qtiles, nh, pair);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
