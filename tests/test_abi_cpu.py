@@ -165,3 +165,63 @@ def test_check_indices_host_errors(L):
     assert s == 2 and b"block_size" in L.dl_last_error()
     s = L.dl_check_indices(None, 2, 0, 0, 0, None, None, 0, 64, 0, None, 0, 8, None)
     assert s == 1 and b"max_context_len" in L.dl_last_error()
+
+
+def test_empty_work_returns_ok_and_negative_sizes_fail(L):
+    """Zero tokens or sequences is valid work: every compute entry point
+    returns DL_OK before it needs a data pointer (so NULLs are fine) and
+    enqueues nothing; negative sizes are rejected as invalid arguments."""
+    bf = dl.DL_BF16
+    c = dl.KVCache(16 * 1024, 32 * 1024, 4, dl.DL_KV_LAYER, None, None)   # fake, aligned
+    d = dl.LayerDims(256, 4, 2, 64, 688, 16, 1e-5, bf)
+    w = dl.LayerWeights(*[256 * (i + 1) for i in range(9)])
+    cr, dr, wr = ctypes.byref(c), ctypes.byref(d), ctypes.byref(w)
+    empty = {
+        "qkv_rope": L.dl_qkv_rope(None, None, None, None, None, None, 16, None, None, None, 0,
+                                  256, 4, 2, 64, bf, None, 0, None),
+        "qkv_rope_cache": L.dl_qkv_rope_cache(None, None, None, None, None, None, 16, None, None,
+                                              None, None, None, 4, cr, 0, 256, 4, 2, 64, 16, bf,
+                                              None, 0, None),
+        "reshape_and_cache": L.dl_reshape_and_cache(None, None, None, None, None, 4, cr, 0, 2, 64,
+                                                    16, bf, None),
+        "linear": L.dl_linear(None, None, None, 0, 256, 64, bf, None, 0, None),
+        "gate_up_silu": L.dl_gate_up_silu(None, None, None, None, 0, 256, 512, bf, None, 0, None),
+        "down_residual": L.dl_down_residual(None, None, None, None, 0, 256, 512, bf, None, 0,
+                                            None),
+        "ffn_swiglu": L.dl_ffn_swiglu(None, None, None, None, None, None, 0, 256, 512, bf, None,
+                                      0, None),
+        "attn_prefill B=0": L.dl_attn_prefill(None, None, None, None, 0, 0, 0, 4, 2, 64, 0.0,
+                                              None, bf, None),
+        "attn_prefill T=0": L.dl_attn_prefill(None, None, None, None, 2, 0, 0, 4, 2, 64, 0.0,
+                                              None, bf, None),
+        "attn_decode_paged": L.dl_attn_decode_paged(None, cr, None, 4, None, 64, 0, 4, 2, 64, 16,
+                                                    0.0, None, bf, None, 0, None),
+        "attn_decode_paged_noalloc": L.dl_attn_decode_paged_noalloc(None, cr, None, 4, None, 64,
+                                                                    0, 4, 2, 64, 16, 0.0, None,
+                                                                    bf, None),
+        "attn_paged_qlens": L.dl_attn_paged_qlens(None, cr, None, 4, None, None, 0, 0, 0, 64, 4, 2,
+                                                  64, 16, 0.0, None, bf, None, 0, None),
+        "layer_prefill": L.dl_layer_prefill(dr, wr, None, 64, None, None, None, None, None, 0, 0, 0,
+                                            cr, None, 4, dl.DL_FUSED, None, 0, None),
+        "layer_decode": L.dl_layer_decode(dr, wr, None, 64, None, None, None, None, 64, 0, cr, None,
+                                          4, dl.DL_FUSED, None, 0, None),
+        "layer_decode_qlens": L.dl_layer_decode_qlens(dr, wr, None, 64, None, None, None, None,
+                                                      None, None, 0, 0, 0, 64, cr, None, 4,
+                                                      dl.DL_FUSED, None, 0, None),
+    }
+    assert all(s == 0 for s in empty.values()), {k: s for k, s in empty.items() if s}
+    negative = {
+        "linear": L.dl_linear(None, None, None, -1, 256, 64, bf, None, 0, None),
+        "gate_up_silu": L.dl_gate_up_silu(None, None, None, None, -3, 256, 512, bf, None, 0, None),
+        "rmsnorm": L.dl_rmsnorm_residual(None, dl.DL_F32, None, None, None, None, -1, 256, 1e-5,
+                                         dl.DL_F32, None),
+        "attn_prefill": L.dl_attn_prefill(None, None, None, None, -1, 0, 0, 4, 2, 64, 0.0, None,
+                                          bf, None),
+        "attn_decode_paged": L.dl_attn_decode_paged(None, cr, None, 4, None, 64, -2, 4, 2, 64, 16,
+                                                    0.0, None, bf, None, 0, None),
+        "layer_prefill": L.dl_layer_prefill(dr, wr, None, 64, None, None, None, None, None, 1, -5,
+                                            0, cr, None, 4, dl.DL_FUSED, None, 0, None),
+        "layer_decode": L.dl_layer_decode(dr, wr, None, 64, None, None, None, None, 64, -1, cr,
+                                          None, 4, dl.DL_FUSED, None, 0, None),
+    }
+    assert all(s == 1 for s in negative.values()), negative    # DL_ERR_INVALID_ARG
