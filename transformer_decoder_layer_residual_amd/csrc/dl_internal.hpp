@@ -35,8 +35,9 @@ enum GemmCfg : int {
 struct GemmPlan {
   int cfg;
   int BM, BN;
-  int splits;        // number of K slices (1 = direct epilogue)
-  int k_per_split;   // multiple of the K tile
+  int splits;        // number of K slices (1 = direct epilogue); kCfgSkinny:
+                     // most workgroups sharing one column tile (fp32 slabs)
+  int k_per_split;   // multiple of the K tile; kCfgSkinny: K stages per tile
   size_t ws_bytes;   // fp32 partials when splits > 1
   int mixed_tn;      // > 0: 256-row tiles for the first mixed_tn N-tiles, 128-row after
 };
