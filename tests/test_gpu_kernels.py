@@ -117,9 +117,11 @@ def test_linear_random_bf16(M, N, K):
 # Decode batches of at most 16 rows against N >= 4096 go to the row-block
 # weight stream (16 weight rows per workgroup, K split over its waves): K
 # ranges that leave each wave a ragged tail of k groups, and each row length
-# class with its own unroll/wave choice (K < 8192, 8192, >= 14336).
+# class with its own unroll/wave choice (K < 8192, 8192, >= 14336); long rows
+# with at least 512 blocks take two blocks per workgroup, also with an odd
+# block count (the last workgroup's second block missing).
 ROW16_SHAPES = [(1, 4096, 4096), (13, 4096, 4128), (16, 4352, 8192), (3, 4096, 14336),
-                (9, 8192, 14368)]
+                (9, 8192, 14368), (5, 8208, 14336)]
 
 
 @pytest.mark.parametrize("M,N,K", ROW16_SHAPES)
@@ -130,6 +132,21 @@ def test_linear_row_block_stream_exact(M, N, K):
     out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
     dl.dl_linear(dev_bf16(x), dev_bf16(w), out)
     assert np.array_equal(host(out), bf(oracle.linear(x, w)))  # |sum| < 2^24: exact
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_down_residual_two_block_row_stream(T):
+    """The 70B-shaped down projection (N 8192, K 28672: 512 row blocks, two per
+    workgroup) through the residual epilogue."""
+    print(f"row16 two-block down T={T}", flush=True)
+    H, I = 8192, 28672
+    a = rnd(T, I)
+    wd = rnd(H, I, scale=0.02)
+    r = R.standard_normal((T, H)).astype(np.float32)
+    y = torch.empty(T, H, device=DEV)
+    dl.dl_down_residual(dev_bf16(a), dev_bf16(wd), y, residual=dev_f32(r))
+    assert_f32_close(host(y), oracle.down_residual(a, wd, r), "down+resid", max_abs=3e-2,
+                     rel=1e-2)
 
 
 @pytest.mark.parametrize("T", [1, 5, 16])

@@ -226,20 +226,30 @@ static hipError_t launch_skinny(const bf16* x, int M, int K, const Map& map, con
   return hipGetLastError();
 }
 
-// Unroll depth and waves per workgroup of the row-block stream, measured on
-// the 8B- and 70B-shaped decode projections: long rows (K >= 14336, the down
-// projections) stream best as 4 waves 8 groups deep, K = 8192 as 8 waves 16
-// deep, shorter rows as 4 waves 16 deep.
+// Unroll depth, waves and 16-row blocks per workgroup of the row-block
+// stream, measured on the 8B- and 70B-shaped decode projections: long rows
+// (K >= 14336, the down projections) stream best as 4 waves 8 groups deep, K =
+// 8192 as 8 waves 16 deep, shorter rows as 4 waves 16 deep.  Two blocks per
+// workgroup (each activation fragment feeding both) paid only for long rows
+// with at least 512 blocks -- the 70B down projection, 86.3 -> 82.2 us with a
+// cache flush before each launch, as 4 waves 4 groups deep; on the 8B gate/up
+// and every K = 8192 projection they were 2-12% slower.
 template <class Map, class Epi>
 static hipError_t launch_row16(const bf16* x, int M, int K, const Map& map, const Epi& epi, int NL,
                                hipStream_t st) {
-  const dim3 grid(NL / 16);
-  if (K >= 14336)
-    hipLaunchKernelGGL((gemm_row16_kernel<8, 4, Map, Epi>), grid, dim3(256), 0, st, x, M, K, map, epi);
+  const int nblk = NL / 16;
+  if (K >= 14336 && nblk >= 512)
+    hipLaunchKernelGGL((gemm_row16_kernel<4, 4, 2, Map, Epi>), dim3((nblk + 1) / 2), dim3(256), 0,
+                       st, x, M, K, map, epi, nblk);
+  else if (K >= 14336)
+    hipLaunchKernelGGL((gemm_row16_kernel<8, 4, 1, Map, Epi>), dim3(nblk), dim3(256), 0, st, x, M,
+                       K, map, epi, nblk);
   else if (K >= 8192)
-    hipLaunchKernelGGL((gemm_row16_kernel<16, 8, Map, Epi>), grid, dim3(512), 0, st, x, M, K, map, epi);
+    hipLaunchKernelGGL((gemm_row16_kernel<16, 8, 1, Map, Epi>), dim3(nblk), dim3(512), 0, st, x,
+                       M, K, map, epi, nblk);
   else
-    hipLaunchKernelGGL((gemm_row16_kernel<16, 4, Map, Epi>), grid, dim3(256), 0, st, x, M, K, map, epi);
+    hipLaunchKernelGGL((gemm_row16_kernel<16, 4, 1, Map, Epi>), dim3(nblk), dim3(256), 0, st, x,
+                       M, K, map, epi, nblk);
   return hipGetLastError();
 }
 

@@ -243,44 +243,55 @@ inline int sk_max_contributors(int tiles_n, int S, int W) {
 // Row-block weight stream for at most 16 activation rows (decode batches of
 // a few sequences), with no partial sums in memory.
 //
-// One workgroup owns 16 weight rows: 8 pair-columns and their 8 partners (P =
-// 8), so N / 16 workgroups cover the output -- 256 and more for every decode
-// projection of the 8B- and 70B-shaped layers.  Its NW waves split K into
-// contiguous ranges; each wave streams its range in 32-wide k groups, loading
-// the 16 x 32 weight block and the 16 x 32 activation block straight into the
-// 16x16x32 MFMA operand layout (lane l: row l % 16, k = 8 * (l / 16) .. + 7),
-// U groups ahead in registers, and accumulates into two alternating
-// accumulators.  The waves' 16 x 16 results are merged through LDS in wave
-// order (fixed, so results do not depend on timing); lane l < 32 of wave 0
-// then holds weight rows 4 (l / 16) .. + 3 for activation row l % 16, and lane
-// l + 32 holds their partners, fetched with one cross-lane swap.  Against the
+// A 16-row block is 8 pair-columns and their 8 partners (P = 8), so N / 16
+// blocks cover the output -- 256 and more for every decode projection of the
+// 8B- and 70B-shaped layers.  A workgroup owns R consecutive blocks (nblk in
+// all; a missing last block is streamed from valid rows and never stored).
+// Its NW waves split K into contiguous ranges; each wave streams its range in
+// 32-wide k groups, loading the R 16 x 32 weight blocks and the 16 x 32
+// activation block straight into the 16x16x32 MFMA operand layout (lane l:
+// row l % 16, k = 8 * (l / 16) .. + 7), U groups ahead in registers, and
+// accumulates each block into two alternating accumulators (even and odd k
+// groups).  With R = 2 every activation fragment feeds two blocks, which
+// halves the activation reads from L2 and doubles the bytes a workgroup
+// streams.  The waves' 16 x 16 results are merged through LDS in wave order
+// (fixed, so results do not depend on timing); wave b then holds block b:
+// lane l < 32 has weight rows 4 (l / 16) .. + 3 for activation row l % 16, and
+// lane l + 32 their partners, fetched with one cross-lane swap.  Against the
 // 128-row stream this removes the fp32 partial round trip and the separate
 // reduction launch (the 8B down projection: 25.9 against 34.0 us with its
 // reduction).  Activation rows past M read row M - 1 and are never stored.
 // ---------------------------------------------------------------------------
-template <int U, int NW, class Map, class Epi>
+template <int U, int NW, int R, class Map, class Epi>
 __global__ void __launch_bounds__(NW * 64)
-gemm_row16_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi) {
-  __shared__ f32x4 red[NW][64];
-  const int tn = blockIdx.x;
+gemm_row16_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int nblk) {
+  static_assert(R >= 1 && R <= NW && U % 2 == 0, "row-block shape");
+  __shared__ f32x4 red[R][NW][64];
+  const int tn0 = blockIdx.x * R;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int r = lane & 15, kq = 8 * (lane >> 4);
-  const bf16* wrow = map.row(tn, r);
-  if (!wrow) wrow = X;                        // rows past a ragged N: never stored
-  const bf16* xrow = X + (int64_t)min(r, M - 1) * K;
   const int G = K / 32;                       // 32-wide k groups (K % 32 == 0)
   const int gpw = (G + NW - 1) / NW;          // groups per wave; the last may get fewer
   const int g0 = wave * gpw;
   const int ng = max(0, min(gpw, G - g0));
   const int nfull = ng / U;                   // whole chunks of U groups
-  const bf16* wp = wrow + (int64_t)g0 * 32 + kq;
-  const bf16* xp = xrow + (int64_t)g0 * 32 + kq;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  u32x4 wb[U], xb[U];
+  const bf16* wp[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    const bf16* wrow = tn0 + b < nblk ? map.row(tn0 + b, r) : nullptr;
+    if (!wrow) wrow = X;                      // rows past a ragged N: never stored
+    wp[b] = wrow + (int64_t)g0 * 32 + kq;
+  }
+  const bf16* xp = X + (int64_t)min(r, M - 1) * K + (int64_t)g0 * 32 + kq;
+  f32x4 acc[R][2];
+#pragma unroll
+  for (int b = 0; b < R; ++b) acc[b][0] = acc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 wb[U][R], xb[U];
   if (nfull > 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      wb[u] = ld16(wp + 32 * u);
+#pragma unroll
+      for (int b = 0; b < R; ++b) wb[u][b] = ld16(wp[b] + 32 * u);
       xb[u] = ld16(xp + 32 * u);
     }
     for (int c = 0; c < nfull; ++c) {
@@ -289,31 +300,37 @@ gemm_row16_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi) {
       const int cn = min(c + 1, nfull - 1);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, wb[u]);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, xb[u]);
-        if (u & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc1, 0, 0, 0);
-        else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc0, 0, 0, 0);
-        wb[u] = ld16(wp + 32 * (cn * U + u));
+        const bf16x8 x = __builtin_bit_cast(bf16x8, xb[u]);
+#pragma unroll
+        for (int b = 0; b < R; ++b)
+          acc[b][u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, wb[u][b]), x, acc[b][u & 1], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < R; ++b) wb[u][b] = ld16(wp[b] + 32 * (cn * U + u));
         xb[u] = ld16(xp + 32 * (cn * U + u));
       }
     }
   }
   for (int g = nfull * U; g < ng; ++g) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(wp + 32 * g));
-    const bf16x8 b = __builtin_bit_cast(bf16x8, ld16(xp + 32 * g));
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc0, 0, 0, 0);
-  }
-  red[wave][lane] = acc0 + acc1;
-  __syncthreads();
-  if (wave != 0) return;
-  f32x4 s = red[0][lane];
+    const bf16x8 x = __builtin_bit_cast(bf16x8, ld16(xp + 32 * g));
 #pragma unroll
-  for (int w = 1; w < NW; ++w) s += red[w][lane];
+    for (int b = 0; b < R; ++b)
+      acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, ld16(wp[b] + 32 * g)), x, acc[b][0], 0, 0, 0);
+  }
+#pragma unroll
+  for (int b = 0; b < R; ++b) red[b][wave][lane] = acc[b][0] + acc[b][1];
+  __syncthreads();
+  if (wave >= R || tn0 + wave >= nblk) return;
+  const int b = wave;
+  f32x4 s = red[b][0][lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) s += red[b][w][lane];
   f32x4 pr;
 #pragma unroll
   for (int e = 0; e < 4; ++e) pr[e] = __shfl_xor(s[e], 32, 64);
   const int m = lane & 15;
-  if (lane < 32 && m < M) epi(m, tn, 4 * (lane >> 4), s, pr);
+  if (lane < 32 && m < M) epi(m, tn0 + b, 4 * (lane >> 4), s, pr);
 }
 
 }  // namespace dl
