@@ -2,6 +2,8 @@
 
 Each csrc/*.hip file is compiled to an object in parallel with hipcc and the
 objects are linked into transformer_decoder_layer_residual_amd/libdl_layer.so.
+The measurement kernels of csrc/probe/ (achievable read, copy and MFMA rates,
+used only by the profiling tool) become libdl_probe.so beside it.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "libdl_layer.so")
+PROBE_LIB = os.path.join(PKG, "libdl_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("DL_OFFLOAD_ARCH", "gfx950")
@@ -59,7 +62,24 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile csrc/probe/*.hip into libdl_probe.so (measurement kernels)."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *CFLAGS, "-shared", "-o", tmp, *srcs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        err = "\n".join(l for l in (r.stderr or "").splitlines()
+                        if "is not a recognized feature for this target" not in l)
+        raise RuntimeError("probe library build failed:\n" + err)
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}", file=sys.stderr)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -17,6 +17,10 @@ Commands (run from the repository root; outputs go where --out says):
   python -m transformer_decoder_layer_residual_amd.profiling bytes-summary \
       --fused-fetch D --fused-write D --unfused-fetch D --unfused-write D \
       --calls 3 --out profiles/NAME.md
+  python -m transformer_decoder_layer_residual_amd.profiling ceilings \
+      --out profiles/NAME.md                  (achievable rates of the box)
+  python -m transformer_decoder_layer_residual_amd.profiling gemm8192 --calls 3
+                                              (run under rocprofv3 --pmc)
 """
 from __future__ import annotations
 
@@ -226,6 +230,143 @@ def run_layer(mode: str, calls: int, config: int = 2):
     print(f"ran {calls} {mode} prefill layers", file=sys.stderr)
 
 
+def _probe_lib():
+    import ctypes
+    path = os.path.join(PKG, "libdl_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "transformer_decoder_layer_residual_amd.build.build()")
+    L = ctypes.CDLL(path)
+    L.dlp_sink_bytes.restype = ctypes.c_size_t
+    L.dlp_mfma_flops.restype = ctypes.c_double
+    L.dlp_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    for n, args in (("dlp_stream_read", [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+                    ("dlp_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
+                    ("dlp_mfma_loop", [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p])):
+        getattr(L, n).restype = ctypes.c_int
+        getattr(L, n).argtypes = args
+    return L
+
+
+def _time_ms(fn, n=10, warm=3):
+    """Mean milliseconds of n back-to-back calls of fn, HIP events on the
+    current stream, after warm untimed calls."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def ceilings(out: str, cmd: str):
+    """Achievable rates of this MI355X: a streaming read and a copy of
+    buffers far larger than the 256 MB MALL, register-only MFMA loops, and a
+    bf16 8192^3 product through this library and through torch (hipBLASLt)."""
+    import torch
+
+    from . import binding as dl
+    L = _probe_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.empty(L.dlp_sink_bytes(), dtype=torch.uint8, device="cuda:0")
+    rows = []
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+
+    def chk(r):
+        if r != 0:
+            raise RuntimeError(f"probe call failed ({r})")
+    best = None
+    for bpc in (1, 2, 4, 8, 16):
+        for unr in (4, 8, 16):
+            ms = _time_ms(lambda: chk(L.dlp_stream_read(buf.data_ptr(), n, sink.data_ptr(), bpc,
+                                                        unr, st)), n=5, warm=1)
+            if best is None or ms < best[0]:
+                best = (ms, bpc, unr)
+    ms, bpc, unr = best
+    rows.append((f"streaming read, 4 GiB, 16-byte loads (best of 1-16 workgroups per CU x 4-16 "
+                 f"loads in flight per lane: {bpc} x {unr})", f"{n / ms / 1e6:,.0f} GB/s",
+                 f"{n / ms / 1e6 / 8000:.2f}", "of 8 TB/s"))
+    half = n // 2
+    src, dst = buf[:half], buf[half:]
+    ms = _time_ms(lambda: chk(L.dlp_copy(src.data_ptr(), dst.data_ptr(), half, st)))
+    rows.append(("copy, 2 GiB read + 2 GiB written", f"{2 * half / ms / 1e6:,.0f} GB/s",
+                 f"{2 * half / ms / 1e6 / 8000:.2f}", "of 8 TB/s"))
+    del buf, src, dst
+    for kind, name, waves in ((0, "v_mfma_f32_32x32x16_bf16", (1, 2, 3)),
+                              (1, "v_mfma_f32_16x16x32_bf16", (1, 2, 4))):
+        iters, best = 2000, None
+        for wv in waves:
+            ms = _time_ms(lambda: chk(L.dlp_mfma_loop(kind, iters, wv, sink.data_ptr(), st)), n=5,
+                          warm=1)
+            fl = L.dlp_mfma_flops(kind, iters, wv)
+            if best is None or fl / ms > best[0]:
+                best = (fl / ms, wv)
+        rate, wv = best
+        rows.append((f"{name}, registers only, 8 chains per wave (best of {list(waves)} waves per "
+                     f"SIMD: {wv})", f"{rate / 1e9:,.0f} TFLOP/s", f"{rate / 1e9 / 2500:.2f}",
+                     "of 2.5 PFLOP/s"))
+    N = 8192
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(0)
+    x = torch.randn(N, N, device="cuda:0", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, N, device="cuda:0", generator=g) * 0.02).to(torch.bfloat16)
+    y = torch.empty(N, N, dtype=torch.bfloat16, device="cuda:0")
+    fl = 2.0 * N ** 3
+    ms = _time_ms(lambda: dl.dl_linear(x, w, y))
+    rows.append(("bf16 8192^3 product, this library (dl_linear)", f"{fl / ms / 1e9:,.0f} TFLOP/s",
+                 f"{fl / ms / 1e9 / 2500:.2f}", "of 2.5 PFLOP/s"))
+    ms = _time_ms(lambda: torch.mm(x, w.t(), out=y))
+    rows.append(("bf16 8192^3 product, torch.mm (hipBLASLt)", f"{fl / ms / 1e9:,.0f} TFLOP/s",
+                 f"{fl / ms / 1e9 / 2500:.2f}", "of 2.5 PFLOP/s"))
+    lines = ["# Achievable rates of the MI355X (measurement kernels and an 8192^3 product)", "",
+             "Streaming read and copy: grid-stride kernels of 16-byte accesses over buffers 16x "
+             "the 256 MB MALL (the read at 1-16 workgroups of 256 threads per CU and 4-16 "
+             "independent loads per lane per trip, the best shown; the copy at 8 workgroups per "
+             "CU), mean of back-to-back launches.  MFMA: each wave issues 8 independent "
+             "accumulator chains on register operands, one workgroup per CU with 1-4 waves per "
+             "SIMD, the best shown.  Products: y = x w^T, x and w 8192 x "
+             "8192 bf16 (x ~ N(0,1), w ~ N(0,0.02^2)), mean of 10 launches.  The layer's "
+             "fractions of peak are read against these rates.", "",
+             "Command (repository root on the MI355X box):", "", "```", cmd, "```", "",
+             "| what | rate | fraction | of |", "|---|---:|---:|---|"]
+    for r in rows:
+        lines.append("| " + " | ".join(r) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[-len(rows) - 2:]))
+
+
+def gemm8192(calls: int):
+    """The bf16 8192^3 product through this library and through torch.mm
+    (hipBLASLt), `calls` times each, for counters."""
+    import torch
+
+    from . import binding as dl
+    N = 8192
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(0)
+    x = torch.randn(N, N, device="cuda:0", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, N, device="cuda:0", generator=g) * 0.02).to(torch.bfloat16)
+    y = torch.empty(N, N, dtype=torch.bfloat16, device="cuda:0")
+    torch.cuda.synchronize()
+    for _ in range(calls):
+        dl.dl_linear(x, w, y)
+    for _ in range(calls):
+        torch.mm(x, w.t(), out=y)
+    torch.cuda.synchronize()
+    print(f"ran {calls} products each way", file=sys.stderr)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="sub", required=True)
@@ -247,6 +388,10 @@ def main(argv=None):
     e.add_argument("--out", required=True)
     e.add_argument("--cmd", required=True)
     e.add_argument("--title", default="Counters per kernel")
+    f_ = sub.add_parser("ceilings")
+    f_.add_argument("--out", required=True)
+    g_ = sub.add_parser("gemm8192")
+    g_.add_argument("--calls", type=int, default=3)
     d = sub.add_parser("bytes-summary")
     for k in ("fused-fetch", "fused-write", "unfused-fetch", "unfused-write"):
         d.add_argument("--" + k, required=True)
@@ -264,6 +409,11 @@ def main(argv=None):
         print(json.dumps(t, indent=1))
     elif args.sub == "counters":
         counters_md(args.dirs, args.out, args.cmd, args.title)
+    elif args.sub == "ceilings":
+        ceilings(args.out, "python -m transformer_decoder_layer_residual_amd.profiling ceilings "
+                 f"--out {args.out}")
+    elif args.sub == "gemm8192":
+        gemm8192(args.calls)
     elif args.sub == "layer-bytes":
         run_layer(args.mode, args.calls, args.config)
     else:
