@@ -2,6 +2,8 @@
 // ping-pong kernel (K % 64 == 0) and the double-buffered 256x256 kernel.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_epi.hpp"
 
 namespace dl {
@@ -142,8 +144,9 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 // Ping-pong prefill tile: BM x 256 x 64, 8 waves in two groups of 4.
 //
 // Group g computes output rows [128 g, 128 g + 128) of the tile; each wave a
-// 64 x 128 block (2 x 4 blocks of 32 x 32, v_mfma_f32_32x32x16_bf16).  The
-// groups run one barrier phase apart: while one group issues its 32 MFMAs for
+// 64 x 128 block (4 x 8 blocks of 16 x 16, v_mfma_f32_16x16x32_bf16; or 2 x 4
+// blocks of 32 x 32 with v_mfma_f32_32x32x16_bf16, see kPPMfma16).  The
+// groups run one barrier phase apart: while one group issues its MFMAs for
 // k-tile t, the other reads all its MFMA fragments of the next k-tile from
 // LDS and issues global->LDS loads, so each SIMD (one wave of each group)
 // always has a wave feeding the matrix pipe.
@@ -154,7 +157,7 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 // phase 2t+4, before either group reads it.
 // Global->LDS loads go straight to LDS (global_load_lds_dwordx4, 1 KB per wave
 // instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
-// so the 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
+// so the 16- and 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
 // ---------------------------------------------------------------------------
 // Chunk swizzles (16-byte chunks within an LDS row); both keep the 32-row
 // fragment reads conflict-free for 32- and 64-bank LDS models.
@@ -184,6 +187,16 @@ struct PPGeom {
   static constexpr int SMEM = MAIN > OUT ? MAIN : OUT;
 };
 
+// Matrix instruction of the ping-pong tile: false = v_mfma_f32_32x32x16_bf16
+// (32 x 32 output blocks, k16 steps), true = v_mfma_f32_16x16x32_bf16 (16 x 16
+// blocks, k32 steps).  Both read the same LDS bytes per product term from the
+// same swizzled rows: every fragment row of a lane is its lane row plus a
+// multiple of 16, and the chunk swizzle depends on a row's low four bits only.
+// The 16x16x32 form is the faster one on the MI355X: register-only loops
+// sustain 2.14 against 1.92 PFLOP/s, and the 7B prefill projections ran 3-11%
+// faster with it (gate/up + SiLU.mul 290-297 against 326-333 us back to back).
+constexpr bool kPPMfma16 = true;
+
 // One BM x 256 output tile: tile `bid` of a tiles_m x tiles_n grid whose
 // N-tiles start at tn0 (so a launch may cover a range of N with one shape);
 // k-tiles kt0 .. kt0 + nkt - 1 are summed (the whole K unless split).
@@ -199,8 +212,10 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   constexpr int STAGE = Geo::STAGE;
   constexpr int NSTAGE = Geo::NSTAGE;
   constexpr int LA = NSTAGE - 1;                    // k-tiles loaded ahead
-  constexpr int MS = BM / 128, NS = 4;              // 32x32 blocks per wave
-  constexpr int KS = BK / 16;                       // k16 steps per tile
+  constexpr bool F16 = kPPMfma16;
+  constexpr int MB = F16 ? 16 : 32;                 // rows of an MFMA output block
+  constexpr int MS = BM / 4 / MB, NS = 128 / MB;    // output blocks per wave (rows, columns)
+  constexpr int KS = BK / (F16 ? 32 : 16);          // MFMA k steps per tile
   constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
   constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
   constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
@@ -220,7 +235,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases in SGPRs
   const int grp = wave >> 2, wig = wave & 3;        // group, wave in group
   const int wm = wig >> 1, wn = wig & 1;
-  const int fr = lane & 31, fh = lane >> 5;
+  const int fr = lane & (MB - 1), fh = lane / MB;   // fragment row, k-chunk group
 
   // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
   // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), RPI rows per instruction.
@@ -256,15 +271,18 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     else wait_vmcnt<0>();
   };
 
-  // ---- fragments (all k16 steps of a k-tile)
+  // ---- fragments (all k steps of a k-tile)
   bf16x8 fx[KS][MS], fw[KS][NS];
-  // Every fragment row a lane reads is fr plus a multiple of 32, so its chunk
-  // swizzle is pp_swz(fr) for all of them: a lane's offset within a 32-row
-  // block at k16 step ks is one of KS values, the rest is wave-uniform.
+  // Every fragment row a lane reads is fr plus a multiple of MB (16 or 32),
+  // so its chunk swizzle is pp_swz(fr) for all of them: a lane's offset within
+  // a block at k step ks is one of KS values, the rest is wave-uniform.  A k
+  // step spans 2 chunks (k16: the two lane halves) or 4 (k32: four lane
+  // groups of 16).
+  constexpr int CPS = F16 ? 4 : 2;                  // 16-byte chunks per k step
   int lane_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    lane_off[ks] = fr * ROWB + (((ks * 2 + fh) ^ pp_swz<BK>(fr)) << 4);
+    lane_off[ks] = fr * ROWB + (((ks * CPS + fh) ^ pp_swz<BK>(fr)) << 4);
   auto read_frags = [&](int kt) {
     const unsigned char* xs = smem + (kt % NSTAGE) * STAGE + (grp * GR + wm * WR) * ROWB;
     const unsigned char* ws = smem + (kt % NSTAGE) * STAGE + BM * ROWB;
@@ -276,28 +294,37 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
       asm volatile("" : "+v"(lo));
 #pragma unroll
       for (int i = 0; i < MS; ++i)
-        fx[ks][i] = *reinterpret_cast<const bf16x8*>(xs + i * 32 * ROWB + lo);
+        fx[ks][i] = *reinterpret_cast<const bf16x8*>(xs + i * MB * ROWB + lo);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const int blk = (s < 2) ? 2 * wn + s : 4 + 2 * wn + (s - 2);  // first half, partners
-        fw[ks][s] = *reinterpret_cast<const bf16x8*>(ws + blk * 32 * ROWB + lo);
+        // first half (blocks of this wave's 64 columns), then their partners
+        const int blk = (s < NS / 2) ? wn * (NS / 2) + s : NS + wn * (NS / 2) + (s - NS / 2);
+        fw[ks][s] = *reinterpret_cast<const bf16x8*>(ws + blk * MB * ROWB + lo);
       }
     }
   };
-  f32x16 acc[MS][NS];
+  using Acc = typename std::conditional<F16, f32x4, f32x16>::type;
+  constexpr int AE = F16 ? 4 : 16;                  // accumulator registers per block
+  Acc acc[MS][NS];
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][s][e] = 0.f;
+      for (int e = 0; e < AE; ++e) acc[i][s][e] = 0.f;
   auto compute = [&]() {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < MS; ++i)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc[i][s] = mfma_32x32x16(fw[ks][s], fx[ks][i], acc[i][s]);
+        for (int s = 0; s < NS; ++s) {
+          if constexpr (F16)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[ks][s], fx[ks][i], acc[i][s], 0,
+                                                                0, 0);
+          else
+            acc[i][s] = mfma_32x32x16(fw[ks][s], fx[ks][i], acc[i][s]);
+        }
   };
 #define DL_PHASE_END()                                     \
   do {                                                     \
@@ -336,8 +363,9 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   // time: the group's waves park their fp32 accumulators row-major in LDS,
   // then all 512 threads take 8-column chunks in row order and run the
   // epilogue on them, so the 16 chunks of an output row (and of its partner
-  // half) leave as whole 128-byte lines.  Lane l holds column m = ... + l % 32
-  // and rows n = 8 q + 4 (l / 32) + j of each 32x32 block.
+  // half) leave as whole 128-byte lines.  Lane l holds activation row l % 32
+  // and weight rows 8 q + 4 (l / 32) + j of each 32x32 block, or activation
+  // row l % 16 and weight rows 4 (l / 16) + j of each 16x16 block.
   float* stage = reinterpret_cast<float*>(smem);
   __syncthreads();                                  // every main-loop LDS read is done
 #pragma unroll
@@ -345,12 +373,12 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     if (grp == pass) {
 #pragma unroll
       for (int i = 0; i < MS; ++i) {
-        const int r = wm * WR + i * 32 + fr;          // row within the group
+        const int r = wm * WR + i * MB + fr;          // row within the group
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const int col = (s < 2 ? 0 : BN / 2) + (2 * wn + (s & 1)) * 32 + 4 * fh;
+          const int col = (s < NS / 2 ? 0 : BN / 2) + (wn * (NS / 2) + s % (NS / 2)) * MB + 4 * fh;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < AE / 4; ++q)
             *reinterpret_cast<f32x4*>(stage + r * OPITCH + col + 8 * q) =
                 f32x4{acc[i][s][4 * q], acc[i][s][4 * q + 1], acc[i][s][4 * q + 2],
                       acc[i][s][4 * q + 3]};
