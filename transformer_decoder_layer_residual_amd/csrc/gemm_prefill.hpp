@@ -10,8 +10,9 @@ namespace dl {
 
 // ---------------------------------------------------------------------------
 // Large prefill tile: 256 x 256 x 64, 8 waves (2 x 4), wave tile 128 x 64 made
-// of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16 (the bf16 MFMA shape that
-// sustains close to the chip's peak; 16x16x32 issues at well under half of it).
+// of 32 x 32 blocks on v_mfma_f32_32x32x16_bf16.  It serves only K that is not
+// a multiple of 64 (every benchmarked projection takes the ping-pong tile
+// below, which runs faster on v_mfma_f32_16x16x32_bf16).
 // Loads are branch-free (rows past M or N are clamped to valid memory; their
 // results are never stored) and only the last K tile, when K is not a
 // multiple of 64, takes the zero-filling path.  MFMA fragments of the next
