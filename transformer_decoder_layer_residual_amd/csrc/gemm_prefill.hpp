@@ -160,12 +160,26 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 // instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
 // so the 16- and 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
 // ---------------------------------------------------------------------------
-// Chunk swizzles (16-byte chunks within an LDS row); both keep the 32-row
-// fragment reads conflict-free for 32- and 64-bank LDS models.
-template <int BK>
+// Chunk swizzles (16-byte chunks within an LDS row), functions of a row's low
+// four bits.  32x32x16 fragments (lane l: row l % 32, chunk c + l / 32): the
+// rows of each 8- or 16-lane group fall on distinct banks.  16x16x32
+// fragments (lane l: row l % 16, chunk c + l / 16) are also read with lanes l
+// and l + 32 -- the same row, chunks c and c + 2 -- in one LDS cycle, so the
+// rows that share a bank half (even or odd rows) must take XOR values from
+// distinct cosets of {0, 2}, and the 16 rows of a block distinct values
+// (with the 32x32 swizzle half of those reads conflicted: LDS bank-conflict
+// cycles at half the LDS active cycles).
+template <int BK, bool F16>
 __device__ __forceinline__ int pp_swz(int r) {
-  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);   // 8 chunks per row
-  else return ((r >> 1) ^ (r >> 3)) & 3;                      // 4 chunks per row
+  if constexpr (F16) {
+    if constexpr (BK == 64)
+      return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+    else
+      return ((r >> 2) & 1) | (((r >> 3) & 1) << 1);
+  } else {
+    if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);   // 8 chunks per row
+    else return ((r >> 1) ^ (r >> 3)) & 3;                      // 4 chunks per row
+  }
 }
 
 template <int N>
@@ -244,7 +258,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
 #pragma unroll
   for (int i = 0; i < LI; ++i) {
     const int row = wave * RPW + i * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ pp_swz<BK>(row);   // logical chunk this lane fetches
+    const int c = (lane % CPR) ^ pp_swz<BK, F16>(row);  // logical chunk this lane fetches
     const bf16* base;
     if (row < BM) {
       base = X + (int64_t)min(tm * BM + row, M - 1) * K;   // rows >= M: valid, never stored
@@ -283,7 +297,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   int lane_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    lane_off[ks] = fr * ROWB + (((ks * CPS + fh) ^ pp_swz<BK>(fr)) << 4);
+    lane_off[ks] = fr * ROWB + (((ks * CPS + fh) ^ pp_swz<BK, F16>(fr)) << 4);
   auto read_frags = [&](int kt) {
     const unsigned char* xs = smem + (kt % NSTAGE) * STAGE + (grp * GR + wm * WR) * ROWB;
     const unsigned char* ws = smem + (kt % NSTAGE) * STAGE + BM * ROWB;

@@ -53,9 +53,10 @@ KERNELS = {
                                     r"|gemm_pp_kernel<256, 64, dl::MapSwiglu",
                                     ("gemm_prefill.hpp", "gemm_epi.hpp", "dl_common.hpp"),
                                     2800 * 512),
-    # the 70B-shaped decode gate/up (K = 8192: 16-deep, 8 waves; B4 and B1 calls)
-    "gemm_gateup_silu_decode_70b": (r"gemm_row16_kernelILi16ELi8ENS_9MapSwiglu"
-                                    r"|gemm_row16_kernel<16, 8, dl::MapSwiglu",
+    # the 70B-shaped decode gate/up (K = 8192: 16-deep, 8 waves, one row block
+    # per workgroup; B4 and B1 calls)
+    "gemm_gateup_silu_decode_70b": (r"gemm_row16_kernelILi16ELi8ELi1ENS_9MapSwiglu"
+                                    r"|gemm_row16_kernel<16, 8, 1, dl::MapSwiglu",
                                     ("gemm_decode.hpp", "gemm_epi.hpp", "dl_common.hpp")),
     "attn_decode_paged": (r"attn_decode_kernelIDF16bDF16bLi128ELi1E"
                           r"|attn_decode_kernel<bool _Accum, bool _Accum, 128, 1,",
