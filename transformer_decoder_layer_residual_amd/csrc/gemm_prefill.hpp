@@ -190,7 +190,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // LDS footprint of one tile shape: the k-tile stages, or the fp32 staging of
 // one group's output rows, whichever is larger.  (A third stage for the
 // weight half of 256-row tiles, which fits the 160 KB exactly, measured no
-// faster: 328.6 against 322.9 us for the 7B gate/up product.)
+// faster: 328.6 against 322.9 us for the 7B gate/up product on the 32x32x16
+// form of the tile.)
 template <int BM, int BK>
 struct PPGeom {
   static constexpr int BN = 256;
@@ -205,8 +206,9 @@ struct PPGeom {
 // Matrix instruction of the ping-pong tile: false = v_mfma_f32_32x32x16_bf16
 // (32 x 32 output blocks, k16 steps), true = v_mfma_f32_16x16x32_bf16 (16 x 16
 // blocks, k32 steps).  Both read the same LDS bytes per product term from the
-// same swizzled rows: every fragment row of a lane is its lane row plus a
-// multiple of 16, and the chunk swizzle depends on a row's low four bits only.
+// same row layout, each with its own chunk swizzle (pp_swz): every fragment
+// row of a lane is its lane row plus a multiple of 16, and a swizzle depends
+// on a row's low four bits only.
 // The 16x16x32 form is the faster one on the MI355X: register-only loops
 // sustain 2.14 against 1.92 PFLOP/s, and the 7B prefill projections ran 3-11%
 // faster with it (gate/up + SiLU.mul 290-297 against 326-333 us back to back).
