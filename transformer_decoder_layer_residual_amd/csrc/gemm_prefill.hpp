@@ -213,6 +213,10 @@ struct PPGeom {
 // sustain 2.14 against 1.92 PFLOP/s, and the 7B prefill projections ran 3-11%
 // faster with it (gate/up + SiLU.mul 290-297 against 326-333 us back to back).
 constexpr bool kPPMfma16 = true;
+// Wave arrangement of 128-row tiles: false = 2 x 2 waves per group (32 rows x
+// 128 columns each), true = 1 x 4 (64 x 64: a fifth fewer fragment reads per
+// product term; the 7B O and down projections 2-6% faster).
+constexpr bool kPP128Rows1 = true;
 
 // One BM x 256 output tile: tile `bid` of a tiles_m x tiles_n grid whose
 // N-tiles start at tn0 (so a launch may cover a range of N with one shape);
@@ -231,11 +235,15 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   constexpr int LA = NSTAGE - 1;                    // k-tiles loaded ahead
   constexpr bool F16 = kPPMfma16;
   constexpr int MB = F16 ? 16 : 32;                 // rows of an MFMA output block
-  constexpr int MS = BM / 4 / MB, NS = 128 / MB;    // output blocks per wave (rows, columns)
+  // waves of a group along rows x columns: 2 x 2, or 1 x 4 for 128-row tiles
+  // with kPP128Rows1 (a wave then holds 64 rows x 64 columns)
+  constexpr int WGN = (BM == 128 && kPP128Rows1) ? 4 : 2, WGM = 4 / WGN;
+  constexpr int GR = BM / 2, WR = GR / WGM;         // rows per group, per wave
+  constexpr int MS = WR / MB, NS = 256 / WGN / MB;  // output blocks per wave (rows, columns)
   constexpr int KS = BK / (F16 ? 32 : 16);          // MFMA k steps per tile
   constexpr int RPW = (BM + BN) / 8;                // LDS rows each wave loads per stage
   constexpr int LI = RPW / RPI;                     // load instructions per wave per stage
-  constexpr int GR = BM / 2, WR = BM / 4;           // rows per group, per wave
+  static_assert(MS >= 1 && NS >= 2, "wave tile");
   constexpr int OPITCH = Geo::OPITCH;
   static_assert(NSTAGE >= 2 && LA <= 3, "stages");
 
@@ -251,7 +259,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: LDS bases in SGPRs
   const int grp = wave >> 2, wig = wave & 3;        // group, wave in group
-  const int wm = wig >> 1, wn = wig & 1;
+  const int wm = wig / WGN, wn = wig % WGN;
   const int fr = lane & (MB - 1), fh = lane / MB;   // fragment row, k-chunk group
 
   // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
@@ -315,7 +323,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         // first half (blocks of this wave's 64 columns), then their partners
-        const int blk = (s < NS / 2) ? wn * (NS / 2) + s : NS + wn * (NS / 2) + (s - NS / 2);
+        const int blk = (s < NS / 2) ? wn * (NS / 2) + s : 128 / MB + wn * (NS / 2) + (s - NS / 2);
         fw[ks][s] = *reinterpret_cast<const bf16x8*>(ws + blk * MB * ROWB + lo);
       }
     }
