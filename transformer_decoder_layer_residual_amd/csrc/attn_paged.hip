@@ -401,7 +401,8 @@ attn_paged_kernel(const T* __restrict__ q, const T* __restrict__ kc, const T* __
 // ---------------------------------------------------------------------------
 
 // DEPTH: wave steps in flight (2 measured best on the 7B verification batch:
-// 5.6 TB/s against 5.5 and 5.4 for 3 and 4, with 4096-key splits)
+// 5.6 TB/s against 5.5 and 5.4 for 3 and 4, with 4096-key splits, and 4.4 for
+// one step in flight)
 template <typename T, int D, int DEPTH = 2>
 __global__ void __launch_bounds__(256, 1)
 attn_paged_narrow_kernel(const T* __restrict__ q, const T* __restrict__ kc,
