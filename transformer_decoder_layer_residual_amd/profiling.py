@@ -347,6 +347,97 @@ def ceilings(out: str, cmd: str):
     print("\n".join(lines[-len(rows) - 2:]))
 
 
+def projections(out: str, cmd: str):
+    """The four prefill projections of the 7B layer (2048 tokens) and of the
+    8B-GQA ragged batch (6235 tokens) through this library's entry points
+    (with their fused epilogues) and as plain torch.mm products of the same
+    shapes (hipBLASLt, no epilogue): cold (1 GiB written and read before
+    every launch, median of 15) and back to back (mean of 20)."""
+    import torch
+
+    from . import binding as dl
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+
+    def rnd(*shape, sc=1.0):
+        return (torch.randn(*shape, device=dev, generator=g) * sc).to(torch.bfloat16)
+
+    flush_w = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    flush_r = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+
+    def cold_ms(fn, n=15):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            flush_w.fill_(i)
+            flush_r.sum()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return ts[len(ts) // 2]
+
+    shapes = [("llama2-7b, 2048 tokens", 2048, 4096, 32, 32, 128, 11008),
+              ("llama3-8b-gqa, 6235 tokens", 6235, 4096, 32, 8, 128, 14336)]
+    rows = []
+    for label, T, H, Hq, Hkv, D, I in shapes:
+        x = rnd(T, H)
+        wq, wk, wv = rnd(Hq * D, H, sc=0.02), rnd(Hkv * D, H, sc=0.02), rnd(Hkv * D, H, sc=0.02)
+        wqkv = torch.cat([wq, wk, wv], 0)
+        wo, wg, wu, wd = (rnd(H, Hq * D, sc=0.02), rnd(I, H, sc=0.02), rnd(I, H, sc=0.02),
+                          rnd(H, I, sc=0.02))
+        wgu = torch.cat([wg, wu], 0)
+        attn, a = rnd(T, Hq * D), rnd(T, I)
+        q = torch.empty(T, Hq, D, dtype=torch.bfloat16, device=dev)
+        k = torch.empty(T, Hkv, D, dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        cs = torch.empty(4096, D, device=dev)
+        dl.dl_rope_table_fill(cs, 4096, D, 1e4)
+        pos = (torch.arange(T, device=dev) % 1024).to(torch.int32)
+        o = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        act = torch.empty(T, I, dtype=torch.bfloat16, device=dev)
+        res = torch.randn(T, H, device=dev, generator=g)
+        y = torch.empty_like(res)
+        ops = [
+            ("QKV + RoPE", T, (Hq + 2 * Hkv) * D, H,
+             lambda: dl.dl_qkv_rope(x, wq, wk, wv, pos, cs, q, k, v),
+             (x, wqkv, torch.empty(T, (Hq + 2 * Hkv) * D, dtype=torch.bfloat16, device=dev))),
+            ("O", T, H, Hq * D, lambda: dl.dl_linear(attn, wo, o), (attn, wo, o)),
+            ("gate/up + SiLU*mul", T, 2 * I, H, lambda: dl.dl_gate_up_silu(x, wg, wu, act),
+             (x, wgu, torch.empty(T, 2 * I, dtype=torch.bfloat16, device=dev))),
+            ("down + residual", T, H, I, lambda: dl.dl_down_residual(a, wd, y, residual=res),
+             (a, wd, o)),
+        ]
+        for name, M, N, K, ours, (mx, mw, my) in ops:
+            fl = 2.0 * M * N * K
+            lib_fn = (lambda mx=mx, mw=mw, my=my: torch.mm(mx, mw.t(), out=my))
+            t = [cold_ms(ours), _time_ms(ours, n=20), cold_ms(lib_fn), _time_ms(lib_fn, n=20)]
+            rows.append((label, name, f"{M} x {N} x {K}",
+                         *(f"{ms * 1e3:.1f} us ({fl / ms / 1e9:,.0f})" for ms in t),
+                         f"{t[2] / t[0]:.2f}"))
+            print(" | ".join(rows[-1]), file=sys.stderr, flush=True)
+    lines = ["# Prefill projections: this library against torch.mm (hipBLASLt)", "",
+             "Each projection of the 7B layer (2048 tokens) and of the 8B-GQA ragged batch (6235 "
+             "tokens) through this library's entry point, with its fused epilogue (RoPE, SiLU*mul, "
+             "residual add), and as a plain torch.mm of the same M x N x K (y = x w^T, bf16, no "
+             "epilogue).  Cold: 1 GiB written and read before every launch, median of 15 "
+             "launches; warm: mean of 20 back-to-back launches.  TFLOP/s in parentheses; the "
+             "last column is hipBLASLt's cold time over ours (above 1: ours is faster).", "",
+             "Command (repository root on the MI355X box):", "", "```", cmd, "```", "",
+             "| workload | projection | M x N x K | ours cold | ours warm | torch.mm cold | "
+             "torch.mm warm | torch.mm / ours (cold) |",
+             "|---|---|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append("| " + " | ".join(r) + " |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines[-len(rows) - 2:]))
+
+
 def gemm8192(calls: int):
     """The bf16 8192^3 product through this library and through torch.mm
     (hipBLASLt), `calls` times each, for counters."""
@@ -391,6 +482,8 @@ def main(argv=None):
     e.add_argument("--title", default="Counters per kernel")
     f_ = sub.add_parser("ceilings")
     f_.add_argument("--out", required=True)
+    p_ = sub.add_parser("projections")
+    p_.add_argument("--out", required=True)
     g_ = sub.add_parser("gemm8192")
     g_.add_argument("--calls", type=int, default=3)
     d = sub.add_parser("bytes-summary")
@@ -413,6 +506,9 @@ def main(argv=None):
     elif args.sub == "ceilings":
         ceilings(args.out, "python -m transformer_decoder_layer_residual_amd.profiling ceilings "
                  f"--out {args.out}")
+    elif args.sub == "projections":
+        projections(args.out, "python -m transformer_decoder_layer_residual_amd.profiling "
+                    f"projections --out {args.out}")
     elif args.sub == "gemm8192":
         gemm8192(args.calls)
     elif args.sub == "layer-bytes":
