@@ -153,9 +153,11 @@ gemm_big_kernel(const bf16* __restrict__ X, int M, int K, Map map, Epi epi, int 
 // always has a wave feeding the matrix pipe.
 //   group 0: MEM(t) in phase 2t+1, COMP(t) in phase 2t+2
 //   group 1: MEM(t) in phase 2t+2, COMP(t) in phase 2t+3
-// K-tiles live in two LDS stages; tile t+2 is loaded into tile t's stage in
-// phase 2t+3 (after both groups read tile t) and waited for at the end of
-// phase 2t+4, before either group reads it.
+// K-tiles live in two to four LDS stages (three weight and two activation
+// stages for 256-row tiles); a tile is loaded into the stage of one both groups
+// have read, by each group in its own MEM phase (kPPMemPhaseLoads), and waited
+// for by the waves that loaded it before the barrier that precedes its first
+// read.
 // Global->LDS loads go straight to LDS (global_load_lds_dwordx4, 1 KB per wave
 // instruction = 8 rows of 128 B); the 16-byte chunks of a row are XOR-swizzled
 // so the 16- and 32-row fragment reads hit distinct banks.  Requires K % 64 == 0.
@@ -188,19 +190,38 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // LDS footprint of one tile shape: the k-tile stages, or the fp32 staging of
-// one group's output rows, whichever is larger.  (A third stage for the
-// weight half of 256-row tiles, which fits the 160 KB exactly, measured no
+// one group's output rows, whichever is larger.  (A third weight stage alone,
+// with both groups still issuing their loads in the odd phases, measured no
 // faster: 328.6 against 322.9 us for the 7B gate/up product on the 32x32x16
-// form of the tile.)
+// form of the tile; what pays is moving the issue points, below.)
+//
+// Loads in MEM phases only (kPPMemPhaseLoads): every group issues its
+// global->LDS loads in its own MEM phase, never in front of its MFMAs, and
+// the two groups' loads of a k-tile go out in different phases instead of all
+// in the odd ones.  Shapes with three or four stages need only a different
+// issue point (group 1 loads tile t+LA in MEM(t), whose stage both groups have
+// read by then, instead of tile t+1+LA in COMP(t)).  Two-stage shapes (256-row
+// tiles, 64-wide k-tiles) split their stages: the activation rows keep two
+// and the weight rows get three, which fill the 160 KB exactly; group 0 loads
+// the activation rows (tile t+1 in phase 2t+1) and group 1 the weight rows
+// (tile t+2 in phase 2t+2).  Measured against issuing in the odd phases: 7B
+// gate/up + SiLU.mul 262 against 287 us back to back (276 against 305-309
+// with a cache flush before each launch), 8B-GQA down 622 against 693 us.
+constexpr bool kPPMemPhaseLoads = true;
+
 template <int BM, int BK>
 struct PPGeom {
   static constexpr int BN = 256;
   static constexpr int STAGE = (BM + BN) * BK * 2;
   static constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
   static constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
+  static constexpr bool SPLIT = kPPMemPhaseLoads && BM == 256 && BK == 64;
+  static constexpr int XST = BM * BK * 2, WST = BN * BK * 2;  // split: activation, weight stage
   static constexpr int OPITCH = BN + 8;             // fp32 row pitch of the output staging
-  static constexpr int MAIN = NSTAGE * STAGE, OUT = (BM / 2) * OPITCH * 4;
+  static constexpr int MAIN = SPLIT ? 2 * XST + 3 * WST : NSTAGE * STAGE;
+  static constexpr int OUT = (BM / 2) * OPITCH * 4;
   static constexpr int SMEM = MAIN > OUT ? MAIN : OUT;
+  static_assert(SMEM <= 160 * 1024, "LDS");
 };
 
 // Matrix instruction of the ping-pong tile: false = v_mfma_f32_32x32x16_bf16
@@ -278,8 +299,17 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     }
     src[i] = reinterpret_cast<const unsigned char*>(base) + (int64_t)kt0 * BK * 2 + c * 16;
   }
+  constexpr bool SPLIT = Geo::SPLIT;
+  // group 1 issues in its MEM phase (three or four stages; see kPPMemPhaseLoads)
+  constexpr bool G1MEM = kPPMemPhaseLoads && LA >= 2;
+  static_assert(!SPLIT || RPW * 4 == BM, "split stages: group 0 loads exactly the activation rows");
   auto issue_loads = [&](int kt) {
-    unsigned char* dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
+    unsigned char* dst;
+    if constexpr (SPLIT)
+      dst = grp == 0 ? smem + (kt % 2) * Geo::XST + wave * RPW * ROWB
+                     : smem + 2 * Geo::XST + (kt % 3) * Geo::WST + (wave - 4) * RPW * ROWB;
+    else
+      dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
     const int64_t koff = (int64_t)kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < LI; ++i)
@@ -309,8 +339,10 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   for (int ks = 0; ks < KS; ++ks)
     lane_off[ks] = fr * ROWB + (((ks * CPS + fh) ^ pp_swz<BK, F16>(fr)) << 4);
   auto read_frags = [&](int kt) {
-    const unsigned char* xs = smem + (kt % NSTAGE) * STAGE + (grp * GR + wm * WR) * ROWB;
-    const unsigned char* ws = smem + (kt % NSTAGE) * STAGE + BM * ROWB;
+    const unsigned char* xs =
+        (SPLIT ? smem + (kt % 2) * Geo::XST : smem + (kt % NSTAGE) * STAGE) + (grp * GR + wm * WR) * ROWB;
+    const unsigned char* ws =
+        SPLIT ? smem + 2 * Geo::XST + (kt % 3) * Geo::WST : smem + (kt % NSTAGE) * STAGE + BM * ROWB;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // opaque to the optimiser, so the offsets of every fragment are not
@@ -362,6 +394,35 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   // one phase later.  Tile t+LA goes into tile t-1's stage in phase 2t+1 (group
   // 0 from its MEM(t), group 1 from its COMP(t-1)); tile t+1 must have landed
   // by the end of phase 2t+2.
+  if constexpr (SPLIT) {
+    // each wave loads only its own half (group 0 activations, group 1
+    // weights); its wait counts cover its own loads
+    issue_loads(0);
+    if (nkt > 1) issue_loads(1);
+    if (nkt > 1) wait_vmcnt<LI>();
+    else wait_vmcnt<0>();
+    DL_PHASE_END();                                 // phase 1 begins
+    if (grp == 1) DL_PHASE_END();                   // group 1 starts one phase later
+    for (int kt = 0; kt < nkt; ++kt) {
+      // MEM(kt): group 0 loads activation tile kt+1 into tile kt-1's stage
+      // (tile 1 came with the prologue); group 1 loads weight tile kt+2 into
+      // tile kt-1's stage, then waits for weight tile kt+1, which group 0
+      // reads in the next phase
+      read_frags(kt);
+      if (grp == 0) {
+        if (kt >= 1 && kt + 1 < nkt) issue_loads(kt + 1);
+      } else {
+        if (kt + 2 < nkt) issue_loads(kt + 2);
+        if (kt + 2 < nkt) wait_vmcnt<LI>();
+        else wait_vmcnt<0>();
+      }
+      DL_PHASE_END();
+      // COMP(kt); group 0 then waits for activation tile kt+1
+      compute();
+      if (grp == 0) wait_vmcnt<0>();
+      DL_PHASE_END();
+    }
+  } else {
   for (int i = 0; i <= LA && i < nkt; ++i) issue_loads(i);
   wait_tile(0, nkt);
   DL_PHASE_END();                                   // phase 1 begins
@@ -372,14 +433,20 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     if (grp == 0) {
       if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
     } else {
+      if constexpr (G1MEM) {
+        if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
+      }
       if (kt + 1 < nkt) wait_tile(kt + 1, nkt);
     }
     DL_PHASE_END();
     // COMP(kt)
-    if (grp == 1 && kt + 1 + LA < nkt) issue_loads(kt + 1 + LA);
+    if constexpr (!G1MEM) {
+      if (grp == 1 && kt + 1 + LA < nkt) issue_loads(kt + 1 + LA);
+    }
     compute();
     if (grp == 0 && kt + 1 < nkt) wait_tile(kt + 1, nkt);
     DL_PHASE_END();
+  }
   }
   if (grp == 0) DL_PHASE_END();                     // balance group 1's extra barrier
 #undef DL_PHASE_END
