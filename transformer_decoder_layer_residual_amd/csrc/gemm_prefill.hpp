@@ -406,13 +406,17 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     for (int kt = 0; kt < nkt; ++kt) {
       // MEM(kt): group 0 loads activation tile kt+1 into tile kt-1's stage
       // (tile 1 came with the prologue); group 1 loads weight tile kt+2 into
-      // tile kt-1's stage, then waits for weight tile kt+1, which group 0
-      // reads in the next phase
-      read_frags(kt);
+      // tile kt-1's stage and, after its fragment reads, waits for weight
+      // tile kt+1, which group 0 reads in the next phase.  Loads go out
+      // before the fragment reads (they target another stage): 1-2% less
+      // time over the four 7B projections than after them.
       if (grp == 0) {
         if (kt >= 1 && kt + 1 < nkt) issue_loads(kt + 1);
       } else {
         if (kt + 2 < nkt) issue_loads(kt + 2);
+      }
+      read_frags(kt);
+      if (grp == 1) {
         if (kt + 2 < nkt) wait_vmcnt<LI>();
         else wait_vmcnt<0>();
       }
@@ -429,13 +433,11 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   if (grp == 1) DL_PHASE_END();                     // group 1 starts one phase later
   for (int kt = 0; kt < nkt; ++kt) {
     // MEM(kt)
-    read_frags(kt);
-    if (grp == 0) {
+    if (grp == 0 || G1MEM) {
       if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
-    } else {
-      if constexpr (G1MEM) {
-        if (kt >= 1 && kt + LA < nkt) issue_loads(kt + LA);
-      }
+    }
+    read_frags(kt);
+    if (grp == 1) {
       if (kt + 1 < nkt) wait_tile(kt + 1, nkt);
     }
     DL_PHASE_END();
