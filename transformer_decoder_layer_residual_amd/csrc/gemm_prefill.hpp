@@ -208,6 +208,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // gate/up + SiLU.mul 262 against 287 us back to back (276 against 305-309
 // with a cache flush before each launch), 8B-GQA down 622 against 693 us.
 constexpr bool kPPMemPhaseLoads = true;
+// Split stages for 128-row tiles too (two activation stages of 16 KB, four
+// weight stages of 32 KB: weight loads three k-tiles ahead instead of two):
+// measured slower on the 7B O projection (3-5%) and the QKV's 128-row tiles
+// (1.5-2%), the down projection within +-2.5%, so 128-row tiles keep their
+// three whole stages.
+constexpr bool kPPSplit128 = false;
 
 template <int BM, int BK>
 struct PPGeom {
@@ -215,10 +221,13 @@ struct PPGeom {
   static constexpr int STAGE = (BM + BN) * BK * 2;
   static constexpr int NSTAGE_FIT = (160 * 1024) / STAGE;
   static constexpr int NSTAGE = NSTAGE_FIT < 4 ? NSTAGE_FIT : 4;  // LDS stages (2 .. 4)
-  static constexpr bool SPLIT = kPPMemPhaseLoads && BM == 256 && BK == 64;
+  static constexpr bool SPLIT =
+      kPPMemPhaseLoads && BK == 64 && (BM == 256 || (BM == 128 && kPPSplit128));
   static constexpr int XST = BM * BK * 2, WST = BN * BK * 2;  // split: activation, weight stage
+  static constexpr int NWS_FIT = (160 * 1024 - 2 * XST) / WST;
+  static constexpr int NWS = NWS_FIT < 4 ? NWS_FIT : 4;      // split: weight stages (3 or 4)
   static constexpr int OPITCH = BN + 8;             // fp32 row pitch of the output staging
-  static constexpr int MAIN = SPLIT ? 2 * XST + 3 * WST : NSTAGE * STAGE;
+  static constexpr int MAIN = SPLIT ? 2 * XST + NWS * WST : NSTAGE * STAGE;
   static constexpr int OUT = (BM / 2) * OPITCH * 4;
   static constexpr int SMEM = MAIN > OUT ? MAIN : OUT;
   static_assert(SMEM <= 160 * 1024, "LDS");
@@ -284,11 +293,22 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   const int fr = lane & (MB - 1), fh = lane / MB;   // fragment row, k-chunk group
 
   // ---- load assignment: wave w fills LDS rows [RPW w, RPW (w + 1)) of a stage
-  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), RPI rows per instruction.
-  const unsigned char* src[LI];
+  // (rows 0..BM-1 = X tile, BM..BM+255 = W tile), RPI rows per instruction;
+  // with split stages group 0's waves fill the X rows (BM / 4 each, LIX
+  // instructions) and group 1's the W rows (64 each, LIW instructions).
+  constexpr bool SPLIT = Geo::SPLIT;
+  constexpr int NWS = Geo::NWS, LAW = NWS - 1;      // split: weight stages, look-ahead
+  constexpr int LIX = BM / 4 / RPI, LIW = 64 / RPI;
+  constexpr int LIS = SPLIT ? LIW : LI;             // source rows kept per wave
+  static_assert(!SPLIT || (LIX <= LIW && LAW >= 2 && LAW <= 3), "split stages");
+  const unsigned char* src[LIS];
 #pragma unroll
-  for (int i = 0; i < LI; ++i) {
-    const int row = wave * RPW + i * RPI + lane / CPR;
+  for (int i = 0; i < LIS; ++i) {
+    // (a group-0 wave of a 128-row tile uses only its first LIX entries; the
+    // rest point at valid rows and are never loaded)
+    const int row = SPLIT ? (grp == 0 ? wave * (BM / 4) + i * RPI + lane / CPR
+                                      : BM + (wave - 4) * 64 + i * RPI + lane / CPR)
+                          : wave * RPW + i * RPI + lane / CPR;
     const int c = (lane % CPR) ^ pp_swz<BK, F16>(row);  // logical chunk this lane fetches
     const bf16* base;
     if (row < BM) {
@@ -299,23 +319,35 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     }
     src[i] = reinterpret_cast<const unsigned char*>(base) + (int64_t)kt0 * BK * 2 + c * 16;
   }
-  constexpr bool SPLIT = Geo::SPLIT;
   // group 1 issues in its MEM phase (three or four stages; see kPPMemPhaseLoads)
   constexpr bool G1MEM = kPPMemPhaseLoads && LA >= 2;
-  static_assert(!SPLIT || RPW * 4 == BM, "split stages: group 0 loads exactly the activation rows");
-  auto issue_loads = [&](int kt) {
-    unsigned char* dst;
-    if constexpr (SPLIT)
-      dst = grp == 0 ? smem + (kt % 2) * Geo::XST + wave * RPW * ROWB
-                     : smem + 2 * Geo::XST + (kt % 3) * Geo::WST + (wave - 4) * RPW * ROWB;
-    else
-      dst = smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB;
+  auto load_rows = [&](unsigned char* dst, int kt, auto n) {
     const int64_t koff = (int64_t)kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < LI; ++i)
+    for (int i = 0; i < decltype(n)::value; ++i)
       __builtin_amdgcn_global_load_lds(
           (const void*)(src[i] + koff),
           (__attribute__((address_space(3))) void*)(dst + i * RPI * ROWB), 16, 0, 0);
+  };
+  auto issue_loads = [&](int kt) {
+    if constexpr (SPLIT) {
+      if (grp == 0)
+        load_rows(smem + (kt % 2) * Geo::XST + wave * (BM / 4) * ROWB, kt,
+                  std::integral_constant<int, LIX>());
+      else
+        load_rows(smem + 2 * Geo::XST + (kt % NWS) * Geo::WST + (wave - 4) * 64 * ROWB, kt,
+                  std::integral_constant<int, LIW>());
+    } else {
+      load_rows(smem + (kt % NSTAGE) * STAGE + wave * RPW * ROWB, kt,
+                std::integral_constant<int, LI>());
+    }
+  };
+  // split stages: group 1 waits for weight tile `need` with `newer` later
+  // weight tiles of its own still in flight
+  auto wait_w = [&](int newer) {
+    if (newer >= 2) wait_vmcnt<2 * LIW>();
+    else if (newer == 1) wait_vmcnt<LIW>();
+    else wait_vmcnt<0>();
   };
   // wait until this wave's part of k-tile `need` has landed; tiles it issued
   // after that one may stay in flight
@@ -342,7 +374,7 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
     const unsigned char* xs =
         (SPLIT ? smem + (kt % 2) * Geo::XST : smem + (kt % NSTAGE) * STAGE) + (grp * GR + wm * WR) * ROWB;
     const unsigned char* ws =
-        SPLIT ? smem + 2 * Geo::XST + (kt % 3) * Geo::WST : smem + (kt % NSTAGE) * STAGE + BM * ROWB;
+        SPLIT ? smem + 2 * Geo::XST + (kt % NWS) * Geo::WST : smem + (kt % NSTAGE) * STAGE + BM * ROWB;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // opaque to the optimiser, so the offsets of every fragment are not
@@ -395,31 +427,35 @@ __device__ __forceinline__ void pp_tile(const bf16* __restrict__ X, int M, int K
   // 0 from its MEM(t), group 1 from its COMP(t-1)); tile t+1 must have landed
   // by the end of phase 2t+2.
   if constexpr (SPLIT) {
-    // each wave loads only its own half (group 0 activations, group 1
+    // each wave loads only its own rows (group 0 activations, group 1
     // weights); its wait counts cover its own loads
-    issue_loads(0);
-    if (nkt > 1) issue_loads(1);
-    if (nkt > 1) wait_vmcnt<LI>();
-    else wait_vmcnt<0>();
+    if (grp == 0) {
+      issue_loads(0);
+      if (nkt > 1) issue_loads(1);
+      if (nkt > 1) wait_vmcnt<LIX>();
+      else wait_vmcnt<0>();
+    } else {
+#pragma unroll
+      for (int j = 0; j < LAW; ++j)
+        if (j < nkt) issue_loads(j);
+      wait_w(min(LAW - 1, nkt - 1));
+    }
     DL_PHASE_END();                                 // phase 1 begins
     if (grp == 1) DL_PHASE_END();                   // group 1 starts one phase later
     for (int kt = 0; kt < nkt; ++kt) {
       // MEM(kt): group 0 loads activation tile kt+1 into tile kt-1's stage
-      // (tile 1 came with the prologue); group 1 loads weight tile kt+2 into
-      // tile kt-1's stage and, after its fragment reads, waits for weight
-      // tile kt+1, which group 0 reads in the next phase.  Loads go out
-      // before the fragment reads (they target another stage): 1-2% less
+      // (tile 1 came with the prologue); group 1 loads weight tile kt+LAW
+      // into tile kt-1's stage and, after its fragment reads, waits for
+      // weight tile kt+1, which group 0 reads in the next phase.  Loads go
+      // out before the fragment reads (they target another stage): 1-2% less
       // time over the four 7B projections than after them.
       if (grp == 0) {
         if (kt >= 1 && kt + 1 < nkt) issue_loads(kt + 1);
       } else {
-        if (kt + 2 < nkt) issue_loads(kt + 2);
+        if (kt + LAW < nkt) issue_loads(kt + LAW);
       }
       read_frags(kt);
-      if (grp == 1) {
-        if (kt + 2 < nkt) wait_vmcnt<LI>();
-        else wait_vmcnt<0>();
-      }
+      if (grp == 1 && kt + 1 < nkt) wait_w(min(LAW - 1, nkt - 2 - kt));
       DL_PHASE_END();
       // COMP(kt); group 0 then waits for activation tile kt+1
       compute();
