@@ -82,6 +82,9 @@ GEMM_SHAPES = [
     (40, 38400, 512),    # decode stream with runs of 2-3 stages: whole tiles and shared ones
     (2048, 12288, 128),  # 384 tiles of 256: 256-row tiles then 128-row tiles in one launch
     (2000, 12288, 192),  # the same with a ragged last row tile
+    # 256-row tiles with one, two and three 64-wide k-tiles: the prologue alone,
+    # and the split-stage schedule before its weight look-ahead fills
+    (2048, 8192, 64), (1024, 16384, 128), (2048, 8192, 192),
 ]
 
 
