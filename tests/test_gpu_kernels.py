@@ -85,6 +85,7 @@ GEMM_SHAPES = [
     # 256-row tiles with one, two and three 64-wide k-tiles: the prologue alone,
     # and the split-stage schedule before its weight look-ahead fills
     (2048, 8192, 64), (1024, 16384, 128), (2048, 8192, 192),
+    (2048, 4096, 8192),  # long rows: half a round of 256-row tiles, split over K
 ]
 
 
@@ -106,7 +107,9 @@ def test_linear_exact_small_integers(dtype, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(7, 256, 4096), (300, 1024, 1000), (2048, 4096, 512),
                                    # ping-pong tiles split over K (tiles < 192): 8 and 5 splits
-                                   (256, 4096, 11008), (300, 2048, 2560)])
+                                   (256, 4096, 11008), (300, 2048, 2560),
+                                   # 256-row tiles split over K (long rows, 128 tiles)
+                                   (2048, 4096, 11008)])
 def test_linear_random_bf16(M, N, K):
     print(f"linear rnd {M}x{N}x{K}", flush=True)
     x = rnd(M, K)

@@ -34,8 +34,13 @@ GemmPlan plan_gemm(int M, int N, int K, bool is_f32, bool paired) {
   } else if (M >= 256 && K % 64 == 0 && fits(kCfg256)) {
     // ping-pong kernel; 256-row tiles when they fill the chip, else 128
     // (a round-count model favoured 128-row tiles for 1.5 rounds of 256-row
-    // ones, but measured no faster and with more panel traffic)
-    cfg = tiles(kCfg256) >= 256 ? kCfg256 : kCfgPP128;
+    // ones, but measured no faster and with more panel traffic).  Long rows
+    // (K >= 8192) take 256-row tiles split over K already from half a round
+    // of them: the tile's smaller fragment traffic per product term then
+    // outweighs the fp32 partial round trip (7B down projection, 2048 x 4096
+    // x 11008, inside the layer step: 0.741 against 0.760-0.780 ms cold; at
+    // K = 4096, the O projection, the split tiles were 80 against 62 us).
+    cfg = (tiles(kCfg256) >= 256 || (tiles(kCfg256) >= 128 && K >= 8192)) ? kCfg256 : kCfgPP128;
   } else if (M >= 512) {
     cfg = (fits(kCfg256) && tiles(kCfg256) >= 256) ? kCfg256 : (fits(kCfg128) ? kCfg128 : kCfg32s);
   } else if (M > 16) {
