@@ -120,6 +120,29 @@ def test_linear_random_bf16(M, N, K):
     assert_bf16_close(host(out)[rows], oracle.linear(x[rows], w, round_bf16=True), "linear")
 
 
+# Every prefill tile path, called repeatedly on the same inputs, gives the same
+# bits each time (the waves of a tile hand k-tiles to each other through LDS
+# stages; a missing wait would show up as run-to-run differences): 256-row
+# tiles with split stages, 256-row tiles split over K with their reduction,
+# 128-row tiles, and the mixed 256/128-row launch.
+@pytest.mark.parametrize("M,N,K", [(2048, 22016, 4096), (2048, 4096, 11008), (2048, 4096, 4096),
+                                   (2048, 12288, 4096)])
+def test_linear_repeat_bit_identical(M, N, K):
+    print(f"linear repeat {M}x{N}x{K}", flush=True)
+    x = rnd(M, K)
+    w = rnd(N, K, scale=0.02)
+    xd, wd = dev_bf16(x), dev_bf16(w)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    dl.dl_linear(xd, wd, out)
+    first = out.clone()
+    for it in range(9):
+        out.zero_()
+        dl.dl_linear(xd, wd, out)
+        assert torch.equal(out, first), f"run {it + 1} differs from the first"
+    rows = np.unique(np.concatenate([np.arange(8), R.integers(0, M, 8), [M - 1]]))
+    assert_bf16_close(host(first)[rows], oracle.linear(x[rows], w, round_bf16=True), "linear")
+
+
 # Decode batches of at most 16 rows against N >= 4096 go to the row-block
 # weight stream (16 weight rows per workgroup, K split over its waves): K
 # ranges that leave each wave a ragged tail of k groups, and each row length
