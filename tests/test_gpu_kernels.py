@@ -178,6 +178,23 @@ def test_down_residual_two_block_row_stream(T):
                      rel=1e-2)
 
 
+def test_down_residual_split_long_rows_ragged_m():
+    """Long rows (K >= 8192) with half a round of 256-row tiles take those tiles
+    split in two over K plus the reduction, here with a ragged last row tile
+    (1900 rows) through the residual epilogue; sampled rows against the oracle."""
+    print("down split long rows M=1900", flush=True)
+    M, H, I = 1900, 4096, 8192
+    a = rnd(M, I)
+    wd = rnd(H, I, scale=0.02)
+    r = R.standard_normal((M, H)).astype(np.float32)
+    y = torch.empty(M, H, device=DEV)
+    dl.dl_down_residual(dev_bf16(a), dev_bf16(wd), y, residual=dev_f32(r))
+    rows = np.unique(np.concatenate([np.arange(4), R.integers(0, M, 12), np.arange(M - 110, M, 9),
+                                     [M - 1]]))
+    assert_f32_close(host(y)[rows], oracle.down_residual(a[rows], wd, r[rows]), "down+resid",
+                     max_abs=3e-2, rel=1e-2)
+
+
 @pytest.mark.parametrize("T", [1, 5, 16])
 def test_ffn_and_qkv_row_block_stream(T):
     print(f"row16 ffn/qkv T={T}", flush=True)
